@@ -1,0 +1,403 @@
+/*
+ * moe_ref.c -- plain CPU oracle of the routed mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline timing).  It
+ * shares no code with the GPU path.  See moe_ref.h for what each function
+ * computes and for the sources on the pages.  Everything here is written for
+ * a reader to check by eye: no blocking, no fusion, fp64 accumulation in
+ * ascending index order.  OpenMP only splits independent output elements
+ * across threads; each element is still computed by one thread in the
+ * written order, so results do not depend on the thread count.
+ */
+#include "moe_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int moe_ref_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Number formats                                                                              */
+/* ------------------------------------------------------------------------------------------ */
+
+static float bf16_bits_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a double to the nearest bf16 (ties to even) in one step, returned as bits. */
+static uint16_t f64_to_bf16_rne(double v) {
+    if (isnan(v)) return 0x7FC0;
+    int neg = signbit(v);
+    double a = fabs(v);
+    double r;
+    if (a == 0.0 || isinf(a)) {
+        r = a;
+    } else {
+        int ex;
+        (void)frexp(a, &ex);            /* a = m * 2^ex, m in [0.5, 1) */
+        int lsb = ex - 8;               /* bf16 keeps 8 significant bits */
+        if (lsb < -133) lsb = -133;     /* subnormal spacing 2^-133 */
+        double q = ldexp(a, -lsb);      /* exact: power-of-two scaling of a double */
+        r = ldexp(nearbyint(q), lsb);   /* default rounding mode: nearest, ties to even */
+        if (r >= ldexp(1.0, 128)) r = INFINITY;
+    }
+    float f = (float)r;                 /* exact: r is representable in bf16, hence fp32 */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t b = (uint16_t)(u >> 16);
+    return neg ? (uint16_t)(b | 0x8000u) : b;
+}
+
+/* OCP Microscaling v1.0 E2M1 magnitudes for the 3 low bits of a code (sign in bit 3). */
+static const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* One MXFP4 element: (-1)^b3 * M[code & 7] * 2^(scale - 127); scale byte 255 encodes NaN. */
+static float mxfp4_value(uint8_t code, uint8_t scale) {
+    if (scale == 255) return NAN;
+    float m = ldexpf(kE2M1[code & 7], (int)scale - 127);
+    return (code & 8) ? -m : m;
+}
+
+int moe_ref_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out) {
+    if (!codes || !scales || !out || rows < 0 || K < 0 || K % 32 != 0) return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < K; ++j) {
+            uint8_t byte = codes[r * (K / 2) + j / 2];
+            uint8_t code = (j % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);
+            out[r * K + j] = mxfp4_value(code, scales[r * (K / 32) + j / 32]);
+        }
+    return 0;
+}
+
+/* Row n of a [N, K] weight matrix of expert e (tensor holds E_or_1 such matrices), upcast to fp64. */
+static void weight_row(int32_t dtype, const void* w, const uint8_t* scale, int64_t e, int64_t N, int64_t K,
+                       int64_t n, double* row) {
+    if (dtype == MOE_REF_F32) {
+        const float* p = (const float*)w + (e * N + n) * K;
+        for (int64_t j = 0; j < K; ++j) row[j] = (double)p[j];
+    } else if (dtype == MOE_REF_BF16) {
+        const uint16_t* p = (const uint16_t*)w + (e * N + n) * K;
+        for (int64_t j = 0; j < K; ++j) row[j] = (double)bf16_bits_to_f32(p[j]);
+    } else {
+        const uint8_t* c = (const uint8_t*)w + (e * N + n) * (K / 2);
+        const uint8_t* sc = scale + (e * N + n) * (K / 32);
+        for (int64_t j = 0; j < K; ++j) {
+            uint8_t code = (j % 2 == 0) ? (uint8_t)(c[j / 2] & 0xF) : (uint8_t)(c[j / 2] >> 4);
+            row[j] = (double)mxfp4_value(code, sc[j / 32]);
+        }
+    }
+}
+
+/* Activation row t of x [T, d], upcast to fp64. */
+static void act_row(int32_t dtype, const void* x, int64_t d, int64_t t, double* row) {
+    if (dtype == MOE_REF_F32) {
+        const float* p = (const float*)x + t * d;
+        for (int64_t i = 0; i < d; ++i) row[i] = (double)p[i];
+    } else {
+        const uint16_t* p = (const uint16_t*)x + t * d;
+        for (int64_t i = 0; i < d; ++i) row[i] = (double)bf16_bits_to_f32(p[i]);
+    }
+}
+
+static double dot(const double* a, const double* b, int64_t n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += a[i] * b[i];
+    return s;
+}
+
+static int shape_ok(const moe_ref_shape* s) {
+    if (!s) return 0;
+    if (s->T < 0 || s->d < 1 || s->E < 1 || s->k < 1 || s->k > s->E) return 0;
+    if (s->act_dtype != MOE_REF_F32 && s->act_dtype != MOE_REF_BF16) return 0;
+    if (s->wt_dtype < MOE_REF_F32 || s->wt_dtype > MOE_REF_MXFP4) return 0;
+    if (s->n_shared < 0 || s->n_shared > 1) return 0;
+    return 1;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Router logits                                                                               */
+/* ------------------------------------------------------------------------------------------ */
+int moe_ref_router_logits(const moe_ref_shape* s, const void* x, const void* w_router, const float* b,
+                          float* logits, double* logits64) {
+    if (!shape_ok(s) || (s->T > 0 && (!x || !w_router || !logits))) return -1;
+    const int64_t T = s->T, d = s->d, E = s->E;
+    /* The router weight has the activation dtype (f32 or bf16); upcast it once. */
+    double* wr = (double*)malloc(sizeof(double) * (size_t)(E * d));
+    for (int64_t e = 0; e < E; ++e) act_row(s->act_dtype, w_router, d, e, wr + e * d);
+#pragma omp parallel
+    {
+        double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            act_row(s->act_dtype, x, d, t, xr);
+            for (int64_t e = 0; e < E; ++e) {
+                double l = dot(xr, wr + e * d, d) + (b ? (double)b[e] : 0.0);
+                logits[t * E + e] = (float)l;
+                if (logits64) logits64[t * E + e] = l;
+            }
+        }
+        free(xr);
+    }
+    free(wr);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Top-k selection and gates                                                                   */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Total order used for selection: does expert i rank before expert j? */
+static int ranks_before(float li, int64_t i, float lj, int64_t j) {
+    int ni = isnan(li), nj = isnan(lj);
+    if (ni && nj) return i < j;
+    if (ni) return 0;
+    if (nj) return 1;
+    if (li > lj) return 1;
+    if (li < lj) return 0;
+    return i < j; /* equal values, +0 == -0 */
+}
+
+int moe_ref_topk(const moe_ref_shape* s, const float* logits, int32_t* topk_idx, double* topk_w) {
+    if (!shape_ok(s) || (s->T > 0 && (!logits || !topk_idx || !topk_w))) return -1;
+    const int64_t T = s->T, E = s->E, k = s->k;
+    char* taken = (char*)malloc((size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        /* k rounds of "best remaining expert" under the total order. */
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+            }
+            taken[best] = 1;
+            topk_idx[t * k + j] = (int32_t)best;
+        }
+        /* Gates: softmax over the selected logits, shifted by the largest (the first selected). */
+        double m = (double)l[topk_idx[t * k]];
+        double den = 0.0;
+        if (s->flags & MOE_REF_NO_RENORM) {
+            for (int64_t e = 0; e < E; ++e) den += exp((double)l[e] - m);
+        } else {
+            for (int64_t j = 0; j < k; ++j) den += exp((double)l[topk_idx[t * k + j]] - m);
+        }
+        for (int64_t j = 0; j < k; ++j) topk_w[t * k + j] = exp((double)l[topk_idx[t * k + j]] - m) / den;
+    }
+    free(taken);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Permute: stable counting sort by expert                                                     */
+/* ------------------------------------------------------------------------------------------ */
+int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* inv_perm) {
+    if (!shape_ok(s) || !counts || !offsets || (s->T > 0 && (!topk_idx || !perm || !inv_perm))) return -1;
+    const int64_t P = s->T * s->k, E = s->E;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (topk_idx[p] < 0 || topk_idx[p] >= E) return -1;
+        counts[topk_idx[p]] += 1;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    for (int64_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t p = 0; p < P; ++p) perm[cursor[topk_idx[p]]++] = (int32_t)p;
+    for (int64_t i = 0; i < P; ++i) inv_perm[perm[i]] = (int32_t)i;
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Expert FFN                                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+/* SwiGLU expert on n tokens (xs [n][d] fp64): ys [n][d] = W2 (silu(Wg x) * (Wu x)).
+   Weight tensors hold several experts; `e` picks one; f is this expert's d_ff. */
+static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, const void* w2, const uint8_t* w2s,
+                       int64_t e, int64_t d, int64_t f, const double* xs, int64_t n, double* ys) {
+    double* a = (double*)malloc(sizeof(double) * (size_t)(n * f + 1));
+    /* Gate and up projections, then the SwiGLU activation. */
+#pragma omp parallel
+    {
+        double* rg = (double*)malloc(sizeof(double) * (size_t)d);
+        double* ru = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < f; ++j) {
+            weight_row(wt, w13, w13s, e, 2 * f, d, j, rg);
+            weight_row(wt, w13, w13s, e, 2 * f, d, f + j, ru);
+            for (int64_t t = 0; t < n; ++t) {
+                double hg = dot(rg, xs + t * d, d);
+                double hu = dot(ru, xs + t * d, d);
+                a[t * f + j] = hg / (1.0 + exp(-hg)) * hu;
+            }
+        }
+        free(rg);
+        free(ru);
+    }
+    /* Down projection. */
+#pragma omp parallel
+    {
+        double* rd = (double*)malloc(sizeof(double) * (size_t)f);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < d; ++i) {
+            weight_row(wt, w2, w2s, e, d, f, i, rd);
+            for (int64_t t = 0; t < n; ++t) ys[t * d + i] = dot(rd, a + t * f, f);
+        }
+        free(rd);
+    }
+    free(a);
+}
+
+int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                        const moe_ref_weights* w, double* y_sorted, double* y_shared) {
+    if (!shape_ok(s) || !w || !offsets) return -1;
+    const int64_t T = s->T, d = s->d, f = s->f, E = s->E, k = s->k;
+    if (s->wt_dtype == MOE_REF_MXFP4 && (d % 32 || f % 32 || !w->w13_scale || !w->w2_scale)) return -1;
+    if (T > 0 && (!x || !perm || !y_sorted || !w->w13 || !w->w2)) return -1;
+    double* xs = (double*)malloc(sizeof(double) * (size_t)(T * d + 1));
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t n = offsets[e + 1] - offsets[e];
+        if (n == 0) continue;
+        for (int64_t i = 0; i < n; ++i) act_row(s->act_dtype, x, d, perm[offsets[e] + i] / k, xs + i * d);
+        expert_ffn(s->wt_dtype, w->w13, w->w13_scale, w->w2, w->w2_scale, e, d, f, xs, n,
+                   y_sorted + (int64_t)offsets[e] * d);
+    }
+    if (y_shared) {
+        if (s->n_shared != 1 || !w->s13 || !w->s2) { free(xs); return -1; }
+        if (s->wt_dtype == MOE_REF_MXFP4 && (s->f_shared % 32 || !w->s13_scale || !w->s2_scale)) { free(xs); return -1; }
+        for (int64_t t = 0; t < T; ++t) act_row(s->act_dtype, x, d, t, xs + t * d);
+        if (T > 0)
+            expert_ffn(s->wt_dtype, w->s13, w->s13_scale, w->s2, w->s2_scale, 0, d, s->f_shared, xs, T, y_shared);
+    }
+    free(xs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Combine                                                                                     */
+/* ------------------------------------------------------------------------------------------ */
+int moe_ref_combine(const moe_ref_shape* s, const double* y_sorted, const int32_t* inv_perm,
+                    const int32_t* topk_idx, const double* topk_w, const double* y_shared,
+                    const double* residual, const uint8_t* expert_mask, double* out) {
+    if (!shape_ok(s)) return -1;
+    const int64_t T = s->T, d = s->d, k = s->k, E = s->E;
+    if (T > 0 && (!y_sorted || !inv_perm || !topk_idx || !topk_w || !out)) return -1;
+    int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+    for (int64_t t = 0; t < T; ++t) {
+        /* The token's k selections, in ascending expert index (insertion sort). */
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t q = j;
+            while (q > 0 && topk_idx[t * k + order[q - 1]] > topk_idx[t * k + j]) {
+                order[q] = order[q - 1];
+                --q;
+            }
+            order[q] = j;
+        }
+        for (int64_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t q = 0; q < k; ++q) {
+                int64_t j = order[q];
+                int64_t e = topk_idx[t * k + j];
+                if (expert_mask && !expert_mask[e]) continue;
+                acc += topk_w[t * k + j] * y_sorted[(int64_t)inv_perm[t * k + j] * d + i];
+            }
+            if (y_shared && (!expert_mask || expert_mask[E])) acc += y_shared[t * d + i];
+            if (residual) acc += residual[t * d + i];
+            out[t * d + i] = acc;
+        }
+    }
+    free(order);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Whole layer                                                                                 */
+/* ------------------------------------------------------------------------------------------ */
+int moe_ref_layer_forward(const moe_ref_shape* s, const void* x, const void* w_router, const float* b,
+                          const moe_ref_weights* w, const uint8_t* expert_mask, double* out,
+                          int32_t* topk_idx_out, double* topk_w_out, float* logits_out) {
+    if (!shape_ok(s) || !w || (s->T > 0 && (!x || !w_router || !out))) return -1;
+    const int64_t T = s->T, d = s->d, E = s->E, k = s->k, P = T * k;
+    if (T == 0) return 0;
+    float* logits = (float*)malloc(sizeof(float) * (size_t)(T * E));
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)P);
+    double* g = (double*)malloc(sizeof(double) * (size_t)P);
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)P);
+    int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)P);
+    double* ys = (double*)malloc(sizeof(double) * (size_t)(P * d));
+    double* ysh = s->n_shared ? (double*)malloc(sizeof(double) * (size_t)(T * d)) : NULL;
+    int rc = moe_ref_router_logits(s, x, w_router, b, logits, NULL);
+    if (!rc) rc = moe_ref_topk(s, logits, idx, g);
+    if (!rc) rc = moe_ref_permute(s, idx, counts, offsets, perm, inv);
+    if (!rc) rc = moe_ref_grouped_ffn(s, x, perm, offsets, w, ys, ysh);
+    if (!rc) {
+        /* With MOE_REF_ACCUMULATE the caller's out holds the residual on entry. */
+        double* res = NULL;
+        if (s->flags & MOE_REF_ACCUMULATE) {
+            res = (double*)malloc(sizeof(double) * (size_t)(T * d));
+            memcpy(res, out, sizeof(double) * (size_t)(T * d));
+        }
+        rc = moe_ref_combine(s, ys, inv, idx, g, ysh, res, expert_mask, out);
+        free(res);
+    }
+    if (!rc && topk_idx_out) memcpy(topk_idx_out, idx, sizeof(int32_t) * (size_t)P);
+    if (!rc && topk_w_out) memcpy(topk_w_out, g, sizeof(double) * (size_t)P);
+    if (!rc && logits_out) memcpy(logits_out, logits, sizeof(float) * (size_t)(T * E));
+    free(logits); free(idx); free(g); free(counts); free(offsets); free(perm); free(inv); free(ys); free(ysh);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Residual stack glue                                                                         */
+/* ------------------------------------------------------------------------------------------ */
+int moe_ref_rmsnorm(int64_t T, int64_t d, const float* h, double eps, int32_t out_dtype, void* x_out) {
+    if (T < 0 || d < 1 || (T > 0 && (!h || !x_out))) return -1;
+    if (out_dtype != MOE_REF_F32 && out_dtype != MOE_REF_BF16) return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < d; ++i) ss += (double)h[t * d + i] * (double)h[t * d + i];
+        double inv = 1.0 / sqrt(ss / (double)d + eps);
+        for (int64_t i = 0; i < d; ++i) {
+            double v = (double)h[t * d + i] * inv;
+            if (out_dtype == MOE_REF_F32) ((float*)x_out)[t * d + i] = (float)v;
+            else ((uint16_t*)x_out)[t * d + i] = f64_to_bf16_rne(v);
+        }
+    }
+    return 0;
+}
+
+int moe_ref_stack_layer(const moe_ref_shape* s, float* h, const void* w_router, const float* b,
+                        const moe_ref_weights* w, int32_t* topk_idx_out) {
+    if (!shape_ok(s) || !h) return -1;
+    const int64_t T = s->T, d = s->d;
+    size_t xb = (size_t)(T * d) * (s->act_dtype == MOE_REF_F32 ? 4 : 2);
+    void* x = malloc(xb + 1);
+    double* out = (double*)malloc(sizeof(double) * (size_t)(T * d + 1));
+    int rc = moe_ref_rmsnorm(T, d, h, 1e-6, s->act_dtype, x);
+    moe_ref_shape s2 = *s;
+    s2.flags &= ~(uint32_t)MOE_REF_ACCUMULATE;
+    if (!rc) rc = moe_ref_layer_forward(&s2, x, w_router, b, w, NULL, out, topk_idx_out, NULL, NULL);
+    if (!rc)
+        for (int64_t i = 0; i < T * d; ++i) h[i] = (float)((double)h[i] + out[i]);
+    free(x);
+    free(out);
+    return rc;
+}

@@ -1,0 +1,109 @@
+/*
+ * moe_ref -- plain, slow, CPU oracle of the routed mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  The GPU product path never calls
+ * it and shares no code, header, table or helper with it.
+ *
+ * What it computes is the plain definition of a dropless top-k MoE layer:
+ * each token activates k of E routed experts (dothoosh.com FreeToken
+ * article, "FreeToken architecture and the sparsity puzzle": 6 of 256 routed
+ * experts in each of 43 layers), optionally plus one always-on shared expert
+ * (dothoosh.com TurboFieldfare article, "Background: Gemma 4 26B A4B": 8 of
+ * 128 routed plus 1 shared), over BF16 or MXFP4 expert weights (dothoosh.com
+ * FreeToken article, "Benchmarks and real performance"), and the partial sums
+ * of the experts merge exactly, with no estimate (same article, mechanism 1,
+ * the q* policy).  The pages give no formulas; the readings taken (softmax
+ * over the selected logits, SwiGLU experts, OCP MX v1.0 E2M1 values with one
+ * E8M0 scale per 32 elements) are listed with the project's design notes.
+ *
+ * Arithmetic: inputs are upcast exactly (bf16 -> fp32 is exact; MXFP4 ->
+ * fp32 by its definition); every dot product and sum accumulates in fp64 in
+ * ascending index order; floating results are returned in fp64, except the
+ * router logits, which are rounded once to fp32 because the expert selection
+ * is taken on fp32 logits, the precision the GPU kernel decides in.
+ *
+ * All pointers are host pointers owned by the caller.  Every function
+ * returns 0 on success and a negative value on invalid arguments.
+ */
+#ifndef MOE_REF_H
+#define MOE_REF_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_REF_F32 = 0, MOE_REF_BF16 = 1, MOE_REF_MXFP4 = 2 };
+enum { MOE_REF_NO_RENORM = 1u << 0, MOE_REF_ACCUMULATE = 1u << 1 };
+
+typedef struct {
+    int64_t T, d, f, E, k, n_shared, f_shared;
+    int32_t act_dtype;   /* MOE_REF_F32 or MOE_REF_BF16 (bf16 given as raw uint16 bits) */
+    int32_t wt_dtype;    /* MOE_REF_F32, MOE_REF_BF16 or MOE_REF_MXFP4 */
+    uint32_t flags;      /* MOE_REF_NO_RENORM, MOE_REF_ACCUMULATE */
+} moe_ref_shape;
+
+/* Routed weights w13 [E, 2f, d] (rows 0..f-1 gate, f..2f-1 up), w2 [E, d, f];
+   for MXFP4, codes [E, N, K/2] (element 2i in the low nibble of byte i) and
+   scales [E, N, K/32] (one E8M0 byte per 32 consecutive elements of a row).
+   Shared expert s13 [2 f_shared, d], s2 [d, f_shared] in the same format. */
+typedef struct {
+    const void* w13; const void* w2; const uint8_t* w13_scale; const uint8_t* w2_scale;
+    const void* s13; const void* s2; const uint8_t* s13_scale; const uint8_t* s2_scale;
+} moe_ref_weights;
+
+int moe_ref_num_threads(void);
+
+/* MXFP4 -> fp32: out[r*K + j] = (-1)^b3 * M[code & 7] * 2^(s - 127), s = 255 -> NaN. */
+int moe_ref_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out);
+
+/* Router logits l[t,e] = sum_i x[t,i] W_r[e,i] + b[e]; logits [T,E] fp32 (the fp64
+   value rounded once); logits64 (nullable) keeps the fp64 value. b may be NULL. */
+int moe_ref_router_logits(const moe_ref_shape* s, const void* x, const void* w_router, const float* b,
+                          float* logits, double* logits64);
+
+/* Top-k selection on fp32 logits [T,E] + gates.  topk_idx [T,k] in selection order
+   (larger logit first, equal logits -> lower expert index, NaN below every number,
+   +0 == -0); topk_w [T,k] = softmax over the selected logits (over all E logits
+   with MOE_REF_NO_RENORM). */
+int moe_ref_topk(const moe_ref_shape* s, const float* logits, int32_t* topk_idx, double* topk_w);
+
+/* Stable counting sort of the flat pairs p = t*k + j by expert: counts [E],
+   offsets [E+1] (exclusive prefix sum), perm [T*k] (pairs in ascending
+   (expert, p) order), inv_perm [T*k] (inv_perm[perm[i]] = i). */
+int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* inv_perm);
+
+/* Expert SwiGLU FFN on the sorted pairs: y_sorted[i] = W2_e (silu(W_g,e x) * (W_u,e x))
+   for x = x[perm[i]/k], e the expert owning sorted slot i; y_sorted [T*k, d].
+   y_shared [T, d] (nullable; needs n_shared = 1) = the shared expert on every token. */
+int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                        const moe_ref_weights* w, double* y_sorted, double* y_shared);
+
+/* out[t] = sum over the token's selected experts, in ascending expert index, of
+   g * y_sorted[inv_perm[t*k+j]], then + y_shared[t] (if given), then + residual[t]
+   (if given).  expert_mask (nullable, E + 1 bytes: routed experts then shared)
+   drops the terms of experts whose byte is 0. */
+int moe_ref_combine(const moe_ref_shape* s, const double* y_sorted, const int32_t* inv_perm,
+                    const int32_t* topk_idx, const double* topk_w, const double* y_shared,
+                    const double* residual, const uint8_t* expert_mask, double* out);
+
+/* Whole layer: logits -> top-k -> permute -> grouped FFN -> combine.  out [T,d] fp64.
+   topk_idx_out / topk_w_out / logits_out nullable.  expert_mask as in combine. */
+int moe_ref_layer_forward(const moe_ref_shape* s, const void* x, const void* w_router, const float* b,
+                          const moe_ref_weights* w, const uint8_t* expert_mask, double* out,
+                          int32_t* topk_idx_out, double* topk_w_out, float* logits_out);
+
+/* Parameter-free RMS normalisation x = h / sqrt(mean(h^2) + eps) per row of the fp32
+   residual stream h [T,d], rounded once (nearest-even) to the activation dtype. */
+int moe_ref_rmsnorm(int64_t T, int64_t d, const float* h, double eps, int32_t out_dtype, void* x_out);
+
+/* One layer of a residual MoE stack: h <- fp32(h + layer(rmsnorm(h))). */
+int moe_ref_stack_layer(const moe_ref_shape* s, float* h, const void* w_router, const float* b,
+                        const moe_ref_weights* w, int32_t* topk_idx_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

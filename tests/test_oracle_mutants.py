@@ -1,0 +1,61 @@
+"""Mutation check of the oracle's pins: each plausible mistake planted in a copy of the
+oracle's source (a dropped term, a wrong sign, index or order, a swapped operand) must make
+at least one pin in test_oracle_pins.py fail.  The mistakes are planted only in temporary
+CPU builds; the committed oracle is untouched.  CPU only."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_ref.c")
+
+MUTANTS = {
+    "swap_gate_up": ("a[t * f + j] = hg / (1.0 + exp(-hg)) * hu;", "a[t * f + j] = hu / (1.0 + exp(-hu)) * hg;"),
+    "silu_sign": ("hg / (1.0 + exp(-hg))", "hg / (1.0 + exp(hg))"),
+    "tie_break_high_index": ("return i < j; /* equal values", "return i > j; /* equal values"),
+    "nan_ranks_first": ("if (ni) return 0;", "if (ni) return 1;"),
+    "nibble_order": ("uint8_t code = (j % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);",
+                     "uint8_t code = (j % 2 == 1) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);"),
+    "nibble_order_rows": ("uint8_t code = (j % 2 == 0) ? (uint8_t)(c[j / 2] & 0xF) : (uint8_t)(c[j / 2] >> 4);",
+                          "uint8_t code = (j % 2 == 1) ? (uint8_t)(c[j / 2] & 0xF) : (uint8_t)(c[j / 2] >> 4);"),
+    "scale_bias": ("(int)scale - 127", "(int)scale - 128"),
+    "e2m1_table": ("4.0f, 6.0f}", "4.0f, 5.0f}"),
+    "unstable_perm": ("for (int64_t p = 0; p < P; ++p) perm[cursor", "for (int64_t p = P - 1; p >= 0; --p) perm[cursor"),
+    "combine_ignores_inv_perm": ("y_sorted[(int64_t)inv_perm[t * k + j] * d + i]", "y_sorted[(int64_t)(t * k + j) * d + i]"),
+    "gate_denominator_drops_term": ("for (int64_t j = 0; j < k; ++j) den +=", "for (int64_t j = 1; j < k; ++j) den +="),
+    "router_bias_dropped": ("+ (b ? (double)b[e] : 0.0)", "+ 0.0"),
+    "rmsnorm_mean": ("ss / (double)d + eps", "ss / (double)(d - 1) + eps"),
+    "shared_expert_dropped": ("if (y_shared && (!expert_mask || expert_mask[E]))", "if (0)"),
+    "residual_dropped": ("if (residual) acc += residual[t * d + i];", "(void)residual;"),
+    "pair_token_index": ("perm[offsets[e] + i] / k", "perm[offsets[e] + i] % k"),
+    "mask_ignored": ("if (expert_mask && !expert_mask[e]) continue;", "(void)e;"),
+    "x_upcast_truncated": ("row[i] = (double)bf16_bits_to_f32(p[i]);", "row[i] = (double)bf16_bits_to_f32(p[i] & 0xFFF0);"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as fh:
+        return fh.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = source.replace(old, new)
+    src = tmp_path / "moe_ref.c"
+    src.write_text(mutated)
+    (tmp_path / "moe_ref.h").write_text(open(os.path.join(ROOT, "oracle", "moe_ref.h")).read())
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-w",
+                    "-o", str(so), str(src), "-lm"], check=True)
+    env = dict(os.environ, MOE_REF_LIB=str(so), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"no pin caught mutant {name}:\n{r.stdout[-2000:]}"

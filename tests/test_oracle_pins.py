@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against what the mathematics and public definitions fix.
+
+Every test here checks the oracle against something other than itself: the OCP MX
+specification's E2M1 table, an independent bit-field decoding, brute-force sorting,
+numpy/scipy library routines (float64 matmul, stable argsort, softmax), closed forms
+and invariants of the layer (sparse == dense with zeroed gates, k = E with identical
+experts == one dense FFN, sum of counts == T*k, exact merge of partial sums).
+CPU only.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import moe_inputs as mi
+import oracle
+from _helpers import assert_close, bf16_to_f64, ref_select, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4 dequantisation (test iv of the layer's acceptance list)
+# ---------------------------------------------------------------------------------------------
+def _golden_e2m1():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx_v1.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            vals[int(c)] = float(v)
+    assert len(vals) == 16
+    return vals
+
+
+def _pack(codes):
+    """Pack a row of 4-bit codes (even element -> low nibble)."""
+    codes = np.asarray(codes, np.uint8)
+    return (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+
+
+def test_e2m1_matches_ocp_table_at_unit_scale():
+    gold = _golden_e2m1()
+    codes = np.array([c for c in range(16)] * 2, np.uint8)  # 32 elements = one scale block
+    out = oracle.mxfp4_dequant(_pack(codes)[None, :], np.array([[127]], np.uint8))[0]
+    for j, c in enumerate(codes):
+        assert out[j] == gold[int(c)], (c, out[j], gold[int(c)])
+        assert math.copysign(1.0, out[j]) == math.copysign(1.0, gold[int(c)]), ("sign of zero", c)
+
+
+def _independent_e2m1(code: int, scale: int) -> np.float32:
+    """Decode from the bit fields (sign, 2-bit exponent with bias 1, 1-bit mantissa) with exact
+    rationals, then scale by 2^(scale-127) and round once to fp32 (overflow -> inf)."""
+    if scale == 255:
+        return np.float32(np.nan)
+    sign = -1 if code & 8 else 1
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    v = mag * Fraction(2) ** (scale - 127)
+    with np.errstate(over="ignore"):
+        f = np.float32(float(v)) if v < Fraction(2) ** 1000 else np.float32(np.inf)
+    if f == 0:
+        return np.float32(-0.0) if sign < 0 else np.float32(0.0)
+    return np.float32(sign * f)
+
+
+def test_mxfp4_dequant_exhaustive_codes_by_scales():
+    """All 16 codes x 256 scale bytes, bit for bit (NaN for scale 0xFF, -0.0 for code 8)."""
+    codes = np.array(list(range(16)) * 2, np.uint8)  # 32 elements per row: one scale block
+    packed = np.tile(_pack(codes), (256, 1))
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    out = oracle.mxfp4_dequant(packed, scales)
+    for s in range(256):
+        for j in range(32):
+            want = _independent_e2m1(int(codes[j]), s)
+            got = out[s, j]
+            if np.isnan(want):
+                assert np.isnan(got), (s, j)
+            else:
+                assert got.view(np.uint32) == want.view(np.uint32), (s, int(codes[j]), got, want)
+
+
+def test_mxfp4_nibble_order_and_scale_blocks():
+    # Byte 0x21: element 0 = code 1 (0.5), element 1 = code 2 (1.0).
+    row = np.zeros(32, np.uint8)
+    row[0] = 0x21
+    out = oracle.mxfp4_dequant(row[None, :], np.array([[127, 127]], np.uint8))[0]
+    assert out[0] == 0.5 and out[1] == 1.0 and np.all(out[2:] == 0)
+    # Scales apply per 32 consecutive elements of a row.
+    codes = np.full(64, 2, np.uint8)  # all 1.0
+    out = oracle.mxfp4_dequant(_pack(codes)[None, :], np.array([[126, 129]], np.uint8))[0]
+    assert np.all(out[:32] == 0.5) and np.all(out[32:] == 4.0)
+    # Rows use their own scale rows.
+    out = oracle.mxfp4_dequant(np.tile(_pack(codes), (2, 1)), np.array([[127, 127], [128, 128]], np.uint8))
+    assert np.all(out[0] == 1.0) and np.all(out[1] == 2.0)
+
+
+# ---------------------------------------------------------------------------------------------
+# Top-k selection and gates
+# ---------------------------------------------------------------------------------------------
+class _S:
+    """Minimal shape object for direct oracle calls."""
+    def __init__(self, **kw):
+        self.T, self.d, self.f, self.E, self.k = 1, 8, 8, 8, 2
+        self.n_shared, self.f_shared, self.act, self.wt = 0, 0, "f32", "f32"
+        self.__dict__.update(kw)
+
+
+def test_topk_exhaustive_ties_E8_k2():
+    """Every logit pattern in {0,1,2}^8 (6561 rows) against a full stable sort by (-l, e)."""
+    grid = np.array(np.meshgrid(*([np.arange(3)] * 8), indexing="ij")).reshape(8, -1).T.astype(np.float32)
+    s = _S(E=8, k=2)
+    idx, _ = oracle.topk(s, grid)
+    for t in range(grid.shape[0]):
+        assert list(idx[t]) == ref_select(grid[t], 2), (grid[t], idx[t])
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_topk_total_order_nan_and_signed_zero(k):
+    rng = np.random.default_rng(7)
+    specials = np.array([np.nan, 0.0, -0.0, np.inf, -np.inf, 1.0, -1.0], np.float32)
+    rows = rng.choice(specials, size=(4000, 8)).astype(np.float32)
+    s = _S(E=8, k=k)
+    idx, _ = oracle.topk(s, rows)
+    for t in range(rows.shape[0]):
+        assert list(idx[t]) == ref_select(rows[t], k), (rows[t], idx[t])
+
+
+def test_gates_sum_to_one_and_match_softmax_of_selected():
+    rng = np.random.default_rng(1)
+    l = rng.normal(size=(500, 128)).astype(np.float32)
+    s = _S(E=128, k=8)
+    idx, g = oracle.topk(s, l)
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    sel = np.take_along_axis(l.astype(np.float64), idx.astype(np.int64), axis=1)
+    np.testing.assert_allclose(g, scipy.special.softmax(sel, axis=1), rtol=1e-13, atol=0)
+    assert np.all(np.diff(sel, axis=1) <= 0), "selection order must be descending logits"
+
+
+def test_no_renorm_with_k_equal_E_is_full_softmax():
+    rng = np.random.default_rng(2)
+    l = rng.normal(size=(200, 16)).astype(np.float32)
+    s = _S(E=16, k=16)
+    idx, g = oracle.topk(s, l, flags=oracle.NO_RENORM)
+    full = scipy.special.softmax(l.astype(np.float64), axis=1)
+    np.testing.assert_allclose(g, np.take_along_axis(full, idx.astype(np.int64), axis=1), rtol=1e-13)
+    # NO_RENORM with k < E: the selected entries of the full softmax (they no longer sum to 1).
+    s2 = _S(E=16, k=4)
+    idx2, g2 = oracle.topk(s2, l, flags=oracle.NO_RENORM)
+    np.testing.assert_allclose(g2, np.take_along_axis(full, idx2.astype(np.int64), axis=1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# Permute (test iii: counts sum to T*k)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 8, 2), (37, 128, 8), (300, 256, 6), (5, 4, 4)])
+def test_permute_is_stable_counting_sort(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    # Distinct experts per token, as top-k produces.
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    s = _S(E=E, k=k, T=T)
+    counts, offsets, perm, inv = oracle.permute(s, idx)
+    flat = idx.reshape(-1)
+    assert counts.sum() == T * k
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    np.testing.assert_array_equal(perm, np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(inv[perm], np.arange(T * k))
+    assert sorted(perm.tolist()) == list(range(T * k))
+
+
+def test_permute_skewed_all_tokens_one_expert():
+    T, E, k = 50, 16, 1
+    idx = np.full((T, k), 5, np.int32)
+    counts, offsets, perm, inv = oracle.permute(_S(E=E, k=k, T=T), idx)
+    assert counts[5] == T and counts.sum() == T
+    np.testing.assert_array_equal(perm, np.arange(T))
+    assert offsets[5] == 0 and offsets[6] == T and offsets[-1] == T
+
+
+# ---------------------------------------------------------------------------------------------
+# Router logits and expert FFN against numpy float64
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c0", "c1"])
+def test_router_logits_match_numpy_matmul(name):
+    s = mi.spec(name, T=16)
+    x = mi.host_x(s)
+    wr, _ = mi.host_router(s)
+    b = np.random.default_rng(0).normal(size=s.E).astype(np.float32)  # a nonzero bias must be added
+    l32, l64 = oracle.router_logits(s, x, wr, b)
+    want = to_f64(x) @ to_f64(wr).T + b.astype(np.float64)
+    np.testing.assert_allclose(l64, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # The fp32 logits are the fp64 value rounded once.
+    np.testing.assert_array_equal(l32, l64.astype(np.float32))
+
+
+def _np_ffn(w13, w2, xv, f):
+    h = w13 @ xv
+    g, u = h[:f], h[f:]
+    return w2 @ (g / (1.0 + np.exp(-g)) * u)
+
+
+@pytest.mark.parametrize("name", ["c0", "c1_small", "c3_small"])
+def test_expert_ffn_matches_numpy(name):
+    if name == "c0":
+        s = mi.spec("c0")
+    elif name == "c1_small":
+        s = mi.LayerSpec("c1s", 6, 256, 96, 8, 3, 1, 64, "bf16", "bf16", 1.0, 0.02, 0.02)
+    else:
+        s = mi.LayerSpec("c3s", 5, 128, 64, 8, 2, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.02)
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w = mi.host_experts(s)
+    sh = mi.host_experts(s, shared=True) if s.n_shared else None
+    l32, _ = oracle.router_logits(s, x, wr, b)
+    idx, _ = oracle.topk(s, l32)
+    counts, offsets, perm, inv = oracle.permute(s, idx)
+    ys, ysh = oracle.grouped_ffn(s, x, perm, offsets, w, sh)
+    if s.wt == "mxfp4":
+        E = s.E
+        w13 = oracle.mxfp4_dequant(w["w13"].reshape(E * 2 * s.f, -1), w["w13_scale"].reshape(E * 2 * s.f, -1))
+        w13 = w13.reshape(E, 2 * s.f, s.d).astype(np.float64)
+        w2 = oracle.mxfp4_dequant(w["w2"].reshape(E * s.d, -1), w["w2_scale"].reshape(E * s.d, -1))
+        w2 = w2.reshape(E, s.d, s.f).astype(np.float64)
+    else:
+        w13, w2 = to_f64(w["w13"]), to_f64(w["w2"])
+    xf = to_f64(x)
+    for i in range(s.T * s.k):
+        p = perm[i]
+        t, e = p // s.k, idx.reshape(-1)[p]
+        assert offsets[e] <= i < offsets[e + 1]
+        want = _np_ffn(w13[e], w2[e], xf[t], s.f)
+        np.testing.assert_allclose(ys[i], want, rtol=1e-10, atol=1e-12 * max(np.abs(want).max(), 1e-300))
+    if sh is not None:
+        for t in range(s.T):
+            want = _np_ffn(to_f64(sh["w13"][0]), to_f64(sh["w2"][0]), xf[t], s.f_shared)
+            np.testing.assert_allclose(ysh[t], want, rtol=1e-10, atol=1e-12 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------------------------
+# Layer invariants (tests i and ii of the acceptance list, and the exact partial-sum merge)
+# ---------------------------------------------------------------------------------------------
+def _small_layers():
+    return [
+        mi.spec("c0"),
+        mi.LayerSpec("c1s", 9, 128, 64, 16, 4, 1, 48, "bf16", "bf16", 1.0, 0.02, 0.02, seed=77),
+        mi.LayerSpec("c3s", 7, 128, 64, 12, 3, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.02, seed=78),
+    ]
+
+
+@pytest.mark.parametrize("s", _small_layers(), ids=lambda s: s.name)
+def test_sparse_equals_dense_with_zeroed_gates(s):
+    """Test (i): the sparse layer equals evaluating all E experts densely with the gates of
+    non-selected experts set to zero.  The dense side is numpy float64 written here
+    (own selection by sorting, own softmax, own FFN), so only fp64 rounding differs."""
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w = mi.host_experts(s)
+    sh = mi.host_experts(s, shared=True) if s.n_shared else None
+    ref = oracle.layer_forward(s, x, wr, b, w, sh)
+    xf = to_f64(x)
+    logits = (xf @ to_f64(wr).T + b.astype(np.float64)).astype(np.float32)
+    if s.wt == "mxfp4":
+        E = s.E
+        w13 = oracle.mxfp4_dequant(w["w13"].reshape(E * 2 * s.f, -1), w["w13_scale"].reshape(E * 2 * s.f, -1)).reshape(E, 2 * s.f, s.d)
+        w2 = oracle.mxfp4_dequant(w["w2"].reshape(E * s.d, -1), w["w2_scale"].reshape(E * s.d, -1)).reshape(E, s.d, s.f)
+        w13, w2 = w13.astype(np.float64), w2.astype(np.float64)
+    else:
+        w13, w2 = to_f64(w["w13"]), to_f64(w["w2"])
+    out = np.zeros((s.T, s.d))
+    for t in range(s.T):
+        sel = ref_select(logits[t], s.k)
+        assert sel == list(ref["topk_idx"][t])
+        gates = np.zeros(s.E)
+        z = np.exp(logits[t][sel].astype(np.float64) - float(logits[t][sel[0]]))
+        gates[sel] = z / z.sum()
+        for e in range(s.E):  # dense over every expert, zero gates included
+            out[t] += gates[e] * _np_ffn(w13[e], w2[e], xf[t], s.f)
+        if sh is not None:
+            out[t] += _np_ffn(to_f64(sh["w13"][0]), to_f64(sh["w2"][0]), xf[t], s.f_shared)
+    assert_close(ref["out"], out, rel=1e-10, abs_of_rms=1e-12, what="sparse vs dense")
+
+
+def test_k_equal_E_with_identical_experts_is_one_dense_ffn():
+    """Test (ii): with k = E and all experts equal, gates sum to 1 and the layer is one FFN."""
+    s = mi.LayerSpec("ident", 10, 64, 32, 8, 8, 0, 0, "f32", "f32", 0.5, 0.1, 0.1, seed=5)
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w = mi.host_experts(s, experts=[0] * s.E)  # expert 0's weights, E times
+    ref = oracle.layer_forward(s, x, wr, b, w)
+    xf = to_f64(x)
+    for t in range(s.T):
+        want = _np_ffn(to_f64(w["w13"][0]), to_f64(w["w2"][0]), xf[t], s.f)
+        np.testing.assert_allclose(ref["out"][t], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+    np.testing.assert_allclose(ref["topk_w"].sum(axis=1), 1.0, atol=1e-14)
+
+
+@pytest.mark.parametrize("s", _small_layers(), ids=lambda s: s.name)
+def test_split_sum_merges_exactly(s):
+    """Partial sums over any split of the experts merge to the full layer (the exact merge of
+    the q* policy's GPU and CPU partial results: dothoosh.com FreeToken article,
+    "FreeToken architecture and the sparsity puzzle", mechanism 1)."""
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w = mi.host_experts(s)
+    sh = mi.host_experts(s, shared=True) if s.n_shared else None
+    full = oracle.layer_forward(s, x, wr, b, w, sh)["out"]
+    rng = np.random.default_rng(11)
+    for _ in range(3):
+        mask_a = (rng.random(s.E + 1) < 0.5).astype(np.uint8)
+        mask_b = (1 - mask_a).astype(np.uint8)
+        a = oracle.layer_forward(s, x, wr, b, w, sh, expert_mask=mask_a)["out"]
+        # Accumulate the second part onto the first, as the merge does.
+        ab = oracle.layer_forward(s, x, wr, b, w, sh, expert_mask=mask_b, flags=oracle.ACCUMULATE, out_init=a)["out"]
+        assert_close(ab, full, rel=1e-12, abs_of_rms=1e-13, what="split-sum")
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_counts_sum_to_T_times_k_on_decode_config(T):
+    s = mi.spec("c1", T=T)
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    l32, _ = oracle.router_logits(s, x, wr, b)
+    idx, g = oracle.topk(s, l32)
+    counts, offsets, perm, inv = oracle.permute(s, idx)
+    assert counts.sum() == T * s.k
+    assert all(len(set(r)) == s.k for r in idx.tolist())
+
+
+# ---------------------------------------------------------------------------------------------
+# Residual-stack glue
+# ---------------------------------------------------------------------------------------------
+def _all_bf16_finite():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_to_f64(bits)
+    ok = np.isfinite(v)
+    return np.sort(np.unique(v[ok]))
+
+
+def _nearest_bf16_brute(v: float, table: np.ndarray) -> float:
+    i = np.searchsorted(table, v)
+    cands = [table[j] for j in (i - 1, i) if 0 <= j < len(table)]
+    best = min(cands, key=lambda c: abs(c - v))
+    ties = [c for c in cands if abs(c - v) == abs(best - v)]
+    if len(ties) > 1:  # tie: the one with an even last mantissa bit
+        ties = [c for c in ties if (np.float32(c).view(np.uint32) >> 16) & 1 == 0]
+    return float(ties[0])
+
+
+def test_rmsnorm_matches_closed_form_and_rounds_to_nearest_bf16():
+    table = _all_bf16_finite()
+    rng = np.random.default_rng(3)
+    h = rng.normal(size=(4, 256)).astype(np.float32)
+    x32 = oracle.rmsnorm(h, 1e-6, "f32")
+    hf = h.astype(np.float64)
+    want = hf / np.sqrt(np.mean(hf * hf, axis=1, keepdims=True) + 1e-6)
+    np.testing.assert_array_equal(x32, want.astype(np.float32))
+    xb = bf16_to_f64(oracle.rmsnorm(h, 1e-6, "bf16"))
+    for t in range(4):
+        for i in range(0, 256, 7):
+            assert xb[t, i] == _nearest_bf16_brute(want[t, i], table), (t, i)
+
+
+def test_stack_layer_is_residual_plus_layer_of_normed_input():
+    s = mi.LayerSpec("stk", 3, 128, 64, 16, 3, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.02, seed=91)
+    rng = np.random.default_rng(4)
+    h = rng.normal(size=(s.T, s.d)).astype(np.float32)
+    wr, b = mi.host_router(s)
+    w = mi.host_experts(s)
+    x = oracle.rmsnorm(h, 1e-6, "bf16")
+    lay = oracle.layer_forward(s, x, wr, b, w)
+    h2 = h.copy()
+    idx = oracle.stack_layer(s, h2, wr, b, w)
+    np.testing.assert_array_equal(idx, lay["topk_idx"])
+    np.testing.assert_array_equal(h2, (h.astype(np.float64) + lay["out"]).astype(np.float32))
+    # Zero expert weights leave the residual stream unchanged.
+    wz = {k: np.zeros_like(v) for k, v in w.items()}
+    h3 = h.copy()
+    oracle.stack_layer(s, h3, wr, b, wz)
+    np.testing.assert_array_equal(h3, h)
