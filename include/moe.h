@@ -1,0 +1,168 @@
+/*
+ * moe.h -- C-ABI of the MI355X (gfx950) routed mixture-of-experts layer.
+ *
+ * The layer is the sparse hot path the FreeToken pages describe: every token
+ * activates k of E routed experts per layer (DeepSeek-V4-Flash: 6 of 256 in
+ * each of 43 layers; dothoosh.com FreeToken article, "FreeToken architecture
+ * and the sparsity puzzle"; aihot.vn FreeToken article, "The gap it
+ * targets"), optionally beside one always-on shared expert (8 of 128 routed
+ * plus 1 shared; dothoosh.com TurboFieldfare article, "Background: Gemma 4
+ * 26B A4B"), with BF16 or MXFP4 expert weights (dothoosh.com FreeToken
+ * article, "Benchmarks and real performance"), and the partial sums of the
+ * experts merge exactly (same article, mechanism 1, the q* policy).  The
+ * pages give no formulas; this library computes the plain dropless top-k
+ * reading:
+ *   logits  l[t,e] = x[t] . W_r[e] + b[e]                        (fp32)
+ *   select  the k largest l[t,.], equal logits -> lower expert index,
+ *           NaN below every number, +0 == -0; topk_idx in that order
+ *   gates   g = softmax over the k selected logits (MOE_F_NO_RENORM: the
+ *           full softmax over all E, read at the selected experts)
+ *   expert  y_e(x) = W2_e (silu(Wg_e x) * (Wu_e x))   (SwiGLU)
+ *   out[t]  = sum over the token's experts, ascending expert index, of
+ *             g * y_e(x[t]), + shared(x[t]) when n_shared = 1
+ *
+ * Conventions for every entry point:
+ *  - `shape`, `weights` and arrays of pointers are HOST memory; every other
+ *    pointer is DEVICE memory owned by the caller, 16-byte aligned.
+ *  - Calls validate all arguments on the host first; on any failure they
+ *    return a negative moe_status and enqueue nothing.  On success they
+ *    enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    return without synchronising.  HIP launch errors come back as
+ *    MOE_ERR_HIP; faults inside kernels surface at the caller's next
+ *    synchronisation.
+ *  - The library allocates no device memory: scratch space comes from the
+ *    caller's workspace `ws` of at least moe_workspace_size(shape) bytes.
+ *    Calls that share a workspace must not overlap in time.
+ *  - T = 0 is a valid empty batch: MOE_OK, nothing enqueued.
+ *  - Results are deterministic run to run (fixed summation orders, no
+ *    floating-point atomics).
+ *
+ * Tensor layouts (row-major, last index contiguous):
+ *   x, out        [T, d_model]          act dtype (f32 or bf16)
+ *   w_router      [E, d_model]          act dtype;  b_router [E] f32 (may be NULL = 0)
+ *   w13           [E, 2*d_ff, d_model]  rows 0..d_ff-1 gate, d_ff..2*d_ff-1 up
+ *   w2            [E, d_model, d_ff]
+ *   s13, s2       shared expert, same layout with E = 1 and shared_d_ff
+ *   MXFP4 weights: codes [.., N, K/2] uint8, element 2i in the LOW nibble of
+ *     byte i, E2M1 per the OCP Microscaling v1.0 specification; scales
+ *     [.., N, K/32] uint8 E8M0 (2^(s-127); 0xFF = NaN), one per 32
+ *     consecutive elements of a row.
+ *   topk_idx [T, k] int32, topk_w [T, k] f32, logits [T, E] f32
+ *   counts [E], offsets [E+1], perm [T*k], inv_perm [T*k] int32
+ *   y_sorted [T*k, d_model], y_shared [T, d_model]  act dtype
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,  /* NULL/misaligned pointer, k not in [1,E], negative sizes, ... */
+    MOE_ERR_UNSUPPORTED = -2,  /* valid but not implemented: dtype pair, E > 1024, k > 64, ... */
+    MOE_ERR_WORKSPACE = -3,    /* ws_bytes < moe_workspace_size(shape) */
+    MOE_ERR_HIP = -4           /* a HIP launch reported an error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+enum {
+    MOE_F_NO_RENORM = 1u << 0,   /* gates = full-softmax probabilities at the selected experts */
+    MOE_F_ACCUMULATE = 1u << 1,  /* out += layer(x) instead of out = layer(x) */
+    MOE_F_FORCE_GEMV = 1u << 3,  /* use the decode (grouped GEMV) kernels at any T */
+    MOE_F_FORCE_GEMM = 1u << 4   /* use the prefill (grouped MFMA GEMM) kernels at any T */
+};
+
+/* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+
+typedef struct {
+    int32_t T;            /* tokens in the batch */
+    int32_t d_model;
+    int32_t d_ff;         /* routed expert hidden size */
+    int32_t n_experts;    /* E, routed experts */
+    int32_t top_k;        /* k */
+    int32_t n_shared;     /* 0 or 1 always-on shared expert (weight 1, no gate) */
+    int32_t shared_d_ff;
+    int32_t act_dtype;    /* moe_dtype: MOE_F32 or MOE_BF16 */
+    int32_t weight_dtype; /* moe_dtype: MOE_F32 (with f32 act), MOE_BF16 or MOE_MXFP4 (with bf16 act) */
+    uint32_t flags;       /* MOE_F_* */
+} moe_shape;
+
+typedef struct {
+    const void* w13;           /* [E, 2f, d] (MXFP4: codes [E, 2f, d/2]) */
+    const void* w2;            /* [E, d, f]  (MXFP4: codes [E, d, f/2]) */
+    const uint8_t* w13_scale;  /* MXFP4 only: [E, 2f, d/32] */
+    const uint8_t* w2_scale;   /* MXFP4 only: [E, d, f/32] */
+    const void* s13;           /* shared expert (n_shared = 1), else NULL */
+    const void* s2;
+    const uint8_t* s13_scale;
+    const uint8_t* s2_scale;
+} moe_weights;
+
+/* Bytes of device workspace the calls below need for this shape (0 on an invalid shape). */
+size_t moe_workspace_size(const moe_shape* shape);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* Router: logits -> top-k selection -> gates (steps a1, a2).
+   logits_in: NULL -> logits are computed from x, w_router, b_router; else a [T,E] f32
+   array used as the logits (x, w_router, b_router ignored).  logits_out (nullable)
+   receives the logits used.  topk_idx, topk_w as described above. */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+              const float* logits_in, int32_t* topk_idx, float* topk_w, float* logits_out,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Grouping of tokens by expert (step a3): stable counting sort of the flat pairs
+   p = t*k + j by expert id.  counts[e], offsets = exclusive prefix sum [E+1],
+   perm = pairs in ascending (expert, p) order, inv_perm[perm[i]] = i.
+   Every topk_idx entry must lie in [0, E). */
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert SwiGLU FFNs on the grouped pairs (steps a4, a5, a6, a7):
+   y_sorted[i] = y_e(x[perm[i] / k]) for the expert e whose segment
+   [offsets[e], offsets[e+1]) holds slot i; y_shared[t] = shared(x[t]) (NULL if
+   n_shared = 0).  perm/offsets as produced by moe_permute. */
+int moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
+                    const moe_weights* weights, void* y_sorted, void* y_shared,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Gate-weighted combine (step a8): out[t] = sum over j in ascending expert order
+   (= ascending inv_perm[t*k+j]) of topk_w[t,j] * y_sorted[inv_perm[t*k+j]],
+   + y_shared[t] (nullable), accumulated in fp32; with MOE_F_ACCUMULATE added to out. */
+int moe_combine(const moe_shape* shape, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
+                const void* y_shared, void* out, void* stream);
+
+/* Whole layer (steps a1..a8), fusing where it pays (at decode the combine is
+   fused into the down projection).  topk_idx_out (nullable) receives [T,k]. */
+int moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                      const moe_weights* weights, void* out, int32_t* topk_idx_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Residual stack of n_layers MoE layers (step a9) on the fp32 residual stream
+   h [T, d_model]: for each layer l, x = act(h / sqrt(mean(h^2) + 1e-6)) rounded to
+   the act dtype, then h += layer_l(x) in fp32.  w_router, b_router and weights are
+   HOST arrays of n_layers entries (each holding device pointers); b_router may be
+   NULL.  Routing is recomputed in every layer. */
+int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const void* const* w_router,
+                      const float* const* b_router, const moe_weights* weights,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP4 -> f32 dequantisation (step a7 on its own): out[r*K + j] =
+   (-1)^b3 * M[code & 7] * 2^(s - 127) with M = {0, .5, 1, 1.5, 2, 3, 4, 6},
+   NaN for s = 0xFF; codes [rows, K/2], scales [rows, K/32]; K % 32 == 0. */
+int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -73,6 +73,7 @@ def _load_host():
 def _load_dev():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  -- bind the library to torch's HIP runtime (loaded first)
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(DEV_LIB)
@@ -89,11 +90,11 @@ def _load_dev():
 
 
 def derive(key: int, x: int) -> int:
-    return int(_load_host().mg_derive(key & MASK64, x & MASK64))
+    return int(_load_host().mg_derive(int(key) & MASK64, int(x) & MASK64))
 
 
 def word(key: int, i: int) -> int:
-    return int(_load_host().mg_word(key & MASK64, i & MASK64))
+    return int(_load_host().mg_word(int(key) & MASK64, int(i) & MASK64))
 
 
 def root(seed: int) -> int:
@@ -180,7 +181,7 @@ def host_normal(n: int, key: int, sigma: float, dtype: str, start: int = 0) -> n
 
 
 def x_row_sub(t: int, attempt: int) -> int:
-    return ((attempt & 0xFFFFFFFF) << 32) | (t & 0xFFFFFFFF)
+    return ((int(attempt) & 0xFFFFFFFF) << 32) | (int(t) & 0xFFFFFFFF)
 
 
 def host_x(s: LayerSpec, layer: int = 0, attempts: Optional[np.ndarray] = None,

@@ -1,0 +1,339 @@
+// C-ABI of the MoE layer: host-side validation, workspace layout and kernel dispatch.
+// Every entry point validates all arguments before it enqueues anything; see include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int DECODE_MAX_T = 32;  // at or below: grouped GEMV kernels (HBM-bound decode)
+constexpr size_t ALIGN = 256;
+
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// Workspace regions (byte offsets from ws).
+struct Layout {
+    size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, act_list, tile_off, meta, blk, a, y, ysh, xn, total;
+};
+
+Layout layout(const moe_shape* s) {
+    Layout L{};
+    const size_t T = (size_t)s->T, E = (size_t)s->n_experts, k = (size_t)s->top_k, d = (size_t)s->d_model;
+    const size_t f = (size_t)s->d_ff, fs = s->n_shared ? (size_t)s->shared_d_ff : 0;
+    const size_t P = T * k;
+    const size_t ab = (size_t)act_bytes(s->act_dtype);
+    const size_t nblk = P > PERMUTE_SMALL_MAX ? (P + PERMUTE_CHUNK - 1) / PERMUTE_CHUNK : 0;
+    size_t o = 0;
+    L.logits = o; o = up(o + T * E * 4);
+    L.topk_idx = o; o = up(o + P * 4);
+    L.topk_w = o; o = up(o + P * 4);
+    L.counts = o; o = up(o + E * 4);
+    L.offsets = o; o = up(o + (E + 1) * 4);
+    L.perm = o; o = up(o + P * 4);
+    L.inv = o; o = up(o + P * 4);
+    L.act_list = o; o = up(o + (E + 1) * 4);
+    L.tile_off = o; o = up(o + (E + 2) * 4);
+    L.meta = o; o = up(o + 16 * 4);
+    L.blk = o; o = up(o + nblk * E * 4);
+    L.a = o; o = up(o + (P * f + T * fs) * 4);   // fp32 at decode, bf16 at prefill (fits either)
+    L.y = o; o = up(o + P * d * ab);
+    L.ysh = o; o = up(o + T * d * ab);
+    L.xn = o; o = up(o + T * d * ab);
+    L.total = o;
+    return L;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
+
+// Shape checks shared by every entry point.
+int check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->T < 0 || s->d_model < 1 || s->d_ff < 1 || s->n_experts < 1) return MOE_ERR_INVALID_ARG;
+    if (s->top_k < 1 || s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+    if (s->n_shared < 0 || s->n_shared > 1) return MOE_ERR_INVALID_ARG;
+    if (s->n_shared == 1 && s->shared_d_ff < 1) return MOE_ERR_INVALID_ARG;
+    const bool pair_ok = (s->act_dtype == MOE_F32 && s->weight_dtype == MOE_F32) ||
+                         (s->act_dtype == MOE_BF16 && (s->weight_dtype == MOE_BF16 || s->weight_dtype == MOE_MXFP4));
+    if (s->act_dtype < MOE_F32 || s->act_dtype > MOE_BF16 || s->weight_dtype < MOE_F32 || s->weight_dtype > MOE_MXFP4)
+        return MOE_ERR_INVALID_ARG;
+    if (!pair_ok) return MOE_ERR_UNSUPPORTED;
+    if (s->n_experts > MOE_MAX_EXPERTS || s->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)s->T * s->top_k > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    // 16-byte vector loads along every contiguous dimension.
+    const int vec = s->act_dtype == MOE_F32 ? 4 : 8;
+    const int fs = s->n_shared ? s->shared_d_ff : 32 * vec;  // no shared expert: nothing to check
+    if (s->weight_dtype == MOE_MXFP4) {
+        if (s->d_model % 32 || s->d_ff % 32 || fs % 32) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (s->d_model % vec || s->d_ff % vec || fs % vec) return MOE_ERR_INVALID_ARG;
+    }
+    if (s->flags & ~(uint32_t)(MOE_F_NO_RENORM | MOE_F_ACCUMULATE | MOE_F_FORCE_GEMV | MOE_F_FORCE_GEMM))
+        return MOE_ERR_INVALID_ARG;
+    if ((s->flags & MOE_F_FORCE_GEMV) && (s->flags & MOE_F_FORCE_GEMM)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+bool gemm_shape_ok(const moe_shape* s) {
+#ifndef MOE_HAVE_GEMM
+    (void)s;
+    return false;
+#else
+    const int fs = s->n_shared ? s->shared_d_ff : 64;
+    return s->act_dtype == MOE_BF16 && s->d_model % 64 == 0 && s->d_ff % 64 == 0 && fs % 64 == 0;
+#endif
+}
+
+// Which FFN kernels run: grouped GEMV (decode) or grouped MFMA GEMM (prefill).
+bool use_gemm(const moe_shape* s) {
+    if (s->flags & MOE_F_FORCE_GEMV) return false;
+    if (!gemm_shape_ok(s)) return false;
+    if (s->flags & MOE_F_FORCE_GEMM) return true;
+    return s->T > DECODE_MAX_T;
+}
+
+int check_weights(const moe_shape* s, const moe_weights* w) {
+    if (!w || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w->w13) || !aligned16(w->w2)) return MOE_ERR_INVALID_ARG;
+    if (s->weight_dtype == MOE_MXFP4 && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (s->n_shared) {
+        if (!w->s13 || !w->s2 || !aligned16(w->s13) || !aligned16(w->s2)) return MOE_ERR_INVALID_ARG;
+        if (s->weight_dtype == MOE_MXFP4 && (!w->s13_scale || !w->s2_scale)) return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+int ptr_ok(const void* p) { return p && aligned16(p); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                  \
+    do {                                               \
+        hipError_t _e = (expr);                        \
+        if (_e != hipSuccess) return MOE_ERR_HIP;      \
+    } while (0)
+
+// Routed + shared FFNs given ws-resident permute results; writes either the fused combine into
+// `out` (decode, T <= 64) or y_sorted / y_shared.
+int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* act_list,
+            const int32_t* tile_off, const int32_t* meta, const moe_weights* w, void* ws, const Layout& L,
+            void* y_sorted, void* y_shared, hipStream_t st) {
+    const int wt = s->weight_dtype;
+    const int fs = s->n_shared ? s->shared_d_ff : 0;
+    if (use_gemm(s)) {
+        uint16_t* a = at<uint16_t>(ws, L.a);
+        MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
+                                 w->s13, w->s13_scale, a, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
+                                 s->n_shared, st));
+        MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale,
+                                (uint16_t*)y_sorted, (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
+                                s->n_experts, s->n_shared, st));
+        return MOE_OK;
+    }
+    float* a = at<float>(ws, L.a);
+    MOE_TRY(launch_gemv_w13(wt, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13, w->s13_scale, a,
+                            s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, st));
+    MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
+                                  w->s2, w->s2_scale, y_sorted, y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
+                                  s->n_experts, s->n_shared, st));
+    return MOE_OK;
+}
+
+// The whole layer on x; out has dtype out_dtype (act dtype for the layer API, f32 for the stack).
+int run_layer(const moe_shape* s, const void* x, const void* w_router, const float* b, const moe_weights* w,
+              void* out, int out_dtype, bool accumulate, int32_t* idx_out, void* ws, const Layout& L,
+              hipStream_t st) {
+    const int T = s->T, E = s->n_experts, k = s->top_k, d = s->d_model, P = T * k;
+    const int fs = s->n_shared ? s->shared_d_ff : 0;
+    float* logits = at<float>(ws, L.logits);
+    int32_t* idx = at<int32_t>(ws, L.topk_idx);
+    float* g = at<float>(ws, L.topk_w);
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    int32_t* act_list = at<int32_t>(ws, L.act_list);
+    int32_t* tile_off = at<int32_t>(ws, L.tile_off);
+    int32_t* meta = at<int32_t>(ws, L.meta);
+    int32_t* blk = at<int32_t>(ws, L.blk);
+    const bool gemm = use_gemm(s);
+    if (gemm && T > DECODE_MAX_T)
+        MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, st));
+    else
+        MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b, logits, T, d, E, st));
+    MOE_TRY(launch_route_topk(logits, T, E, k, (s->flags & MOE_F_NO_RENORM) != 0, idx, g, idx_out, st));
+    MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
+    if (!gemm && T <= 64) {
+        float* a = at<float>(ws, L.a);
+        MOE_TRY(launch_gemv_w13(s->weight_dtype, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13,
+                                w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, st));
+        MOE_TRY(launch_gemv_w2_combine(s->weight_dtype, out_dtype == MOE_BF16, a, perm, offsets, act_list, meta, g,
+                                       w->w2, w->w2_scale, w->s2, w->s2_scale, out, T, d, s->d_ff, fs, k,
+                                       s->n_shared, accumulate, st));
+        return MOE_OK;
+    }
+    void* y = at<void>(ws, L.y);
+    void* ysh = s->n_shared ? at<void>(ws, L.ysh) : nullptr;
+    int rc = run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y, ysh, st);
+    if (rc != MOE_OK) return rc;
+    MOE_TRY(launch_combine(s->act_dtype == MOE_BF16 ? 1 : 0, out_dtype == MOE_BF16 ? 1 : 0, y, inv, g, ysh, out, T,
+                           d, k, accumulate, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape* s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return layout(s).total;
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const float* b_router, const float* logits_in,
+              int32_t* topk_idx, float* topk_w, float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if (!ptr_ok(topk_idx) || !ptr_ok(topk_w)) return MOE_ERR_INVALID_ARG;
+    if (logits_out && !aligned16(logits_out)) return MOE_ERR_INVALID_ARG;
+    if (logits_in) {
+        if (!aligned16(logits_in)) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (!ptr_ok(x) || !ptr_ok(w_router)) return MOE_ERR_INVALID_ARG;
+        if (b_router && !aligned16(b_router)) return MOE_ERR_INVALID_ARG;
+    }
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int T = s->T, E = s->n_experts;
+    const float* logits = logits_in;
+    if (!logits_in) {
+        float* dst = logits_out ? logits_out : at<float>(ws, L.logits);
+        if (use_gemm(s) && T > DECODE_MAX_T)
+            MOE_TRY(launch_route_logits_mfma(x, w_router, b_router, dst, T, s->d_model, E, st));
+        else
+            MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b_router, dst, T, s->d_model, E, st));
+        logits = dst;
+    } else if (logits_out && logits_out != logits_in) {
+        MOE_TRY(hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
+    }
+    MOE_TRY(launch_route_topk(logits, T, E, s->top_k, (s->flags & MOE_F_NO_RENORM) != 0, topk_idx, topk_w, nullptr, st));
+    return MOE_OK;
+}
+
+int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if (!ptr_ok(topk_idx) || !ptr_ok(counts) || !ptr_ok(offsets) || !ptr_ok(perm) || !ptr_ok(inv_perm))
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    MOE_TRY(launch_permute(topk_idx, s->T * s->top_k, s->n_experts, GEMM_BM, counts, offsets, perm, inv_perm,
+                           at<int32_t>(ws, L.act_list), at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.meta),
+                           at<int32_t>(ws, L.blk), (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                    const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if ((rc = check_weights(s, w)) != MOE_OK) return rc;
+    if (!ptr_ok(x) || !ptr_ok(perm) || !ptr_ok(offsets) || !ptr_ok(y_sorted)) return MOE_ERR_INVALID_ARG;
+    if (s->n_shared ? !ptr_ok(y_shared) : y_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t* act_list = at<int32_t>(ws, L.act_list);
+    int32_t* tile_off = at<int32_t>(ws, L.tile_off);
+    int32_t* meta = at<int32_t>(ws, L.meta);
+    MOE_TRY(launch_active_from_offsets(offsets, s->n_experts, GEMM_BM, act_list, tile_off, meta, st));
+    return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, st);
+}
+
+int moe_combine(const moe_shape* s, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
+                const void* y_shared, void* out, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if (!ptr_ok(y_sorted) || !ptr_ok(inv_perm) || !ptr_ok(topk_w) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
+    if (y_shared && !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
+    const int dt = s->act_dtype == MOE_BF16 ? 1 : 0;
+    MOE_TRY(launch_combine(dt, dt, y_sorted, inv_perm, topk_w, y_shared, out, s->T, s->d_model, s->top_k,
+                           (s->flags & MOE_F_ACCUMULATE) != 0, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                      const moe_weights* w, void* out, int32_t* topk_idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T == 0) return MOE_OK;
+    if ((rc = check_weights(s, w)) != MOE_OK) return rc;
+    if (!ptr_ok(x) || !ptr_ok(w_router) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
+    if ((b_router && !aligned16(b_router)) || (topk_idx_out && !aligned16(topk_idx_out))) return MOE_ERR_INVALID_ARG;
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return run_layer(s, x, w_router, b_router, w, out, s->act_dtype, (s->flags & MOE_F_ACCUMULATE) != 0,
+                     topk_idx_out, ws, L, (hipStream_t)stream);
+}
+
+int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void* const* w_router,
+                      const float* const* b_router, const moe_weights* w, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (n_layers < 0 || !w_router || !w) return MOE_ERR_INVALID_ARG;
+    if (s->T == 0 || n_layers == 0) return MOE_OK;
+    if (!ptr_ok(h)) return MOE_ERR_INVALID_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((rc = check_weights(s, &w[l])) != MOE_OK) return rc;
+        if (!ptr_ok(w_router[l])) return MOE_ERR_INVALID_ARG;
+        if (b_router && b_router[l] && !aligned16(b_router[l])) return MOE_ERR_INVALID_ARG;
+    }
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    void* xn = at<void>(ws, L.xn);
+    for (int l = 0; l < n_layers; ++l) {
+        MOE_TRY(launch_rmsnorm(s->act_dtype == MOE_BF16 ? 1 : 0, h, xn, s->T, s->d_model, 1e-6f, st));
+        rc = run_layer(s, xn, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr, ws,
+                       L, st);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
+}
+
+int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out, void* stream) {
+    if (rows < 0 || K < 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0 || K == 0) return MOE_OK;
+    if (!ptr_ok(codes) || !scales || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_mxfp4_dequant(codes, scales, out, rows, K, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_E 1024
+#define MOE_MAX_K 64
+#define PERMUTE_SMALL_MAX 4096
+#define PERMUTE_CHUNK 2048
+#define GEMM_BM 128  // token rows per grouped-GEMM tile (tile list granularity)
+
+namespace moe {
+
+hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
+                               int T, int d, int E, hipStream_t st);
+hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
+                                    int E, hipStream_t st);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, bool no_renorm, int32_t* idx, float* w,
+                             int32_t* idx2, hipStream_t st);
+
+hipError_t launch_permute(const int32_t* idx, int P, int E, int bm, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int32_t* act_list, int32_t* tile_off, int32_t* meta,
+                          int32_t* blk, hipStream_t st);
+hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int bm, int32_t* act_list, int32_t* tile_off,
+                                      int32_t* meta, hipStream_t st);
+
+hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int32_t* offsets,
+                           const int32_t* act_list, const int32_t* meta, const void* w13, const uint8_t* w13s,
+                           const void* s13, const uint8_t* s13s, float* a, int T, int d, int f, int fs, int k,
+                           int E, int n_shared, hipStream_t st);
+hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
+                                  const int32_t* act_list, const int32_t* meta, const float* topk_w, const void* w2,
+                                  const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* out, int T, int d,
+                                  int f, int fs, int k, int n_shared, bool accumulate, hipStream_t st);
+hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
+                                 const int32_t* act_list, const int32_t* meta, const void* w2, const uint8_t* w2s,
+                                 const void* s2, const uint8_t* s2s, void* y, void* y_shared, int T, int d, int f,
+                                 int fs, int k, int E, int n_shared, hipStream_t st);
+
+// Prefill grouped GEMM (MFMA).  a_bf16: routed [P, f] then shared [T, fs].
+hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, const int32_t* offsets,
+                            const int32_t* tile_off, const int32_t* meta, const void* w13, const uint8_t* w13s,
+                            const void* s13, const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k,
+                            int E, int n_shared, hipStream_t st);
+hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t* tile_off,
+                           const int32_t* meta, const void* w2, const uint8_t* w2s, const void* s2,
+                           const uint8_t* s2s, uint16_t* y, uint16_t* y_shared, int T, int d, int f, int fs, int k,
+                           int E, int n_shared, hipStream_t st);
+
+hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
+                          const void* ysh, void* out, int T, int d, int k, bool accumulate, hipStream_t st);
+hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, float* out, int64_t rows, int64_t K,
+                                hipStream_t st);
+hipError_t launch_rmsnorm(int x_dtype, const float* h, void* x, int T, int d, float eps, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,166 @@
+// Router (steps a1, a2): logits l = x W_r^T + b, then a wavefront per token selects the
+// k largest logits (ties -> lowest expert index) and forms the softmax gates.
+//
+// The pages say only that each token is routed to k experts per layer and that the
+// routing changes from token to token (dothoosh.com FreeToken article, "FreeToken
+// architecture and the sparsity puzzle" and mechanism 2); the softmax-over-selected
+// gating and the tie rule are this library's stated reading.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------------------------------------
+// Logits, decode shape: one wavefront per expert row of W_r, all tokens of the batch.
+// The row (d elements) is streamed once with 16-byte loads; tokens are taken TG at a time.
+// ------------------------------------------------------------------------------------------------
+template <typename A> struct vec16;
+template <> struct vec16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void load(const float* p, float* v) {
+        float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+};
+template <> struct vec16<uint16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void load(const uint16_t* p, float* v) {
+        uint4 q = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+};
+
+template <typename A, int TG>
+__global__ void __launch_bounds__(256) route_logits_gemv(const A* __restrict__ x, const A* __restrict__ wr,
+                                                         const float* __restrict__ b, float* __restrict__ logits,
+                                                         int T, int d, int E) {
+    constexpr int V = vec16<A>::N;
+    const int e = blockIdx.x * 4 + wave_id();
+    if (e >= E) return;
+    const int lane = lane_id();
+    const A* w = wr + (int64_t)e * d;
+    const float bias = b ? b[e] : 0.0f;
+    for (int t0 = 0; t0 < T; t0 += TG) {
+        float acc[TG];
+#pragma unroll
+        for (int q = 0; q < TG; ++q) acc[q] = 0.0f;
+        for (int i = lane * V; i < d; i += MOE_WAVE * V) {
+            float wv[V];
+            vec16<A>::load(w + i, wv);
+#pragma unroll
+            for (int q = 0; q < TG; ++q) {
+                if (t0 + q < T) {
+                    float xv[V];
+                    vec16<A>::load(x + (int64_t)(t0 + q) * d + i, xv);
+#pragma unroll
+                    for (int v = 0; v < V; ++v) acc[q] = fmaf(wv[v], xv[v], acc[q]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < TG; ++q) {
+            float s = wave_sum(acc[q]);
+            if (lane == 0 && t0 + q < T) logits[(int64_t)(t0 + q) * E + e] = s + bias;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Top-k + gates: one wavefront per token.  Each lane holds EPL logits (expert lane + 64 j) as
+// 64-bit keys that order the logits totally: high word = order-preserving image of the fp32
+// value (NaN lowest, -0 mapped to +0), low word = ~expert so that equal values prefer the
+// lower expert.  k rounds of a wave-wide max pick the experts in selection order.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+    uint32_t ord;
+    if (v != v) {
+        ord = 0u;
+    } else {
+        uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
+        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+template <int EPL>
+__global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logits, int T, int E, int k,
+                                                  uint32_t no_renorm, int32_t* __restrict__ idx_out,
+                                                  float* __restrict__ w_out, int32_t* __restrict__ idx_out2) {
+    const int t = blockIdx.x * 4 + wave_id();
+    if (t >= T) return;
+    const int lane = lane_id();
+    const float* l = logits + (int64_t)t * E;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        int e = lane + MOE_WAVE * j;
+        key[j] = (e < E) ? select_key(l[e], e) : 0ull;
+    }
+    int my_sel = 0;
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) best = key[j] > best ? key[j] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + MOE_WAVE * j == e) key[j] = 0ull;
+        if (lane == r) my_sel = e;
+    }
+    // Gates: exp(l - m) with m the first (largest) selected logit.
+    const float m = l[__shfl(my_sel, 0, MOE_WAVE)];
+    const float term = (lane < k) ? expf(l[my_sel] - m) : 0.0f;
+    float den;
+    if (no_renorm) {
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            int e = lane + MOE_WAVE * j;
+            if (e < E) part += expf(l[e] - m);
+        }
+        den = wave_sum(part);
+    } else {
+        den = wave_sum(term);
+    }
+    if (lane < k) {
+        idx_out[(int64_t)t * k + lane] = my_sel;
+        w_out[(int64_t)t * k + lane] = term / den;
+        if (idx_out2) idx_out2[(int64_t)t * k + lane] = my_sel;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Host launchers
+// ------------------------------------------------------------------------------------------------
+hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
+                               int T, int d, int E, hipStream_t st) {
+    dim3 grid((E + 3) / 4), block(256);
+    if (act_dtype == 0)
+        hipLaunchKernelGGL((route_logits_gemv<float, 8>), grid, block, 0, st, (const float*)x, (const float*)wr, b,
+                           logits, T, d, E);
+    else
+        hipLaunchKernelGGL((route_logits_gemv<uint16_t, 8>), grid, block, 0, st, (const uint16_t*)x,
+                           (const uint16_t*)wr, b, logits, T, d, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, bool no_renorm, int32_t* idx, float* w,
+                             int32_t* idx2, hipStream_t st) {
+    dim3 grid((T + 3) / 4), block(256);
+    uint32_t nr = no_renorm ? 1u : 0u;
+    if (E <= 64)
+        hipLaunchKernelGGL((route_topk<1>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    else if (E <= 128)
+        hipLaunchKernelGGL((route_topk<2>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    else if (E <= 256)
+        hipLaunchKernelGGL((route_topk<4>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    else if (E <= 512)
+        hipLaunchKernelGGL((route_topk<8>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    else
+        hipLaunchKernelGGL((route_topk<16>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    return hipGetLastError();
+}
+
+}  // namespace moe

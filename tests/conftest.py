@@ -3,6 +3,9 @@ import sys
 
 import pytest
 
+# Load torch (and its HIP runtime) before any library of this repository that links HIP.
+import torch  # noqa: F401,E402
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
