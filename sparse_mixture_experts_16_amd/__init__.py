@@ -27,7 +27,8 @@ MAX_EXPERTS, MAX_TOPK = 1024, 64
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_layer_forward", "moe_stack_forward", "moe_mxfp4_dequant"]
+           "moe_combine", "moe_layer_forward", "moe_stack_forward", "moe_mxfp4_dequant", "moe_profile_kernel"]
+KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
 
 
 class Shape(ctypes.Structure):
@@ -57,6 +58,7 @@ _lib.moe_combine.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+_lib.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
 for _n in EXPORTS[2:]:
     getattr(_lib, _n).restype = ctypes.c_int
 
@@ -183,6 +185,11 @@ def mxfp4_dequant(codes, scales, out, stream=None):
     rows = codes.numel() // half_k
     _check(_lib.moe_mxfp4_dequant(_ptr(codes), _ptr(scales), rows, 2 * half_k, _ptr(out), _stream(stream)),
            "moe_mxfp4_dequant")
+
+
+def profile_kernel(kernel: int, ev_start=None, ev_stop=None):
+    """Bracket launches of one kernel class with caller-owned hipEvent_t handles (ints)."""
+    _check(_lib.moe_profile_kernel(kernel, ev_start, ev_stop), "moe_profile_kernel")
 
 
 # ------------------------------------------------------------------------------------------------

@@ -83,14 +83,10 @@ int check_shape(const moe_shape* s) {
     return MOE_OK;
 }
 
+// The MFMA kernels tile K by 64 and the gate/up columns by 64.
 bool gemm_shape_ok(const moe_shape* s) {
-#ifndef MOE_HAVE_GEMM
-    (void)s;
-    return false;
-#else
     const int fs = s->n_shared ? s->shared_d_ff : 64;
     return s->act_dtype == MOE_BF16 && s->d_model % 64 == 0 && s->d_ff % 64 == 0 && fs % 64 == 0;
-#endif
 }
 
 // Which FFN kernels run: grouped GEMV (decode) or grouped MFMA GEMM (prefill).
@@ -122,6 +118,16 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
         if (_e != hipSuccess) return MOE_ERR_HIP;      \
     } while (0)
 
+// Optional timing hook (moe_profile_kernel): events recorded around one kernel class.
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+int g_prof_kernel = -1;
+
+inline hipError_t prof_mark(int kernel, bool start, hipStream_t st) {
+    if (kernel != g_prof_kernel) return hipSuccess;
+    hipEvent_t ev = start ? g_prof_start : g_prof_stop;
+    return ev ? hipEventRecord(ev, st) : hipSuccess;
+}
+
 // Routed + shared FFNs given ws-resident permute results; writes either the fused combine into
 // `out` (decode, T <= 64) or y_sorted / y_shared.
 int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* act_list,
@@ -131,20 +137,28 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
     const int fs = s->n_shared ? s->shared_d_ff : 0;
     if (use_gemm(s)) {
         uint16_t* a = at<uint16_t>(ws, L.a);
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
         MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
                                  w->s13, w->s13_scale, a, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
                                  s->n_shared, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
         MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale,
                                 (uint16_t*)y_sorted, (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
                                 s->n_experts, s->n_shared, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
         return MOE_OK;
     }
     float* a = at<float>(ws, L.a);
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
     MOE_TRY(launch_gemv_w13(wt, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13, w->s13_scale, a,
                             s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, st));
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
     MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
                                   w->s2, w->s2_scale, y_sorted, y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
                                   s->n_experts, s->n_shared, st));
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
     return MOE_OK;
 }
 
@@ -174,11 +188,15 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
     if (!gemm && T <= 64) {
         float* a = at<float>(ws, L.a);
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
         MOE_TRY(launch_gemv_w13(s->weight_dtype, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13,
                                 w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
         MOE_TRY(launch_gemv_w2_combine(s->weight_dtype, out_dtype == MOE_BF16, a, perm, offsets, act_list, meta, g,
                                        w->w2, w->w2_scale, w->s2, w->s2_scale, out, T, d, s->d_ff, fs, k,
                                        s->n_shared, accumulate, st));
+        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
         return MOE_OK;
     }
     void* y = at<void>(ws, L.y);
@@ -325,6 +343,15 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
                        L, st);
         if (rc != MOE_OK) return rc;
     }
+    return MOE_OK;
+}
+
+int moe_profile_kernel(int kernel, void* ev_start, void* ev_stop) {
+    if (kernel < -1 || kernel > MOE_KERNEL_FFN_DOWN) return MOE_ERR_INVALID_ARG;
+    if (kernel >= 0 && (!ev_start || !ev_stop)) return MOE_ERR_INVALID_ARG;
+    g_prof_kernel = kernel;
+    g_prof_start = (hipEvent_t)ev_start;
+    g_prof_stop = (hipEvent_t)ev_stop;
     return MOE_OK;
 }
 

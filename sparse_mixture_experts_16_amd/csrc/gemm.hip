@@ -1,25 +1,352 @@
-// Prefill path of the expert FFNs (grouped MFMA GEMM) -- placeholder launchers until the MFMA
-// kernels land; the host dispatch never selects this path while they report hipErrorNotSupported.
+// Prefill path (steps a1, a4..a7 at large T): grouped GEMM on the gfx950 matrix cores.
+//
+// At prefill thousands of tokens reach nearly every expert (dothoosh.com FreeToken article,
+// "FreeToken architecture and the sparsity puzzle", first failure mode), so each expert's
+// weights are read once and reused across all of its tokens: this is a dense contraction per
+// expert and belongs on MFMA.  One kernel template covers three products:
+//
+//   MODE_W13     a[pos, j] = silu(x_t . Wg_e[j]) * (x_t . Wu_e[j])   A rows gathered via perm
+//   MODE_W2      y[pos, n] = a[pos] . W2_e[n]                          A rows contiguous
+//   MODE_ROUTER  l[t, e]   = x_t . W_r[e] + b[e]                       one group, fp32 out
+//
+// Tiles are 128 (token rows) x 128 (weight rows) x 64 (K); four wavefronts each own a 64x64
+// quarter computed with v_mfma_f32_16x16x32_bf16 (operand lane layout: lane l holds row l%16,
+// k = 8*(l/16)..+7 of A and column l%16 of B; the accumulator holds column l%16, rows
+// 4*(l/16)..+3).  Tiles stream through double-buffered LDS rows padded to 72 bf16 so that the
+// 16-byte fragment reads of 8 consecutive rows fall on distinct banks.  MXFP4 weights are
+// expanded to bf16 (exactly: E2M1 x 2^k fits bf16) with the scaled converts on the way into
+// LDS.  For MODE_W13 the LDS B tile interleaves 32 gate rows and the matching 32 up rows per
+// wavefront column, so the SwiGLU pairs meet in the same lane and the activation is fused
+// into the epilogue.
+//
+// Tile order: a flat list over (group, m-tile, n-tile), n fastest, built per workgroup from
+// the expert offsets; workgroup b takes list entry (b % 8) * (grid / 8) + b / 8 so that each
+// of the 8 XCDs walks a contiguous stretch of the list and an expert's weight tiles are
+// shared in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
+#include "wchunk.h"
 
 namespace moe {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int TBM = 128, TBN = 128, TBK = 64, LDP = TBK + 8;
+enum { MODE_W13 = 0, MODE_W2 = 1, MODE_ROUTER = 2 };
+
+struct GemmArgs {
+    const uint16_t* A;        // W13/ROUTER: x [T, d]; W2: a (routed [P, f], shared at +P*f as [T, fs])
+    const int32_t* perm;      // W13: sorted slot -> pair
+    const int32_t* offsets;   // [E+1] (W13/W2)
+    const uint8_t* w;         // routed weights (ROUTER: W_r [E, d] bf16)
+    const uint8_t* wsc;       // routed MXFP4 scales
+    const uint8_t* sw;        // shared expert weights
+    const uint8_t* swsc;
+    const float* bias;        // ROUTER: b [E] or NULL
+    void* out;                // W13: a (bf16); W2: y (bf16) [P, d]; ROUTER: logits (f32) [T, E]
+    uint16_t* out_sh;         // W2: y_shared [T, d]
+    int T, d, f, fs, k, E, n_shared;
+};
+
+__device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
+    bf16x2_t v;
+    switch (sel) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3); break;
+    }
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4); a 0xFF scale gives NaN.
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
+    const float sc = e8m0_to_f32(s);
+    uint4 r;
+    r.x = cvt2(w, sc, 0);
+    r.y = cvt2(w, sc, 1);
+    r.z = cvt2(w, sc, 2);
+    r.w = cvt2(w, sc, 3);
+    if (s == 255u) r = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    return r;
+}
+
+template <int MODE, int WT>
+__global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][TBM * LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][TBN * LDP];
+    __shared__ int s_pref[MOE_MAX_E + 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+    const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
+    const int P = p.T * p.k;
+
+    // ---- flat tile list: tiles of group g = ceil(rows_g / 128) * ntiles_g
+    auto tiles_of = [&](int g) -> int {
+        int rows, nt;
+        if (MODE == MODE_ROUTER) {
+            rows = p.T;
+            nt = (p.E + TBN - 1) / TBN;
+        } else {
+            const bool sh = g == p.E;
+            rows = sh ? p.T : p.offsets[g + 1] - p.offsets[g];
+            nt = (MODE == MODE_W13) ? (sh ? p.fs : p.f) / 64 : (p.d + TBN - 1) / TBN;
+        }
+        return ((rows + TBM - 1) / TBM) * nt;
+    };
+    if (wv == 0) {
+        const int per = (G + 63) / 64;
+        const int lo = min(lane * per, G), hi = min(lo + per, G);
+        int sum = 0;
+        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += u;
+        }
+        int run = incl - sum;
+        for (int g = lo; g < hi; ++g) {
+            s_pref[g] = run;
+            run += tiles_of(g);
+        }
+        if (lane == 63) s_pref[G] = incl;
+    }
+    __syncthreads();
+
+    const int nb = gridDim.x;  // a multiple of 8
+    const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+    if (L >= s_pref[G]) return;
+    int g = 0;
+    {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= L) lo = mid;
+            else hi = mid;
+        }
+        g = lo;
+    }
+    const bool shared = (MODE != MODE_ROUTER) && g == p.E;
+    const int fg = shared ? p.fs : p.f;
+    int rows_g, base, ntiles, K, N;
+    const uint8_t* W;
+    const uint8_t* WS;
+    if (MODE == MODE_ROUTER) {
+        rows_g = p.T; base = 0; K = p.d; N = p.E; ntiles = (p.E + TBN - 1) / TBN;
+        W = p.w; WS = nullptr;
+    } else {
+        rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
+        base = shared ? 0 : p.offsets[g];
+        if (MODE == MODE_W13) { K = p.d; N = 2 * fg; ntiles = fg / 64; }
+        else { K = fg; N = p.d; ntiles = (p.d + TBN - 1) / TBN; }
+        const int64_t rb = row_bytes(WT, K), sb = K / 32;
+        W = shared ? p.sw : p.w + (int64_t)g * N * rb;
+        WS = (WT == 2) ? (shared ? p.swsc : p.wsc + (int64_t)g * N * sb) : nullptr;
+    }
+    const int local = L - s_pref[g];
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int m0 = mt * TBM;
+    const int mrows = min(TBM, rows_g - m0);
+    const int64_t wrb = row_bytes(WT, K), wsb = K / 32;
+
+    // ---- this thread's global source rows for the A and B tiles
+    const int kc = tid & 7;  // 16-byte chunk within a 64-wide K slice (bf16)
+    const uint16_t* arow[4];
+    const uint8_t* brow[4];
+    const uint8_t* bsrow = nullptr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        if (r < mrows) {
+            int64_t src;
+            if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
+            else if (MODE == MODE_W2) src = shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
+            else src = (int64_t)(m0 + r) * p.d;
+            arow[i] = p.A + src;
+        } else {
+            arow[i] = nullptr;
+        }
+    }
+    auto wrow_of = [&](int n) -> int {  // LDS B row -> weight row (or -1)
+        if (MODE == MODE_W13) {
+            const int j0 = nt * 64, h = n >> 6, w = n & 63;
+            return w < 32 ? j0 + h * 32 + w : fg + j0 + h * 32 + (w - 32);
+        }
+        const int r = nt * TBN + n;
+        return r < N ? r : -1;
+    };
+    if (WT == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int wr = wrow_of((tid >> 3) + 32 * i);
+            brow[i] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
+        }
+    } else {
+        const int wr = wrow_of(tid >> 1);
+        brow[0] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
+        bsrow = wr >= 0 ? WS + (int64_t)wr * wsb : nullptr;
+        brow[1] = brow[2] = brow[3] = nullptr;
+    }
+
+    uint4 ra[4], rb[4];
+    uint32_t rs = 0;
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
+        if (WT == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + (int64_t)(k0 + kc * 8) * 2) : make_uint4(0, 0, 0, 0);
+        } else {
+            const int half = tid & 1;
+            rb[0] = brow[0] ? *reinterpret_cast<const uint4*>(brow[0] + k0 / 2 + half * 16) : make_uint4(0, 0, 0, 0);
+            rs = bsrow ? bsrow[k0 / 32 + half] : 127u;
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (tid >> 3) + 32 * i;
+            *reinterpret_cast<uint4*>(&sA[buf][r * LDP + kc * 8]) = ra[i];
+        }
+        if (WT == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = (tid >> 3) + 32 * i;
+                *reinterpret_cast<uint4*>(&sB[buf][n * LDP + kc * 8]) = rb[i];
+            }
+        } else {
+            const int n = tid >> 1, half = tid & 1;
+            uint16_t* dst = &sB[buf][n * LDP + half * 32];
+            *reinterpret_cast<uint4*>(dst + 0) = fp4x8_to_bf16(rb[0].x, rs);
+            *reinterpret_cast<uint4*>(dst + 8) = fp4x8_to_bf16(rb[0].y, rs);
+            *reinterpret_cast<uint4*>(dst + 16) = fp4x8_to_bf16(rb[0].z, rs);
+            *reinterpret_cast<uint4*>(dst + 24) = fp4x8_to_bf16(rb[0].w, rs);
+        }
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nk = K / TBK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * TBK);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8_t af[4], bfr[4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+                af[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                    &sA[buf][(wm * 64 + ms * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+                bfr[ns] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                    &sB[buf][(wn * 64 + ns * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = wm * 64 + ms * 16 + (lane >> 4) * 4 + jj;
+            if (r >= mrows) continue;
+            const int row = m0 + r;
+            if (MODE == MODE_W13) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) +
+                              (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f);
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const int j = nt * 64 + wn * 32 + ns * 16 + (lane & 15);
+                    const float gt = acc[ms][ns][jj], up = acc[ms][ns + 2][jj];
+                    o[j] = f32_to_bf16(gt / (1.0f + expf(-gt)) * up);
+                }
+            } else if (MODE == MODE_W2) {
+                uint16_t* o = shared ? p.out_sh + (int64_t)row * p.d
+                                     : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d;
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns) {
+                    const int n = nt * TBN + wn * 64 + ns * 16 + (lane & 15);
+                    if (n < N) o[n] = f32_to_bf16(acc[ms][ns][jj]);
+                }
+            } else {
+                float* o = reinterpret_cast<float*>(p.out) + (int64_t)row * p.E;
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns) {
+                    const int n = nt * TBN + wn * 64 + ns * 16 + (lane & 15);
+                    if (n < N) o[n] = acc[ms][ns][jj] + (p.bias ? p.bias[n] : 0.0f);
+                }
+            }
+        }
+    }
+}
+
+static unsigned grid8(int64_t tiles) {
+    int64_t g = (tiles + 7) / 8 * 8;
+    return (unsigned)(g < 8 ? 8 : g);
+}
+
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
                                     int E, hipStream_t st) {
-    return launch_route_logits(1, x, wr, b, logits, T, d, E, st);
+    GemmArgs p{};
+    p.A = (const uint16_t*)x;
+    p.w = (const uint8_t*)wr;
+    p.bias = b;
+    p.out = logits;
+    p.T = T; p.d = d; p.E = E; p.k = 1;
+    const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + TBN - 1) / TBN);
+    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1>), dim3(grid8(tiles)), dim3(256), 0, st, p);
+    return hipGetLastError();
 }
 
-hipError_t launch_ggemm_w13(int, const uint16_t*, const int32_t*, const int32_t*, const int32_t*, const int32_t*,
-                            const void*, const uint8_t*, const void*, const uint8_t*, uint16_t*, int, int, int, int,
-                            int, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t routed_mt = (P + TBM - 1) / TBM + (P < E ? P : E);
+    const int64_t shared_mt = n_shared ? (T + TBM - 1) / TBM : 0;
+    return routed_mt * rows_nt + shared_mt * shared_nt;
 }
 
-hipError_t launch_ggemm_w2(int, const uint16_t*, const int32_t*, const int32_t*, const int32_t*, const void*,
-                           const uint8_t*, const void*, const uint8_t*, uint16_t*, uint16_t*, int, int, int, int,
-                           int, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, const int32_t* offsets,
+                            const int32_t*, const int32_t*, const void* w13, const uint8_t* w13s, const void* s13,
+                            const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k, int E, int n_shared,
+                            hipStream_t st) {
+    GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
+               T, d, f, fs, k, E, n_shared};
+    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / 64, n_shared ? fs / 64 : 0));
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W13, 2>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t*, const int32_t*,
+                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y,
+                           uint16_t* y_shared, int T, int d, int f, int fs, int k, int E, int n_shared,
+                           hipStream_t st) {
+    GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
+               T, d, f, fs, k, E, n_shared};
+    const int nt = (d + TBN - 1) / TBN;
+    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W2, 2>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
 }
 
 }  // namespace moe
