@@ -152,20 +152,21 @@ def run_layer_workload(hip, name, steps, warmup):
     shape = moe.make_shape(s)
     ws = moe.workspace(shape)
     out = torch.empty((T, s.d), dtype=torch.bfloat16, device="cuda")
-    idx_log = torch.empty((max(steps, 1), T, s.k), dtype=torch.int32, device="cuda")
+    row = (T * s.k + 3) // 4 * 4  # keep every step's slice 16-byte aligned
+    idx_log = torch.empty((max(steps, 1), row), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
     def step(i, log=None):
         wr, b, W, _, _ = layers[i % copies]
         moe.layer_forward_raw(shape, x_pool[i % n_batches], wr, b, W, out,
-                              idx_log[log] if log is not None else None, ws)
+                              idx_log[log, :T * s.k] if log is not None else None, ws)
 
     total, _ = _timed(hip, stream, step, steps, warmup)
     _, k_up = _timed(hip, stream, lambda i: step(i, log=(i - warmup) if i >= warmup else None), steps, warmup,
                      profile=moe.KERNEL_FFN_UP)
     torch.cuda.synchronize()
     # Routing actually taken (timed pass 2 logged it) -> unique experts per step.
-    idx = idx_log.cpu().numpy()
+    idx = idx_log[:, :T * s.k].cpu().numpy()
     uniq = np.array([len(np.unique(idx[i])) for i in range(steps)], np.float64)
     counts = np.bincount(idx.reshape(-1), minlength=s.E)
     up_b, down_b = expert_bytes(s)
@@ -305,7 +306,11 @@ def main():
     if not args.no_sweep:
         names = [n for n in (args.sweep_list.split(",") if args.sweep_list else WORKLOADS) if n and n != args.workload]
         for n in names:
-            sweep[n] = run(n, args.steps, args.warmup)
+            try:
+                sweep[n] = run(n, args.steps, args.warmup)
+            except Exception as exc:  # keep the line printable; the failure is reported in it
+                sweep[n] = {"error": repr(exc)}
+                print(f"[bench] {n} failed: {exc!r}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline()
     if head["bound"] == "hbm":
         roof = dict(bound="hbm", achieved=head["ffn_up_GBps"], peak=HBM_PEAK_GBS, unit="GB/s",

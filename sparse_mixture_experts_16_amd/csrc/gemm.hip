@@ -9,7 +9,7 @@
 //   MODE_W2      y[pos, n] = a[pos] . W2_e[n]                          A rows contiguous
 //   MODE_ROUTER  l[t, e]   = x_t . W_r[e] + b[e]                       one group, fp32 out
 //
-// Tiles are 128 (token rows) x 128 (weight rows) x 64 (K); four wavefronts each own a 64x64
+// Tiles are 128 (token rows) x 128 (weight rows) x 64 or 32 (K); four wavefronts each own a 64x64
 // quarter computed with v_mfma_f32_16x16x32_bf16 (operand lane layout: lane l holds row l%16,
 // k = 8*(l/16)..+7 of A and column l%16 of B; the accumulator holds column l%16, rows
 // 4*(l/16)..+3).  Tiles stream through double-buffered LDS rows padded to 72 bf16 so that the
@@ -32,11 +32,11 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int TBM = 128, TBN = 128, TBK = 64, LDP = TBK + 8;
+constexpr int TBM = 128, TBN = 128;
 enum { MODE_W13 = 0, MODE_W2 = 1, MODE_ROUTER = 2 };
 
 struct GemmArgs {
-    const uint16_t* A;        // W13/ROUTER: x [T, d]; W2: a (routed [P, f], shared at +P*f as [T, fs])
+    const uint16_t* A;        // W13/ROUTER: x [T, d]; W2: a hi plane (routed [P, f], shared at +P*f as [T, fs])
     const int32_t* perm;      // W13: sorted slot -> pair
     const int32_t* offsets;   // [E+1] (W13/W2)
     const uint8_t* w;         // routed weights (ROUTER: W_r [E, d] bf16)
@@ -44,8 +44,9 @@ struct GemmArgs {
     const uint8_t* sw;        // shared expert weights
     const uint8_t* swsc;
     const float* bias;        // ROUTER: b [E] or NULL
-    void* out;                // W13: a (bf16); W2: y (bf16) [P, d]; ROUTER: logits (f32) [T, E]
+    void* out;                // W13: a hi plane (bf16); W2: y (bf16) [P, d]; ROUTER: logits (f32) [T, E]
     uint16_t* out_sh;         // W2: y_shared [T, d]
+    int64_t lo_off;           // elements from the a hi plane to the a lo plane
     int T, d, f, fs, k, E, n_shared;
 };
 
@@ -72,9 +73,19 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     return r;
 }
 
-template <int MODE, int WT>
+// BK: K depth of one LDS stage (64, or 32 for the split down projection).
+// SPLIT: the A operand comes as two bf16 planes a = hi + lo (lo = a - hi rounded to bf16), and
+// every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
+// through the bf16 matrix cores.
+template <int MODE, int WT, int BK, bool SPLIT>
 __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][TBM * LDP];
+    constexpr int LDP = BK + 8;          // padded LDS row pitch (bf16 elements)
+    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
+    constexpr int RPP = 256 / CPR;       // tile rows covered by one pass of the workgroup
+    constexpr int NP = TBM / RPP;        // passes per 128-row tile
+    constexpr int NPL = SPLIT ? 2 : 1;   // A planes
+    constexpr int C4 = BK / 32;          // MXFP4: 16-byte code chunks per tile row
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][NPL][TBM * LDP];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][TBN * LDP];
     __shared__ int s_pref[MOE_MAX_E + 2];
 
@@ -152,13 +163,13 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
     const int64_t wrb = row_bytes(WT, K), wsb = K / 32;
 
     // ---- this thread's global source rows for the A and B tiles
-    const int kc = tid & 7;  // 16-byte chunk within a 64-wide K slice (bf16)
-    const uint16_t* arow[4];
-    const uint8_t* brow[4];
+    const int kc = tid % CPR;  // 16-byte chunk within a BK-wide K slice (bf16)
+    const uint16_t* arow[NP];
+    const uint8_t* brow[NP];
     const uint8_t* bsrow = nullptr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 32 * i;
+    for (int i = 0; i < NP; ++i) {
+        const int r = tid / CPR + RPP * i;
         if (r < mrows) {
             int64_t src;
             if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
@@ -179,47 +190,55 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
     };
     if (WT == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int wr = wrow_of((tid >> 3) + 32 * i);
+        for (int i = 0; i < NP; ++i) {
+            const int wr = wrow_of(tid / CPR + RPP * i);
             brow[i] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
         }
     } else {
-        const int wr = wrow_of(tid >> 1);
-        brow[0] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
-        bsrow = wr >= 0 ? WS + (int64_t)wr * wsb : nullptr;
-        brow[1] = brow[2] = brow[3] = nullptr;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) brow[i] = nullptr;
+        if (tid < TBN * C4) {
+            const int wr = wrow_of(tid / C4);
+            brow[0] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
+            bsrow = wr >= 0 ? WS + (int64_t)wr * wsb : nullptr;
+        }
     }
 
-    uint4 ra[4], rb[4];
-    uint32_t rs = 0;
+    uint4 ra[NPL][NP], rb[NP];
+    uint32_t rs = 127u;
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < NP; ++i) {
+            ra[0][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
+            if (SPLIT)
+                ra[NPL - 1][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + p.lo_off + k0 + kc * 8)
+                                         : make_uint4(0, 0, 0, 0);
+        }
         if (WT == 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NP; ++i)
                 rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + (int64_t)(k0 + kc * 8) * 2) : make_uint4(0, 0, 0, 0);
         } else {
-            const int half = tid & 1;
+            const int half = tid % C4;
             rb[0] = brow[0] ? *reinterpret_cast<const uint4*>(brow[0] + k0 / 2 + half * 16) : make_uint4(0, 0, 0, 0);
             rs = bsrow ? bsrow[k0 / 32 + half] : 127u;
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = (tid >> 3) + 32 * i;
-            *reinterpret_cast<uint4*>(&sA[buf][r * LDP + kc * 8]) = ra[i];
+        for (int i = 0; i < NP; ++i) {
+            const int r = tid / CPR + RPP * i;
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl) *reinterpret_cast<uint4*>(&sA[buf][pl][r * LDP + kc * 8]) = ra[pl][i];
         }
         if (WT == 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = (tid >> 3) + 32 * i;
+            for (int i = 0; i < NP; ++i) {
+                const int n = tid / CPR + RPP * i;
                 *reinterpret_cast<uint4*>(&sB[buf][n * LDP + kc * 8]) = rb[i];
             }
-        } else {
-            const int n = tid >> 1, half = tid & 1;
+        } else if (tid < TBN * C4) {
+            const int n = tid / C4, half = tid % C4;
             uint16_t* dst = &sB[buf][n * LDP + half * 32];
             *reinterpret_cast<uint4*>(dst + 0) = fp4x8_to_bf16(rb[0].x, rs);
             *reinterpret_cast<uint4*>(dst + 8) = fp4x8_to_bf16(rb[0].y, rs);
@@ -234,29 +253,33 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = K / TBK;
+    const int nk = K / BK;
     gload(0);
     sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * TBK);
+        if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8_t af[4], bfr[4];
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-                af[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    &sA[buf][(wm * 64 + ms * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            bf16x8_t bfr[4];
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
                 bfr[ns] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
                     &sB[buf][(wn * 64 + ns * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+            for (int pl = 0; pl < NPL; ++pl) {
+                bf16x8_t af[4];
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+                for (int ms = 0; ms < 4; ++ms)
+                    af[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                        &sA[buf][pl][(wm * 64 + ms * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                    for (int ns = 0; ns < 4; ++ns)
+                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+            }
         }
         if (kt + 1 < nk) sstore(buf ^ 1);
         __syncthreads();
@@ -277,7 +300,10 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
                 for (int ns = 0; ns < 2; ++ns) {
                     const int j = nt * 64 + wn * 32 + ns * 16 + (lane & 15);
                     const float gt = acc[ms][ns][jj], up = acc[ms][ns + 2][jj];
-                    o[j] = f32_to_bf16(gt / (1.0f + expf(-gt)) * up);
+                    const float av = gt / (1.0f + expf(-gt)) * up;
+                    const uint16_t hi = f32_to_bf16(av);
+                    o[j] = hi;
+                    o[p.lo_off + j] = f32_to_bf16(av - bf16_to_f32(hi));
                 }
             } else if (MODE == MODE_W2) {
                 uint16_t* o = shared ? p.out_sh + (int64_t)row * p.d
@@ -313,8 +339,13 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     p.out = logits;
     p.T = T; p.d = d; p.E = E; p.k = 1;
     const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + TBN - 1) / TBN);
-    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1>), dim3(grid8(tiles)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 64, false>), dim3(grid8(tiles)), dim3(256), 0, st, p);
     return hipGetLastError();
+}
+
+// The SwiGLU activation is stored as two bf16 planes (hi, then lo) of P*f + T*fs elements each.
+static int64_t a_lo_offset(int T, int k, int f, int fs, int n_shared) {
+    return (int64_t)T * k * f + (n_shared ? (int64_t)T * fs : 0);
 }
 
 static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
@@ -329,10 +360,10 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k, int E, int n_shared,
                             hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
-               T, d, f, fs, k, E, n_shared};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / 64, n_shared ? fs / 64 : 0));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W13, 2>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1, 64, false>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W13, 2, 64, false>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -341,11 +372,11 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            uint16_t* y_shared, int T, int d, int f, int fs, int k, int E, int n_shared,
                            hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
-               T, d, f, fs, k, E, n_shared};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
     const int nt = (d + TBN - 1) / TBN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W2, 2>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1, 32, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W2, 2, 32, true>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
