@@ -106,7 +106,9 @@ typedef struct {
     const uint8_t* s2_scale;
 } moe_weights;
 
-/* Bytes of device workspace the calls below need for this shape (0 on an invalid shape). */
+/* Bytes of device workspace the calls below need for this shape (0 on an invalid shape).
+   A workspace buffer must be zero-filled before its first use; every call leaves it ready
+   for the next one (the decode router keeps a completion counter in its first bytes). */
 size_t moe_workspace_size(const moe_shape* shape);
 
 /* Static description of a status code. */

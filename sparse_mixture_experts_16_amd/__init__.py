@@ -113,7 +113,7 @@ def workspace(shape: Shape, device="cuda"):
     dev = torch.device(device)
     cur = _ws_cache.get(dev)
     if cur is None or cur.numel() < n:
-        cur = torch.empty(n, dtype=torch.uint8, device=dev)
+        cur = torch.zeros(n, dtype=torch.uint8, device=dev)  # a fresh workspace must start zero-filled
         _ws_cache[dev] = cur
     return cur
 

@@ -23,7 +23,8 @@ int act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 // Workspace regions (byte offsets from ws).
 struct Layout {
-    size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, act_list, tile_off, meta, blk, a, y, ysh, xn, total;
+    size_t ticket, logits, topk_idx, topk_w, counts, offsets, perm, inv, act_list, tile_off, meta, blk, slots, pos_tok,
+        pos_gate, a, y, ysh, xn, total;
 };
 
 Layout layout(const moe_shape* s) {
@@ -33,7 +34,9 @@ Layout layout(const moe_shape* s) {
     const size_t P = T * k;
     const size_t ab = (size_t)act_bytes(s->act_dtype);
     const size_t nblk = P > PERMUTE_SMALL_MAX ? (P + PERMUTE_CHUNK - 1) / PERMUTE_CHUNK : 0;
+    const size_t fmax = fs > f ? fs : f;
     size_t o = 0;
+    L.ticket = o; o = up(o + 4);   // zero while no call runs (see moe_workspace_size)
     L.logits = o; o = up(o + T * E * 4);
     L.topk_idx = o; o = up(o + P * 4);
     L.topk_w = o; o = up(o + P * 4);
@@ -45,7 +48,12 @@ Layout layout(const moe_shape* s) {
     L.tile_off = o; o = up(o + (E + 2) * 4);
     L.meta = o; o = up(o + 16 * 4);
     L.blk = o; o = up(o + nblk * E * 4);
-    L.a = o; o = up(o + (P * f + T * fs) * 4);   // fp32 at decode, bf16 at prefill (fits either)
+    L.slots = o; o = up(o + (E + 1) * 16);
+    L.pos_tok = o; o = up(o + (P + T) * 4);
+    L.pos_gate = o; o = up(o + (P + T) * 4);
+    // fp32 rows of width fmax at decode, two bf16 planes at prefill
+    const size_t a_dec = (P + T) * fmax * 4, a_pre = (P * f + T * fs) * 4;
+    L.a = o; o = up(o + (a_dec > a_pre ? a_dec : a_pre));
     L.y = o; o = up(o + P * d * ab);
     L.ysh = o; o = up(o + T * d * ab);
     L.xn = o; o = up(o + T * d * ab);
@@ -162,6 +170,22 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
     return MOE_OK;
 }
 
+// Decode FFN (gate/up, then down fused with the combine) from the slot table dec_route wrote.
+int run_dec_ffn(const moe_shape* s, const void* x, const moe_weights* w, void* out, int out_dtype, bool accumulate,
+                void* ws, const Layout& L, hipStream_t st) {
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
+    hipError_t e = launch_dec_ffn(s->weight_dtype, out_dtype == MOE_BF16, x, at<int32_t>(ws, L.meta),
+                                  at<int4>(ws, L.slots), at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate),
+                                  w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2, w->s2_scale,
+                                  at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0,
+                                  s->top_k, s->n_experts, s->n_shared, accumulate, st,
+                                  g_prof_kernel == MOE_KERNEL_FFN_UP ? g_prof_stop : nullptr,
+                                  g_prof_kernel == MOE_KERNEL_FFN_DOWN ? g_prof_start : nullptr);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
+    return MOE_OK;
+}
+
 // The whole layer on x; out has dtype out_dtype (act dtype for the layer API, f32 for the stack).
 int run_layer(const moe_shape* s, const void* x, const void* w_router, const float* b, const moe_weights* w,
               void* out, int out_dtype, bool accumulate, int32_t* idx_out, void* ws, const Layout& L,
@@ -180,6 +204,13 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     int32_t* meta = at<int32_t>(ws, L.meta);
     int32_t* blk = at<int32_t>(ws, L.blk);
     const bool gemm = use_gemm(s);
+    if (!gemm && T <= DECODE_MAX_T) {
+        MOE_TRY(launch_dec_route(s->act_dtype, x, w_router, b, logits, idx, g, idx_out, counts, offsets, perm, inv, meta,
+                                 at<int4>(ws, L.slots), at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate), nullptr,
+                                 at<unsigned>(ws, L.ticket), T, d, E, k, s->n_shared,
+                                 (s->flags & MOE_F_NO_RENORM) != 0, false, st));
+        return run_dec_ffn(s, x, w, out, out_dtype, accumulate, ws, L, st);
+    }
     if (gemm && T > DECODE_MAX_T)
         MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, st));
     else
@@ -337,6 +368,21 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
     if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     void* xn = at<void>(ws, L.xn);
+    if (!use_gemm(s) && s->T <= DECODE_MAX_T) {
+        // decode: the router kernel normalises h itself and leaves x for the FFN kernels
+        for (int l = 0; l < n_layers; ++l) {
+            MOE_TRY(launch_dec_route(s->act_dtype, h, w_router[l], b_router ? b_router[l] : nullptr, at<float>(ws, L.logits),
+                                     at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_w), nullptr,
+                                     at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                                     at<int32_t>(ws, L.inv), at<int32_t>(ws, L.meta), at<int4>(ws, L.slots),
+                                     at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate), xn,
+                                     at<unsigned>(ws, L.ticket), s->T, s->d_model, s->n_experts, s->top_k,
+                                     s->n_shared, (s->flags & MOE_F_NO_RENORM) != 0, true, st));
+            rc = run_dec_ffn(s, xn, &w[l], h, MOE_F32, true, ws, L, st);
+            if (rc != MOE_OK) return rc;
+        }
+        return MOE_OK;
+    }
     for (int l = 0; l < n_layers; ++l) {
         MOE_TRY(launch_rmsnorm(s->act_dtype == MOE_BF16 ? 1 : 0, h, xn, s->T, s->d_model, 1e-6f, st));
         rc = run_layer(s, xn, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr, ws,

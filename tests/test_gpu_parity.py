@@ -225,6 +225,46 @@ def test_layer_forward_skewed_routing_and_empty_batch():
     moe.layer_forward_raw(shape, dev(x), dev(wr), dev(b), moe.make_weights(wd, shd), out)
 
 
+DECODE_ODD = [
+    mi.LayerSpec("dec_fs_gt_f", 7, 256, 64, 16, 3, 1, 192, "bf16", "bf16", 1.0, 0.05, 0.05, seed=31),
+    mi.LayerSpec("dec_fs_lt_f", 5, 256, 192, 16, 3, 1, 64, "bf16", "bf16", 1.0, 0.05, 0.05, seed=32),
+    mi.LayerSpec("dec_mxfp4_shared", 3, 128, 96, 12, 4, 1, 64, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=33),
+    mi.LayerSpec("dec_long_k", 2, 4096, 64, 8, 2, 1, 32, "bf16", "bf16", 1.0, 0.02, 0.02, seed=34),
+    mi.LayerSpec("dec_long_f", 3, 64, 2048, 8, 2, 0, 0, "bf16", "bf16", 1.0, 0.02, 0.02, seed=35),
+    mi.LayerSpec("dec_f32_E1", 4, 64, 32, 1, 1, 0, 0, "f32", "f32", 0.5, 0.1, 0.1, seed=36),
+]
+
+
+@pytest.mark.parametrize("s", DECODE_ODD, ids=lambda s: s.name)
+def test_layer_forward_decode_odd_shapes(s):
+    """Shared d_ff larger / smaller than the routed one, rows longer than one K step, E = 1."""
+    x, wr, b, _ = margin_x(s)
+    w, sh, wd, shd = _weights(s)
+    ref = oracle.layer_forward(s, x, wr, b, w, sh)
+    res = moe.layer_forward(s, dev(x), dev(wr), dev(b), wd, shd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
+    assert_close(host(res["out"]), ref["out"], what=s.name)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_stack_forward_small(T):
+    """moe_stack_forward over 3 layers against the oracle's stack layer applied 3 times."""
+    s = mi.LayerSpec("stk", T, 256, 128, 16, 3, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=41, n_layers=3)
+    rng = np.random.default_rng(5)
+    h0 = rng.normal(size=(T, s.d)).astype(np.float32)
+    layers = [(mi.host_router(s, l), mi.host_experts(s, l)) for l in range(3)]
+    h_ref = h0.copy()
+    idx_ref = [oracle.stack_layer(s, h_ref, wr, b, w) for (wr, b), w in layers]
+    shape = moe.make_shape(s)
+    h = dev(h0)
+    wds = [{k: dev(v) for k, v in w.items()} for _, w in layers]
+    moe.stack_forward(shape, h, [dev(wr) for (wr, _), _ in layers], [dev(b) for (_, b), _ in layers],
+                      [moe.make_weights(wd) for wd in wds])
+    torch.cuda.synchronize()
+    assert_close(host(h), h_ref.astype(np.float64), what=f"stack T={T}")
+
+
 def test_no_renorm_gates():
     s = mi.spec("c1", T=16)
     x, wr, b, _ = margin_x(s)
