@@ -170,20 +170,29 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
     return MOE_OK;
 }
 
-// Decode FFN (gate/up, then down fused with the combine) from the slot table dec_route wrote.
-int run_dec_ffn(const moe_shape* s, const void* x, const moe_weights* w, void* out, int out_dtype, bool accumulate,
-                void* ws, const Layout& L, hipStream_t st) {
+// Decode path: router logits, then gate/up (routing redone per workgroup) and down + combine.
+// prenorm: x is the fp32 residual stream, normalised by the logits kernel into ws.xn.
+int run_decode(const moe_shape* s, const void* x, const void* w_router, const float* b, const moe_weights* w,
+               void* out, int out_dtype, bool accumulate, int32_t* idx_out, bool prenorm, void* ws, const Layout& L,
+               hipStream_t st) {
+    void* xn = at<void>(ws, L.xn);
+    MOE_TRY(launch_dec_logits(s->act_dtype, x, w_router, b, at<float>(ws, L.logits), xn, s->T, s->d_model,
+                              s->n_experts, prenorm, st));
     MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
-    hipError_t e = launch_dec_ffn(s->weight_dtype, out_dtype == MOE_BF16, x, at<int32_t>(ws, L.meta),
-                                  at<int4>(ws, L.slots), at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate),
-                                  w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2, w->s2_scale,
-                                  at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0,
-                                  s->top_k, s->n_experts, s->n_shared, accumulate, st,
-                                  g_prof_kernel == MOE_KERNEL_FFN_UP ? g_prof_stop : nullptr,
-                                  g_prof_kernel == MOE_KERNEL_FFN_DOWN ? g_prof_start : nullptr);
+    hipError_t e = launch_dec_ffn(
+        s->weight_dtype, out_dtype == MOE_BF16, prenorm ? xn : x, at<float>(ws, L.logits), at<int32_t>(ws, L.topk_idx),
+        at<float>(ws, L.topk_w), idx_out, at<int32_t>(ws, L.meta), at<int4>(ws, L.slots), at<float>(ws, L.pos_gate),
+        (s->flags & MOE_F_NO_RENORM) != 0, w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2,
+        w->s2_scale, at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
+        s->n_experts, s->n_shared, accumulate, st, g_prof_kernel == MOE_KERNEL_FFN_UP ? g_prof_stop : nullptr,
+        g_prof_kernel == MOE_KERNEL_FFN_DOWN ? g_prof_start : nullptr);
     if (e != hipSuccess) return MOE_ERR_HIP;
     MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
     return MOE_OK;
+}
+
+bool use_decode(const moe_shape* s) {
+    return !use_gemm(s) && s->T <= DECODE_MAX_T && dec_supported(s->T, s->n_experts, s->top_k);
 }
 
 // The whole layer on x; out has dtype out_dtype (act dtype for the layer API, f32 for the stack).
@@ -204,13 +213,7 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     int32_t* meta = at<int32_t>(ws, L.meta);
     int32_t* blk = at<int32_t>(ws, L.blk);
     const bool gemm = use_gemm(s);
-    if (!gemm && T <= DECODE_MAX_T) {
-        MOE_TRY(launch_dec_route(s->act_dtype, x, w_router, b, logits, idx, g, idx_out, counts, offsets, perm, inv, meta,
-                                 at<int4>(ws, L.slots), at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate), nullptr,
-                                 at<unsigned>(ws, L.ticket), T, d, E, k, s->n_shared,
-                                 (s->flags & MOE_F_NO_RENORM) != 0, false, st));
-        return run_dec_ffn(s, x, w, out, out_dtype, accumulate, ws, L, st);
-    }
+    if (use_decode(s)) return run_decode(s, x, w_router, b, w, out, out_dtype, accumulate, idx_out, false, ws, L, st);
     if (gemm && T > DECODE_MAX_T)
         MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, st));
     else
@@ -368,17 +371,11 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
     if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     void* xn = at<void>(ws, L.xn);
-    if (!use_gemm(s) && s->T <= DECODE_MAX_T) {
-        // decode: the router kernel normalises h itself and leaves x for the FFN kernels
+    if (use_decode(s)) {
+        // decode: the logits kernel normalises h itself and leaves x for the FFN kernels
         for (int l = 0; l < n_layers; ++l) {
-            MOE_TRY(launch_dec_route(s->act_dtype, h, w_router[l], b_router ? b_router[l] : nullptr, at<float>(ws, L.logits),
-                                     at<int32_t>(ws, L.topk_idx), at<float>(ws, L.topk_w), nullptr,
-                                     at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
-                                     at<int32_t>(ws, L.inv), at<int32_t>(ws, L.meta), at<int4>(ws, L.slots),
-                                     at<int32_t>(ws, L.pos_tok), at<float>(ws, L.pos_gate), xn,
-                                     at<unsigned>(ws, L.ticket), s->T, s->d_model, s->n_experts, s->top_k,
-                                     s->n_shared, (s->flags & MOE_F_NO_RENORM) != 0, true, st));
-            rc = run_dec_ffn(s, xn, &w[l], h, MOE_F32, true, ws, L, st);
+            rc = run_decode(s, h, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr,
+                            true, ws, L, st);
             if (rc != MOE_OK) return rc;
         }
         return MOE_OK;

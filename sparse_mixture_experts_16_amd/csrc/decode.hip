@@ -1,29 +1,33 @@
-// Decode path of the whole layer (T <= 32 tokens) in three launches.
+// Decode path of the whole layer (T <= 32 tokens, T*E <= 8192) in three launches.
 //
 // At decode a token touches only its k experts (FreeToken/dothoosh, "Architecture and the
 // sparsity puzzle": 13B of 284B parameters per token), so the layer is a stream of a few
-// experts' weight rows from HBM.  Everything that is not that stream is latency, so the three
-// kernels are arranged to start the weight stream as early as possible and keep many 16-byte
-// loads in flight per lane:
+// experts' weight rows from HBM and everything else is latency.  The launches are arranged so
+// that no workgroup ever waits for another one inside a kernel:
 //
-//   dec_route   one wavefront per router row computes the logits of every token; the last
-//               workgroup to finish (ticket counter) selects the top-k, forms the gates, sorts
-//               the pairs by expert and writes a compact slot table:
-//                 slot s = (expert, first sorted position, pairs) for the experts that got
-//                 tokens, ascending, then the shared expert; pos_tok / pos_gate per position.
-//               With RMS-norm input (the residual stack) every workgroup normalises h itself.
-//   dec_w13     gate/up rows of each slot's expert -> a = silu(g) * u (fp32), one wavefront
-//               per (slot, R columns).
-//   dec_w2c     down projection fused with the combine: a wavefront owns R output rows of
-//               every token, issues the loads of a batch of SB experts' rows at once, and adds
-//               the experts in ascending order (shared last) -- deterministic, no atomics.
+//   dec_logits  one wavefront per router row computes the logits of every token (with the
+//               residual stack, every workgroup also RMS-normalises its tokens itself and
+//               workgroup 0 stores the normalised input for the FFN kernels).
+//   dec_w13     every workgroup first redoes the routing from the logits in LDS -- top-k and
+//               gates per token, grouping by expert into a slot table (expert, first sorted
+//               position, pairs, token mask) -- then computes its share of
+//               a[pos, j] = silu(Wg_e[j] . x_t) * (Wu_e[j] . x_t) in fp32.  Workgroup 0 also
+//               publishes the routing (top-k, slot table, per-position gate) for the down
+//               kernel and the caller.
+//   dec_w2c     down projection fused with the combine: a workgroup owns R output rows of
+//               every token; its 8 wavefronts split the slots, each adds g * (W2_e[i] . a) for
+//               its slots, and the 8 partial sums are added in wavefront order through LDS --
+//               a fixed order, so results are deterministic and need no atomics.
 #include "common.h"
 #include "kernels.h"
 #include "wchunk.h"
 
 namespace moe {
 
-__device__ __forceinline__ uint64_t dec_select_key(float v, int e) {
+constexpr int DEC_MAX_T = 32;
+constexpr int DEC_MAX_TE = 8192;  // logits held in LDS by every gate/up workgroup
+
+__device__ __forceinline__ uint64_t dec_key(float v, int e) {
     uint32_t ord;
     if (v != v) {
         ord = 0u;
@@ -34,9 +38,6 @@ __device__ __forceinline__ uint64_t dec_select_key(float v, int e) {
     return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// ------------------------------------------------------------------------------------------------
-// dec_route
-// ------------------------------------------------------------------------------------------------
 template <typename A> struct rvec;
 template <> struct rvec<float> {
     static constexpr int N = 4;
@@ -54,126 +55,123 @@ template <> struct rvec<uint16_t> {
     }
 };
 
-struct DecRouteArgs {
-    const void* x;         // [T, d] act dtype, or (prenorm) the fp32 residual stream h [T, d]
-    const void* wr;        // [E, d] act dtype
-    const float* b;        // [E] or NULL
-    float* logits;         // [T, E]
-    int32_t* topk_idx;     // [T, k]
-    float* topk_w;         // [T, k]
-    int32_t* idx_out;      // optional copy of topk_idx
-    int32_t* counts;       // [E]
-    int32_t* offsets;      // [E+1]
-    int32_t* perm;         // [P]
-    int32_t* inv;          // [P]
-    int32_t* meta;         // meta[0] = slots (incl. shared)
-    int4* slots;           // [E+1] (expert, pos0, npos, shared)
-    int32_t* pos_tok;      // [P + T]
-    float* pos_gate;       // [P + T]
-    void* xn;              // prenorm: normalised x written here (act dtype) by the last workgroup
-    unsigned* ticket;      // zero on entry; left zero on exit
-    int T, d, E, k, n_shared, no_renorm, prenorm;
+// ------------------------------------------------------------------------------------------------
+// dec_logits
+// ------------------------------------------------------------------------------------------------
+struct DecLogitsArgs {
+    const void* x;   // [T, d] act dtype, or (prenorm) the fp32 residual stream h [T, d]
+    const void* wr;  // [E, d] act dtype
+    const float* b;  // [E] or NULL
+    float* logits;   // [T, E]
+    void* xn;        // prenorm: normalised input (act dtype), written by workgroup 0
+    int T, d, E, prenorm;
 };
 
-// Row of token t of the layer input, as fp32 values, for chunk i (V elements).
 template <typename A>
-__device__ __forceinline__ void load_x(const DecRouteArgs& p, int t, int i, float inv, float* v) {
+__global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
     constexpr int V = rvec<A>::N;
-    if (p.prenorm) {
-        const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * p.d + i;
-#pragma unroll
-        for (int q = 0; q < V; ++q) v[q] = bf16_to_f32(f32_to_bf16(h[q] * inv));  // the bf16 value K2 will see
-        if (sizeof(A) == 4) {
-#pragma unroll
-            for (int q = 0; q < V; ++q) v[q] = h[q] * inv;
-        }
-    } else {
-        rvec<A>::load(reinterpret_cast<const A*>(p.x) + (int64_t)t * p.d + i, v);
-    }
-}
-
-template <typename A>
-__global__ void __launch_bounds__(512) dec_route(DecRouteArgs p) {
-    constexpr int V = rvec<A>::N;
-    constexpr int NW = 8;  // wavefronts per workgroup
-    __shared__ float s_inv[32];
-    __shared__ int s_cnt[MOE_MAX_E];
-    __shared__ int s_cur[MOE_MAX_E];
-    __shared__ int s_last;
+    __shared__ float s_inv[DEC_MAX_T];
     const int lane = lane_id(), wv = wave_id();
-    const int T = p.T, E = p.E, k = p.k, d = p.d;
-
-    // RMS normalisation factors of the residual stream (stack input), one per token.
+    const int T = p.T, d = p.d;
     if (p.prenorm) {
-        for (int t = wv; t < T; t += NW) {
+        for (int t = wv; t < T; t += 4) {
             const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * d;
             float ss = 0.0f;
-            for (int i = lane; i < d; i += MOE_WAVE) ss = fmaf(h[i], h[i], ss);
+            for (int i = lane * 4; i < d; i += MOE_WAVE * 4) {
+                const float4 q = *reinterpret_cast<const float4*>(h + i);
+                ss = fmaf(q.x, q.x, ss); ss = fmaf(q.y, q.y, ss); ss = fmaf(q.z, q.z, ss); ss = fmaf(q.w, q.w, ss);
+            }
             ss = wave_sum(ss);
             if (lane == 0) s_inv[t] = 1.0f / sqrtf(ss / (float)d + 1e-6f);
         }
         __syncthreads();
-    }
-
-    // Logits: wavefront per router row.
-    const int e = blockIdx.x * NW + wv;
-    if (e < E) {
-        const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)e * d;
-        const float bias = p.b ? p.b[e] : 0.0f;
-        for (int t0 = 0; t0 < T; t0 += 8) {
-            float acc[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-            for (int i = lane * V; i < d; i += MOE_WAVE * V) {
-                float wvv[V];
-                rvec<A>::load(w + i, wvv);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (t0 + q < T) {
-                        float xv[V];
-                        load_x<A>(p, t0 + q, i, p.prenorm ? s_inv[t0 + q] : 1.0f, xv);
-#pragma unroll
-                        for (int v = 0; v < V; ++v) acc[q] = fmaf(wvv[v], xv[v], acc[q]);
-                    }
+        if (blockIdx.x == 0)
+            for (int t = 0; t < T; ++t)
+                for (int i = threadIdx.x; i < d; i += blockDim.x) {
+                    const float v = reinterpret_cast<const float*>(p.x)[(int64_t)t * d + i] * s_inv[t];
+                    io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)t * d + i, v);
                 }
-            }
+    }
+    const int e = blockIdx.x * 4 + wv;
+    if (e >= p.E) return;
+    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)e * d;
+    const float bias = p.b ? p.b[e] : 0.0f;
+    for (int t0 = 0; t0 < T; t0 += 8) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int i = lane * V; i < d; i += MOE_WAVE * V) {
+            float wvv[V];
+            rvec<A>::load(w + i, wvv);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float s = wave_sum(acc[q]);
-                if (lane == 0 && t0 + q < T) p.logits[(int64_t)(t0 + q) * E + e] = s + bias;
+                if (t0 + q >= T) break;
+                float xv[V];
+                if (p.prenorm) {
+                    const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d + i;
+                    const float inv = s_inv[t0 + q];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        const float hv = h[v] * inv;
+                        xv[v] = sizeof(A) == 2 ? bf16_to_f32(f32_to_bf16(hv)) : hv;  // the value the FFN reads
+                    }
+                } else {
+                    rvec<A>::load(reinterpret_cast<const A*>(p.x) + (int64_t)(t0 + q) * d + i, xv);
+                }
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[q] = fmaf(wvv[v], xv[v], acc[q]);
             }
         }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float s = wave_sum(acc[q]);
+            if (lane == 0 && t0 + q < T) p.logits[(int64_t)(t0 + q) * p.E + e] = s + bias;
+        }
     }
+}
 
-    // Ticket: the last workgroup continues with selection and grouping.
-    __threadfence();
+// ------------------------------------------------------------------------------------------------
+// Routing from the logits, inside one workgroup of 256 threads, in LDS.
+// Slot s = (expert, first sorted position, pairs, token mask); slots ascend by expert, the
+// shared expert (if any) is the last slot, expert id E, positions P..P+T-1.
+// ------------------------------------------------------------------------------------------------
+struct DecRoute {
+    int n_slots;
+    int n_routed;
+    int4 slot[MOE_MAX_E + 1];
+    float gate[DEC_MAX_T * MOE_MAX_K];  // [t][j]
+    int sel[DEC_MAX_T * MOE_MAX_K];     // [t][j]
+};
+
+struct DecRouteIO {
+    const float* logits;
+    int32_t* topk_idx;   // workgroup 0 publishes the routing
+    float* topk_w;
+    int32_t* idx_out;
+    int32_t* meta;       // [0] = slots
+    int4* slots;
+    float* pos_gate;     // [P + T]
+    int T, E, k, n_shared, no_renorm;
+};
+
+__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask) {
+    const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    const int T = io.T, E = io.E, k = io.k;
+    const bool pub = blockIdx.x == 0;
+    for (int i = tid; i < T * E; i += blockDim.x) s_logits[i] = io.logits[i];
+    for (int e = tid; e < E; e += blockDim.x) {
+        s_cnt[e] = 0;
+        s_mask[e] = 0;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned t = atomicAdd(p.ticket, 1u);
-        s_last = (t == gridDim.x - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Normalised input for the FFN kernels (stack).
-    if (p.prenorm) {
-        for (int t = 0; t < T; ++t)
-            for (int i = threadIdx.x; i < d; i += blockDim.x) {
-                const float v = reinterpret_cast<const float*>(p.x)[(int64_t)t * d + i] * s_inv[t];
-                io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)t * d + i, v);
-            }
-    }
-
-    // Top-k + gates: wavefront per token.
-    for (int t = wv; t < T; t += NW) {
-        const volatile float* l = p.logits + (int64_t)t * E;
+    // top-k + gates, a wavefront per token
+    for (int t = wv; t < T; t += 4) {
+        const float* l = s_logits + t * E;
         uint64_t key[MOE_MAX_E / MOE_WAVE];
-        const int epl = (E + MOE_WAVE - 1) / MOE_WAVE;
 #pragma unroll
         for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j) {
-            const int ee = lane + MOE_WAVE * j;
-            key[j] = (j < epl && ee < E) ? dec_select_key(l[ee], ee) : 0ull;
+            const int e = lane + MOE_WAVE * j;
+            key[j] = e < E ? dec_key(l[e], e) : 0ull;
         }
         int my_sel = 0;
         for (int r = 0; r < k; ++r) {
@@ -181,112 +179,99 @@ __global__ void __launch_bounds__(512) dec_route(DecRouteArgs p) {
 #pragma unroll
             for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j) best = key[j] > best ? key[j] : best;
             best = wave_max_u64(best);
-            const int ee = (int)(0xFFFFFFFFu - (uint32_t)best);
+            const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
 #pragma unroll
             for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j)
-                if (lane + MOE_WAVE * j == ee) key[j] = 0ull;
-            if (lane == r) my_sel = ee;
+                if (lane + MOE_WAVE * j == e) key[j] = 0ull;
+            if (lane == r) my_sel = e;
         }
         const float m = l[__shfl(my_sel, 0, MOE_WAVE)];
         const float term = (lane < k) ? expf(l[my_sel] - m) : 0.0f;
         float den;
-        if (p.no_renorm) {
+        if (io.no_renorm) {
             float part = 0.0f;
-            for (int ee = lane; ee < E; ee += MOE_WAVE) part += expf(l[ee] - m);
+            for (int e = lane; e < E; e += MOE_WAVE) part += expf(l[e] - m);
             den = wave_sum(part);
         } else {
             den = wave_sum(term);
         }
         if (lane < k) {
-            p.topk_idx[(int64_t)t * k + lane] = my_sel;
-            p.topk_w[(int64_t)t * k + lane] = term / den;
-            if (p.idx_out) p.idx_out[(int64_t)t * k + lane] = my_sel;
+            const float g = term / den;
+            R.sel[t * k + lane] = my_sel;
+            R.gate[t * k + lane] = g;
+            atomicAdd(&s_cnt[my_sel], 1);
+            atomicOr(&s_mask[my_sel], 1 << t);
+            if (pub) {
+                io.topk_idx[t * k + lane] = my_sel;
+                io.topk_w[t * k + lane] = g;
+                if (io.idx_out) io.idx_out[t * k + lane] = my_sel;
+            }
         }
     }
     __syncthreads();
-
-    // Counting sort of the T*k pairs (wave 0 scatters stably), slot table.
+    // slot table: exclusive scan over experts (wavefront 0)
     const int P = T * k;
-    for (int ee = threadIdx.x; ee < E; ee += blockDim.x) s_cnt[ee] = 0;
-    __syncthreads();
-    for (int q = threadIdx.x; q < P; q += blockDim.x) atomicAdd(&s_cnt[p.topk_idx[q]], 1);
-    __syncthreads();
     if (wv == 0) {
-        // exclusive scan over experts, active list
         const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
         const int lo = min(lane * per, E), hi = min(lo + per, E);
         int sc = 0, sa = 0;
-        for (int ee = lo; ee < hi; ++ee) {
-            sc += s_cnt[ee];
-            sa += s_cnt[ee] > 0;
+        for (int e = lo; e < hi; ++e) {
+            sc += s_cnt[e];
+            sa += s_cnt[e] > 0;
         }
         int ic = sc, ia = sa;
 #pragma unroll
         for (int o = 1; o < MOE_WAVE; o <<= 1) {
             const int u = __shfl_up(ic, o, MOE_WAVE), w = __shfl_up(ia, o, MOE_WAVE);
-            if (lane >= o) { ic += u; ia += w; }
+            if (lane >= o) {
+                ic += u;
+                ia += w;
+            }
         }
         int pc = ic - sc, pa = ia - sa;
-        for (int ee = lo; ee < hi; ++ee) {
-            const int c = s_cnt[ee];
-            p.counts[ee] = c;
-            p.offsets[ee] = pc;
-            s_cur[ee] = pc;
-            if (c > 0) p.slots[pa++] = make_int4(ee, pc, c, 0);
+        for (int e = lo; e < hi; ++e) {
+            const int c = s_cnt[e];
+            if (c > 0) R.slot[pa++] = make_int4(e, pc, c, s_mask[e]);
             pc += c;
         }
         if (lane == MOE_WAVE - 1) {
-            p.offsets[E] = pc;
-            if (p.n_shared) p.slots[pa] = make_int4(E, P, T, 1);
-            p.meta[0] = pa + p.n_shared;
+            R.n_routed = pa;
+            R.n_slots = pa + io.n_shared;
+            if (io.n_shared) R.slot[pa] = make_int4(E, P, T, (int)(T >= 32 ? 0xFFFFFFFFu : ((1u << T) - 1u)));
         }
-        // stable scatter (ballot per expert-id bit)
-        int nbits = 0;
-        while ((1 << nbits) < E) ++nbits;
-        const uint64_t lt = lanemask_lt();
-        for (int c0 = 0; c0 < P; c0 += MOE_WAVE) {
-            const int q = c0 + lane;
-            const bool valid = q < P;
-            const int ee = valid ? p.topk_idx[q] : 0;
-            uint64_t msk = __ballot(valid);
-            for (int bb = 0; bb < nbits; ++bb) {
-                const bool bit = (ee >> bb) & 1;
-                const uint64_t bl = __ballot(valid && bit);
-                msk &= bit ? bl : ~bl;
-            }
-            if (valid) {
-                const int base = s_cur[ee];
-                const int pos = base + __popcll(msk & lt);
-                p.perm[pos] = q;
-                p.inv[q] = pos;
-                p.pos_tok[pos] = q / k;
-                p.pos_gate[pos] = p.topk_w[q];
-                if ((msk >> lane) == 1ull) s_cur[ee] = base + __popcll(msk);
-            }
-        }
-        if (p.n_shared)
-            for (int t = lane; t < T; t += MOE_WAVE) {
-                p.pos_tok[P + t] = t;
-                p.pos_gate[P + t] = 1.0f;
-            }
     }
-    if (threadIdx.x == 0) *p.ticket = 0u;  // ready for the next call
+    __syncthreads();
+    if (pub) {
+        // gate per sorted position for the down kernel: a slot's positions follow its tokens in order
+        for (int s = wv; s < R.n_slots; s += 4) {
+            const int4 S = R.slot[s];
+            if (lane == 0) io.slots[s] = S;
+            const uint32_t m = (uint32_t)S.w;
+            if (lane < T && ((m >> lane) & 1u)) {
+                const uint32_t below = lane == 0 ? 0u : (m & (0xFFFFFFFFu >> (32 - lane)));
+                const int pos = S.y + __popc(below);
+                float g = 1.0f;
+                if (S.x < E)
+                    for (int j = 0; j < k; ++j)
+                        if (R.sel[lane * k + j] == S.x) g = R.gate[lane * k + j];
+                io.pos_gate[pos] = g;
+            }
+        }
+        if (tid == 0) io.meta[0] = R.n_slots;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
-// dec_w13: a[pos, j] = silu(Wg[j] . x) * (Wu[j] . x) for every position of every slot
+// dec_w13
 // ------------------------------------------------------------------------------------------------
 struct DecFfnArgs {
     const void* x;          // [T, d] act dtype
-    const int32_t* meta;
-    const int4* slots;
-    const int32_t* pos_tok;
-    const float* pos_gate;
+    DecRouteIO rt;
     const uint8_t* w13; const uint8_t* w13s;   // routed gate/up
     const uint8_t* s13; const uint8_t* s13s;   // shared gate/up
     const uint8_t* w2; const uint8_t* w2s;     // routed down
     const uint8_t* s2; const uint8_t* s2s;     // shared down
-    float* a;               // [P + T, fmax]
+    float* a;               // [P + T, fmax] fp32
     void* out;              // [T, d] (f32 or bf16)
     int T, d, f, fs, fmax, k, accumulate;
 };
@@ -299,189 +284,190 @@ __global__ void __launch_bounds__(256) dec_w13(DecFfnArgs p) {
     using W = WChunk<WT>;
     using A = typename DecAct<WT>::T;
     constexpr int EC = W::EC;
+    __shared__ DecRoute rs;
+    __shared__ float s_logits[DEC_MAX_TE];
+    __shared__ int s_cnt[MOE_MAX_E];
+    __shared__ int s_mask[MOE_MAX_E];
+    dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask);
+
     const int lane = lane_id();
-    const int n_slots = p.meta[0];
-    const int T = p.T;
     const int ngr = (p.f + R - 1) / R, ngs = (p.fs + R - 1) / R;
-    const int wave_global = blockIdx.x * 4 + wave_id();
-    const int n_waves = gridDim.x * 4;
-    // items: routed slots first (ngr each), the shared slot last (ngs)
-    const int4 last = n_slots > 0 ? p.slots[n_slots - 1] : make_int4(0, 0, 0, 0);
-    const int n_routed = (n_slots > 0 && last.w) ? n_slots - 1 : n_slots;
-    const int r_items = n_routed * ngr;
-    const int n_items = r_items + (n_slots > n_routed ? ngs : 0);
+    const int r_items = rs.n_routed * ngr;
+    const int n_items = r_items + (rs.n_slots > rs.n_routed ? ngs : 0);
     const int NC = p.d / EC;
     const int64_t rb = row_bytes(WT, p.d), sb = p.d / 32;
-    for (int item = wave_global; item < n_items; item += n_waves) {
-        // routed slots first (ngr items each), then the shared slot (ngs items)
-        const int s = item < r_items ? item / ngr : n_routed;
+    const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
+    for (int item = blockIdx.x * 4 + wave_id(); item < n_items; item += gridDim.x * 4) {
+        const int s = item < r_items ? item / ngr : rs.n_routed;
         const int jg = item < r_items ? item % ngr : item - r_items;
-        const int4 S = p.slots[s];
-        const bool sh = S.w != 0;
+        const int4 S = rs.slot[s];
+        const bool sh = s >= rs.n_routed;
         const int fc = sh ? p.fs : p.f;
         const int j0 = jg * R;
         const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)S.x * 2 * p.f * rb;
         const uint8_t* sbp = (WT == 2) ? (sh ? p.s13s : p.w13s + (int64_t)S.x * 2 * p.f * sb) : nullptr;
-        // One K step covers the row when NC <= 64*U (the configured shapes); otherwise every
-        // pair re-streams the rows step by step (L1/L2 hits after the first pair).
-        const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
-        const int npass = nsteps == 1 ? 1 : S.z;
-        for (int ps = 0; ps < npass; ++ps) {
-            const int q_lo = nsteps == 1 ? 0 : ps, q_hi = nsteps == 1 ? S.z : ps + 1;
-            float ag[R][4], au[R][4];  // up to 4 pairs accumulated across K steps (slow path: 1)
+        // the slot's tokens in ascending order, 4 at a time; one K step covers a row in the
+        // configured shapes, otherwise rows are re-streamed per group of tokens (cache hits)
+        uint32_t mask = (uint32_t)S.w;
+        int pos = S.y;
+        while (mask) {
+            int tk[4];
+            int nq = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tk[q] = -1;
+                if (mask) {
+                    tk[q] = __ffs(mask) - 1;
+                    mask &= mask - 1u;
+                    ++nq;
+                }
+            }
+            float ag[R][4], au[R][4];
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) ag[r][q] = au[r][q] = 0.0f;
-            for (int qb = q_lo; qb < q_hi; qb += 4) {
-                for (int st = 0; st < nsteps; ++st) {
-                    const int c0 = st * MOE_WAVE * U;
-                    W wg[R][U], wu[R][U];
+            for (int st = 0; st < nsteps; ++st) {
+                const int c0 = st * MOE_WAVE * U;
+                W wg[R][U], wu[R][U];
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            const int c = c0 + lane + MOE_WAVE * u, j = j0 + r;
-                            if (c < NC && j < fc) {
-                                wg[r][u].load(wb + (int64_t)j * rb, sbp ? sbp + (int64_t)j * sb : nullptr, c);
-                                wu[r][u].load(wb + (int64_t)(fc + j) * rb, sbp ? sbp + (int64_t)(fc + j) * sb : nullptr, c);
-                            } else {
-                                wg[r][u].zero();
-                                wu[r][u].zero();
-                            }
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + lane + MOE_WAVE * u, j = j0 + r;
+                        if (c < NC && j < fc) {
+                            wg[r][u].load(wb + (int64_t)j * rb, sbp ? sbp + (int64_t)j * sb : nullptr, c);
+                            wu[r][u].load(wb + (int64_t)(fc + j) * rb, sbp ? sbp + (int64_t)(fc + j) * sb : nullptr, c);
+                        } else {
+                            wg[r][u].zero();
+                            wu[r][u].zero();
                         }
+                    }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (qb + q >= q_hi) break;
-                        const int t = p.pos_tok[S.y + qb + q];
-                        const A* xr = reinterpret_cast<const A*>(p.x) + (int64_t)t * p.d;
+                for (int q = 0; q < 4; ++q) {
+                    if (tk[q] < 0) break;
+                    const A* xr = reinterpret_cast<const A*>(p.x) + (int64_t)tk[q] * p.d;
 #pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            const int c = c0 + lane + MOE_WAVE * u;
-                            if (c < NC) {
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + lane + MOE_WAVE * u;
+                        if (c < NC) {
 #pragma unroll
-                                for (int r = 0; r < R; ++r) {
-                                    if constexpr (WT == 0) {
-                                        ag[r][q] = wg[r][u].dot_f32(xr + (int64_t)c * EC, ag[r][q]);
-                                        au[r][q] = wu[r][u].dot_f32(xr + (int64_t)c * EC, au[r][q]);
-                                    } else {
-                                        ag[r][q] = wg[r][u].dot_bf16(xr + (int64_t)c * EC, ag[r][q]);
-                                        au[r][q] = wu[r][u].dot_bf16(xr + (int64_t)c * EC, au[r][q]);
-                                    }
+                            for (int r = 0; r < R; ++r) {
+                                if constexpr (WT == 0) {
+                                    ag[r][q] = wg[r][u].dot_f32(xr + (int64_t)c * EC, ag[r][q]);
+                                    au[r][q] = wu[r][u].dot_f32(xr + (int64_t)c * EC, au[r][q]);
+                                } else {
+                                    ag[r][q] = wg[r][u].dot_bf16(xr + (int64_t)c * EC, ag[r][q]);
+                                    au[r][q] = wu[r][u].dot_bf16(xr + (int64_t)c * EC, au[r][q]);
                                 }
                             }
                         }
                     }
                 }
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (qb + q >= q_hi) break;
-                    const int pos = S.y + qb + q;
+            for (int q = 0; q < 4; ++q) {
+                if (q >= nq) break;
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const float g = wave_sum(ag[r][q]), u = wave_sum(au[r][q]);
-                        ag[r][q] = au[r][q] = 0.0f;
-                        const int j = j0 + r;
-                        if (lane == 0 && j < fc) p.a[(int64_t)pos * p.fmax + j] = g / (1.0f + expf(-g)) * u;
-                    }
+                for (int r = 0; r < R; ++r) {
+                    const float g = wave_sum(ag[r][q]), u = wave_sum(au[r][q]);
+                    const int j = j0 + r;
+                    if (lane == 0 && j < fc) p.a[(int64_t)(pos + q) * p.fmax + j] = g / (1.0f + expf(-g)) * u;
                 }
             }
+            pos += nq;
         }
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// dec_w2c: out[t, i] = sum_slots g * (W2_e[i] . a[pos]) (+ out), slots in ascending expert order
+// dec_w2c: out[t, i] (+)= sum over slots of g * (W2_e[i] . a[pos]); R rows per workgroup of 8 waves
 // ------------------------------------------------------------------------------------------------
-template <int WT, int R, int U, int SB, bool OUT_BF16>
-__global__ void __launch_bounds__(256) dec_w2c(DecFfnArgs p) {
+template <int WT, int R, int U, bool OUT_BF16>
+__global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
     using W = WChunk<WT>;
     constexpr int EC = W::EC;
-    const int lane = lane_id();
-    const int n_slots = p.meta[0];
-    const int n_items = (p.d + R - 1) / R;
-    const int wave_global = blockIdx.x * 4 + wave_id();
-    const int n_waves = gridDim.x * 4;
-    for (int item = wave_global; item < n_items; item += n_waves) {
-        const int i0 = item * R;
-        float o[R];
+    constexpr int NW = 8;
+    __shared__ float s_part[NW][R][DEC_MAX_T];
+    __shared__ int4 s_slot[MOE_MAX_E + 1];
+    __shared__ int s_n;
+    const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    if (tid == 0) s_n = p.rt.meta[0];
+    __syncthreads();
+    const int n_slots = s_n;
+    for (int s = tid; s < n_slots; s += blockDim.x) s_slot[s] = p.rt.slots[s];
+    __syncthreads();
+    const int T = p.T;
+    const int i0 = blockIdx.x * R;
+    float o[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) o[r] = 0.0f;
-        const int NCmax = (p.fs > p.f ? p.fs : p.f) / EC;
-        for (int s0 = 0; s0 < n_slots; s0 += SB) {
-            int4 S[SB];
+    for (int r = 0; r < R; ++r) o[r] = 0.0f;
+    for (int s = wv; s < n_slots; s += NW) {
+        const int4 S = s_slot[s];
+        const bool sh = S.x == p.rt.E;
+        const int fc = sh ? p.fs : p.f;
+        const int NC = fc / EC;
+        const int64_t rb = row_bytes(WT, fc), sbb = fc / 32;
+        const uint8_t* base = sh ? p.s2 : p.w2 + (int64_t)S.x * p.d * rb;
+        const uint8_t* sbase = (WT == 2) ? (sh ? p.s2s : p.w2s + (int64_t)S.x * p.d * sbb) : nullptr;
+        for (int c0 = 0; c0 < NC; c0 += MOE_WAVE * U) {
+            W w[R][U];
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb) S[sb] = (s0 + sb < n_slots) ? p.slots[s0 + sb] : make_int4(0, 0, 0, -1);
-            // K steps (one for the configured shapes); each adds g * partial dot to o
-            for (int c0 = 0; c0 < NCmax; c0 += MOE_WAVE * U) {
-                // every row of the batch: issue all loads first
-                W w[SB][R][U];
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int sb = 0; sb < SB; ++sb) {
-                    const bool live = S[sb].w >= 0;
-                    const bool sh = S[sb].w == 1;
-                    const int fc = sh ? p.fs : p.f;
-                    const int NC = fc / EC;
-                    const int64_t rb = row_bytes(WT, fc), sbb = fc / 32;
-                    const uint8_t* base = sh ? p.s2 : p.w2 + (int64_t)S[sb].x * p.d * rb;
-                    const uint8_t* sbase = (WT == 2) ? (sh ? p.s2s : p.w2s + (int64_t)S[sb].x * p.d * sbb) : nullptr;
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + r, c = c0 + lane + MOE_WAVE * u;
+                    if (i < p.d && c < NC) w[r][u].load(base + (int64_t)i * rb, sbase ? sbase + (int64_t)i * sbb : nullptr, c);
+                    else w[r][u].zero();
+                }
+            uint32_t mask = (uint32_t)S.w;
+            for (int q = 0; q < S.z; ++q) {
+                const int t = __ffs(mask) - 1;
+                mask &= mask - 1u;
+                const int pos = S.y + q;
+                const float g = p.rt.pos_gate[pos];
+                const float* ar = p.a + (int64_t)pos * p.fmax;
+                float acc[R];
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            const int i = i0 + r, c = c0 + lane + MOE_WAVE * u;
-                            if (live && i < p.d && c < NC)
-                                w[sb][r][u].load(base + (int64_t)i * rb, sbase ? sbase + (int64_t)i * sbb : nullptr, c);
-                            else
-                                w[sb][r][u].zero();
-                        }
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + lane + MOE_WAVE * u;
+                    if (c < NC) {
+#pragma unroll
+                        for (int r = 0; r < R; ++r) acc[r] = w[r][u].dot_f32(ar + (int64_t)c * EC, acc[r]);
+                    }
                 }
 #pragma unroll
-                for (int sb = 0; sb < SB; ++sb) {
-                    if (S[sb].w < 0) continue;
-                    const bool sh = S[sb].w == 1;
-                    const int fc = sh ? p.fs : p.f;
-                    const int NC = fc / EC;
-                    for (int q = 0; q < S[sb].z; ++q) {
-                        const int pos = S[sb].y + q;
-                        const int t = p.pos_tok[pos];
-                        const float g = p.pos_gate[pos];
-                        const float* ar = p.a + (int64_t)pos * p.fmax;
-                        float acc[R];
-#pragma unroll
-                        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-#pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            const int c = c0 + lane + MOE_WAVE * u;
-                            if (c < NC) {
-#pragma unroll
-                                for (int r = 0; r < R; ++r) acc[r] = w[sb][r][u].dot_f32(ar + (int64_t)c * EC, acc[r]);
-                            }
-                        }
-#pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const float y = wave_sum(acc[r]);
-                            if (lane == t) o[r] = fmaf(g, y, o[r]);
-                        }
-                    }
+                for (int r = 0; r < R; ++r) {
+                    const float y = wave_sum(acc[r]);
+                    if (lane == t) o[r] = fmaf(g, y, o[r]);
                 }
             }
         }
-        if (lane < p.T) {
+    }
+    if (lane < DEC_MAX_T) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int i = i0 + r;
-                if (i >= p.d) continue;
-                const int64_t off = (int64_t)lane * p.d + i;
-                if (OUT_BF16) {
-                    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-                    const float prev = p.accumulate ? bf16_to_f32(out[off]) : 0.0f;
-                    out[off] = f32_to_bf16(prev + o[r]);
-                } else {
-                    float* out = reinterpret_cast<float*>(p.out);
-                    const float prev = p.accumulate ? out[off] : 0.0f;
-                    out[off] = prev + o[r];
-                }
+        for (int r = 0; r < R; ++r) s_part[wv][r][lane] = o[r];
+    }
+    __syncthreads();
+    if (wv == 0 && lane < T) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = i0 + r;
+            if (i >= p.d) continue;
+            float v = 0.0f;
+#pragma unroll
+            for (int w8 = 0; w8 < NW; ++w8) v += s_part[w8][r][lane];
+            const int64_t off = (int64_t)lane * p.d + i;
+            if (OUT_BF16) {
+                uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+                const float prev = p.accumulate ? bf16_to_f32(out[off]) : 0.0f;
+                out[off] = f32_to_bf16(prev + v);
+            } else {
+                float* out = reinterpret_cast<float*>(p.out);
+                const float prev = p.accumulate ? out[off] : 0.0f;
+                out[off] = prev + v;
             }
         }
     }
@@ -490,37 +476,35 @@ __global__ void __launch_bounds__(256) dec_w2c(DecFfnArgs p) {
 // ------------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------------
-hipError_t launch_dec_route(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
-                            int32_t* topk_idx, float* topk_w, int32_t* idx_out, int32_t* counts, int32_t* offsets,
-                            int32_t* perm, int32_t* inv, int32_t* meta, int4* slots, int32_t* pos_tok,
-                            float* pos_gate, void* xn, unsigned* ticket, int T, int d, int E, int k, int n_shared,
-                            bool no_renorm, bool prenorm, hipStream_t st) {
-    DecRouteArgs p{x, wr, b, logits, topk_idx, topk_w, idx_out, counts, offsets, perm, inv, meta, slots, pos_tok,
-                   pos_gate, xn, ticket, T, d, E, k, n_shared, no_renorm ? 1 : 0, prenorm ? 1 : 0};
-    const dim3 grid((E + 7) / 8), block(512);
-    if (act_dtype == 0) hipLaunchKernelGGL((dec_route<float>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((dec_route<uint16_t>), grid, block, 0, st, p);
+bool dec_supported(int T, int E, int k) { return T >= 1 && T <= DEC_MAX_T && T * E <= DEC_MAX_TE && k <= MOE_MAX_K; }
+
+hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
+                             int T, int d, int E, bool prenorm, hipStream_t st) {
+    DecLogitsArgs p{x, wr, b, logits, xn, T, d, E, prenorm ? 1 : 0};
+    const dim3 grid((E + 3) / 4), block(256);
+    if (act_dtype == 0) hipLaunchKernelGGL((dec_logits<float>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((dec_logits<uint16_t>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
 static unsigned dec_grid(int64_t max_items) {
-    int64_t waves = max_items < 256 * 16 ? max_items : 256 * 16;
+    // two resident workgroups of 4 wavefronts per CU (the routing prologue's LDS), items loop
+    int64_t waves = max_items < 256 * 8 ? max_items : 256 * 8;
     int64_t blocks = (waves + 3) / 4;
     return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
-hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const int32_t* meta, const int4* slots,
-                          const int32_t* pos_tok, const float* pos_gate, const void* w13, const uint8_t* w13s,
-                          const void* s13, const uint8_t* s13s, const void* w2, const uint8_t* w2s, const void* s2,
-                          const uint8_t* s2s, float* a, void* out, int T, int d, int f, int fs, int k, int E,
-                          int n_shared, bool accumulate, hipStream_t st, hipEvent_t ev_up_done,
-                          hipEvent_t ev_down_start) {
+hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* logits, int32_t* topk_idx,
+                          float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
+                          bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
+                          const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st,
+                          hipEvent_t ev_up_done, hipEvent_t ev_down_start) {
     const int fmax = (n_shared && fs > f) ? fs : f;
-    DecFfnArgs p{x, meta, slots, pos_tok, pos_gate, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s,
-                 (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k,
-                 accumulate ? 1 : 0};
+    DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0};
+    DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
+                 (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0};
     const int64_t max_slots = (int64_t)(T * k < E ? T * k : E);
-    // gate/up
     if (wt == 0) {
         constexpr int R = 2;
         const int64_t items = max_slots * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
@@ -538,16 +522,15 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const int32_t* m
     if (e != hipSuccess) return e;
     if (ev_up_done && (e = hipEventRecord(ev_up_done, st)) != hipSuccess) return e;
     if (ev_down_start && (e = hipEventRecord(ev_down_start, st)) != hipSuccess) return e;
-    // down + combine
-#define MOE_DW2(WTV, RV, UV, SBV)                                                                                    \
-    do {                                                                                                             \
-        const int64_t items = (d + RV - 1) / RV;                                                                     \
-        if (out_bf16) hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, SBV, true>), dim3(dec_grid(items)), dim3(256), 0, st, p); \
-        else hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, SBV, false>), dim3(dec_grid(items)), dim3(256), 0, st, p);       \
+#define MOE_DW2(WTV, RV, UV)                                                                                     \
+    do {                                                                                                         \
+        const dim3 grid((d + RV - 1) / RV);                                                                      \
+        if (out_bf16) hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, true>), grid, dim3(512), 0, st, p);                 \
+        else hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                         \
     } while (0)
-    if (wt == 0) MOE_DW2(0, 1, 1, 8);
-    else if (wt == 1) MOE_DW2(1, 1, 2, 8);
-    else MOE_DW2(2, 2, 1, 8);
+    if (wt == 0) MOE_DW2(0, 2, 1);
+    else if (wt == 1) MOE_DW2(1, 4, 2);
+    else MOE_DW2(2, 4, 1);
 #undef MOE_DW2
     return hipGetLastError();
 }

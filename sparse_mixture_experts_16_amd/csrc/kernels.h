@@ -47,19 +47,17 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            const uint8_t* s2s, uint16_t* y, uint16_t* y_shared, int T, int d, int f, int fs, int k,
                            int E, int n_shared, hipStream_t st);
 
-// Decode path (T <= 32): fused router (logits, top-k, gates, grouping, slot table) and the FFN.
-hipError_t launch_dec_route(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
-                            int32_t* topk_idx, float* topk_w, int32_t* idx_out, int32_t* counts, int32_t* offsets,
-                            int32_t* perm, int32_t* inv, int32_t* meta, int4* slots, int32_t* pos_tok,
-                            float* pos_gate, void* xn, unsigned* ticket, int T, int d, int E, int k, int n_shared,
-                            bool no_renorm, bool prenorm, hipStream_t st);
-// ev_mid (nullable) is recorded between the gate/up and the down kernel.
-hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const int32_t* meta, const int4* slots,
-                          const int32_t* pos_tok, const float* pos_gate, const void* w13, const uint8_t* w13s,
-                          const void* s13, const uint8_t* s13s, const void* w2, const uint8_t* w2s, const void* s2,
-                          const uint8_t* s2s, float* a, void* out, int T, int d, int f, int fs, int k, int E,
-                          int n_shared, bool accumulate, hipStream_t st, hipEvent_t ev_up_done,
-                          hipEvent_t ev_down_start);
+// Decode path (T <= 32, T*E <= 8192): router logits, then the FFN kernels (the gate/up kernel
+// redoes the routing per workgroup in LDS; workgroup 0 publishes it).
+bool dec_supported(int T, int E, int k);
+hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
+                             int T, int d, int E, bool prenorm, hipStream_t st);
+hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* logits, int32_t* topk_idx,
+                          float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
+                          bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
+                          const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st,
+                          hipEvent_t ev_up_done, hipEvent_t ev_down_start);
 
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
                           const void* ysh, void* out, int T, int d, int k, bool accumulate, hipStream_t st);
