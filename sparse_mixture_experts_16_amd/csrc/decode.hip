@@ -67,10 +67,13 @@ struct DecLogitsArgs {
     int T, d, E, prenorm;
 };
 
+// x tile [T, KT] staged in LDS (bf16 kept as bf16, f32 as f32); one wavefront per router row.
 template <typename A>
 __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
     constexpr int V = rvec<A>::N;
+    constexpr int KT = sizeof(A) == 2 ? 1024 : 512;  // 64 KB of LDS for 32 tokens
     __shared__ float s_inv[DEC_MAX_T];
+    __shared__ __attribute__((aligned(16))) A s_x[DEC_MAX_T * KT];
     const int lane = lane_id(), wv = wave_id();
     const int T = p.T, d = p.d;
     if (p.prenorm) {
@@ -85,47 +88,50 @@ __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
             if (lane == 0) s_inv[t] = 1.0f / sqrtf(ss / (float)d + 1e-6f);
         }
         __syncthreads();
-        if (blockIdx.x == 0)
-            for (int t = 0; t < T; ++t)
-                for (int i = threadIdx.x; i < d; i += blockDim.x) {
-                    const float v = reinterpret_cast<const float*>(p.x)[(int64_t)t * d + i] * s_inv[t];
-                    io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)t * d + i, v);
-                }
     }
     const int e = blockIdx.x * 4 + wv;
-    if (e >= p.E) return;
-    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)e * d;
-    const float bias = p.b ? p.b[e] : 0.0f;
-    for (int t0 = 0; t0 < T; t0 += 8) {
-        float acc[8];
+    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)(e < p.E ? e : 0) * d;
+    float acc[DEC_MAX_T];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-        for (int i = lane * V; i < d; i += MOE_WAVE * V) {
-            float wvv[V];
-            rvec<A>::load(w + i, wvv);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (t0 + q >= T) break;
-                float xv[V];
-                if (p.prenorm) {
-                    const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d + i;
-                    const float inv = s_inv[t0 + q];
-#pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        const float hv = h[v] * inv;
-                        xv[v] = sizeof(A) == 2 ? bf16_to_f32(f32_to_bf16(hv)) : hv;  // the value the FFN reads
-                    }
-                } else {
-                    rvec<A>::load(reinterpret_cast<const A*>(p.x) + (int64_t)(t0 + q) * d + i, xv);
-                }
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[q] = fmaf(wvv[v], xv[v], acc[q]);
+    for (int t = 0; t < DEC_MAX_T; ++t) acc[t] = 0.0f;
+    for (int k0 = 0; k0 < d; k0 += KT) {
+        const int kt = min(KT, d - k0);
+        // stage x[:, k0:k0+kt]; with the stack input, normalise and round as the FFN will see it
+        __syncthreads();
+        for (int i = threadIdx.x; i < T * kt; i += blockDim.x) {
+            const int t = i / kt, c = i - t * kt;
+            if (p.prenorm) {
+                const float v = reinterpret_cast<const float*>(p.x)[(int64_t)t * d + k0 + c] * s_inv[t];
+                io<A>::st(s_x, t * KT + c, v);
+                if (blockIdx.x == 0) io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)t * d + k0 + c, v);
+            } else {
+                s_x[t * KT + c] = reinterpret_cast<const A*>(p.x)[(int64_t)t * d + k0 + c];
             }
         }
+        __syncthreads();
+        if (e < p.E) {
+            for (int c = lane * V; c < kt; c += MOE_WAVE * V) {
+                float wvv[V];
+                rvec<A>::load(w + k0 + c, wvv);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float s = wave_sum(acc[q]);
-            if (lane == 0 && t0 + q < T) p.logits[(int64_t)(t0 + q) * p.E + e] = s + bias;
+                for (int t = 0; t < DEC_MAX_T; ++t) {
+                    if (t < T) {
+                        float xv[V];
+                        rvec<A>::load(s_x + t * KT + c, xv);
+#pragma unroll
+                        for (int v = 0; v < V; ++v) acc[t] = fmaf(wvv[v], xv[v], acc[t]);
+                    }
+                }
+            }
+        }
+    }
+    if (e >= p.E) return;
+    const float bias = p.b ? p.b[e] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < DEC_MAX_T; ++t) {
+        if (t < T) {
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0) p.logits[(int64_t)t * p.E + e] = sum + bias;
         }
     }
 }
@@ -138,10 +144,15 @@ __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
 struct DecRoute {
     int n_slots;
     int n_routed;
-    int4 slot[MOE_MAX_E + 1];
-    float gate[DEC_MAX_T * MOE_MAX_K];  // [t][j]
-    int sel[DEC_MAX_T * MOE_MAX_K];     // [t][j]
+    int4* slot;   // [E + 1]
+    float* gate;  // [T * k], [t][j]
+    int* sel;     // [T * k]
 };
+
+// Dynamic LDS carve-up of the routing prologue: slots, logits, gates, experts, counts, masks.
+__host__ __device__ inline size_t dec_route_lds_bytes(int T, int E, int k) {
+    return (size_t)(E + 1) * 16 + (size_t)T * E * 4 + (size_t)T * k * 8 + (size_t)E * 8 + 16;
+}
 
 struct DecRouteIO {
     const float* logits;
@@ -156,6 +167,7 @@ struct DecRouteIO {
 
 __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
     const bool pub = blockIdx.x == 0;
     for (int i = tid; i < T * E; i += blockDim.x) s_logits[i] = io.logits[i];
@@ -165,7 +177,7 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     }
     __syncthreads();
     // top-k + gates, a wavefront per token
-    for (int t = wv; t < T; t += 4) {
+    for (int t = wv; t < T; t += NW) {
         const float* l = s_logits + t * E;
         uint64_t key[MOE_MAX_E / MOE_WAVE];
 #pragma unroll
@@ -243,7 +255,7 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     __syncthreads();
     if (pub) {
         // gate per sorted position for the down kernel: a slot's positions follow its tokens in order
-        for (int s = wv; s < R.n_slots; s += 4) {
+        for (int s = wv; s < R.n_slots; s += NW) {
             const int4 S = R.slot[s];
             if (lane == 0) io.slots[s] = S;
             const uint32_t m = (uint32_t)S.w;
@@ -280,15 +292,23 @@ template <int WT> struct DecAct { using T = uint16_t; };
 template <> struct DecAct<0> { using T = float; };
 
 template <int WT, int R, int U>
-__global__ void __launch_bounds__(256) dec_w13(DecFfnArgs p) {
+__global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
     using W = WChunk<WT>;
     using A = typename DecAct<WT>::T;
     constexpr int EC = W::EC;
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     __shared__ DecRoute rs;
-    __shared__ float s_logits[DEC_MAX_TE];
-    __shared__ int s_cnt[MOE_MAX_E];
-    __shared__ int s_mask[MOE_MAX_E];
-    dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask);
+    {
+        const int T = p.rt.T, E = p.rt.E, k = p.rt.k;
+        unsigned char* q = dyn_lds;
+        rs.slot = reinterpret_cast<int4*>(q); q += (size_t)(E + 1) * 16;
+        float* s_logits = reinterpret_cast<float*>(q); q += (size_t)T * E * 4;
+        rs.gate = reinterpret_cast<float*>(q); q += (size_t)T * k * 4;
+        rs.sel = reinterpret_cast<int*>(q); q += (size_t)T * k * 4;
+        int* s_cnt = reinterpret_cast<int*>(q); q += (size_t)E * 4;
+        int* s_mask = reinterpret_cast<int*>(q);
+        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask);
+    }
 
     const int lane = lane_id();
     const int ngr = (p.f + R - 1) / R, ngs = (p.fs + R - 1) / R;
@@ -297,7 +317,8 @@ __global__ void __launch_bounds__(256) dec_w13(DecFfnArgs p) {
     const int NC = p.d / EC;
     const int64_t rb = row_bytes(WT, p.d), sb = p.d / 32;
     const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
-    for (int item = blockIdx.x * 4 + wave_id(); item < n_items; item += gridDim.x * 4) {
+    const int NWB = blockDim.x / MOE_WAVE;
+    for (int item = blockIdx.x * NWB + wave_id(); item < n_items; item += gridDim.x * NWB) {
         const int s = item < r_items ? item / ngr : rs.n_routed;
         const int jg = item < r_items ? item % ngr : item - r_items;
         const int4 S = rs.slot[s];
@@ -476,7 +497,9 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
 // ------------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------------
-bool dec_supported(int T, int E, int k) { return T >= 1 && T <= DEC_MAX_T && T * E <= DEC_MAX_TE && k <= MOE_MAX_K; }
+bool dec_supported(int T, int E, int k) {
+    return T >= 1 && T <= DEC_MAX_T && T * E <= DEC_MAX_TE && k <= MOE_MAX_K && dec_route_lds_bytes(T, E, k) <= 60 * 1024;
+}
 
 hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
                              int T, int d, int E, bool prenorm, hipStream_t st) {
@@ -487,10 +510,11 @@ hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const
     return hipGetLastError();
 }
 
+// One 8-wavefront workgroup per CU at most (the routing prologue runs once per workgroup);
+// the wavefronts loop over the (slot, R columns) items.
 static unsigned dec_grid(int64_t max_items) {
-    // two resident workgroups of 4 wavefronts per CU (the routing prologue's LDS), items loop
-    int64_t waves = max_items < 256 * 8 ? max_items : 256 * 8;
-    int64_t blocks = (waves + 3) / 4;
+    int64_t blocks = (max_items + 7) / 8;
+    if (blocks > 256) blocks = 256;
     return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
@@ -505,19 +529,16 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
                  (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0};
     const int64_t max_slots = (int64_t)(T * k < E ? T * k : E);
-    if (wt == 0) {
-        constexpr int R = 2;
-        const int64_t items = max_slots * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((dec_w13<0, R, 1>), dim3(dec_grid(items)), dim3(256), 0, st, p);
-    } else if (wt == 1) {
-        constexpr int R = 2;
-        const int64_t items = max_slots * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((dec_w13<1, R, 4>), dim3(dec_grid(items)), dim3(256), 0, st, p);
-    } else {
-        constexpr int R = 4;
-        const int64_t items = max_slots * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((dec_w13<2, R, 2>), dim3(dec_grid(items)), dim3(256), 0, st, p);
-    }
+    const size_t lds = dec_route_lds_bytes(T, E, k);
+#define MOE_DW13(WTV, RV, UV)                                                                                    \
+    do {                                                                                                         \
+        const int64_t items = max_slots * ((f + RV - 1) / RV) + (n_shared ? (fs + RV - 1) / RV : 0);             \
+        hipLaunchKernelGGL((dec_w13<WTV, RV, UV>), dim3(dec_grid(items)), dim3(512), lds, st, p);               \
+    } while (0)
+    if (wt == 0) MOE_DW13(0, 2, 1);
+    else if (wt == 1) MOE_DW13(1, 4, 4);
+    else MOE_DW13(2, 4, 2);
+#undef MOE_DW13
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_up_done && (e = hipEventRecord(ev_up_done, st)) != hipSuccess) return e;
@@ -528,9 +549,9 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
         if (out_bf16) hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, true>), grid, dim3(512), 0, st, p);                 \
         else hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                         \
     } while (0)
-    if (wt == 0) MOE_DW2(0, 2, 1);
-    else if (wt == 1) MOE_DW2(1, 4, 2);
-    else MOE_DW2(2, 4, 1);
+    if (wt == 0) MOE_DW2(0, 4, 1);
+    else if (wt == 1) MOE_DW2(1, 8, 2);
+    else MOE_DW2(2, 16, 1);
 #undef MOE_DW2
     return hipGetLastError();
 }
