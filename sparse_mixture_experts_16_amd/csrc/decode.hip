@@ -67,71 +67,80 @@ struct DecLogitsArgs {
     int T, d, E, prenorm;
 };
 
-// x tile [T, KT] staged in LDS (bf16 kept as bf16, f32 as f32); one wavefront per router row.
+// One wavefront per (router row, group of 8 tokens): grid = (E/4, T/8).  The row and the
+// tokens' x chunks are loaded together before any arithmetic so their latencies overlap.
 template <typename A>
 __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
     constexpr int V = rvec<A>::N;
-    constexpr int KT = sizeof(A) == 2 ? 1024 : 512;  // 64 KB of LDS for 32 tokens
-    __shared__ float s_inv[DEC_MAX_T];
-    __shared__ __attribute__((aligned(16))) A s_x[DEC_MAX_T * KT];
+    __shared__ float s_inv[8];
     const int lane = lane_id(), wv = wave_id();
     const int T = p.T, d = p.d;
+    const int t0 = blockIdx.y * 8;
+    const int nt = min(8, T - t0);
     if (p.prenorm) {
-        for (int t = wv; t < T; t += 4) {
-            const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * d;
+        for (int q = wv; q < nt; q += 4) {
+            const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d;
             float ss = 0.0f;
             for (int i = lane * 4; i < d; i += MOE_WAVE * 4) {
-                const float4 q = *reinterpret_cast<const float4*>(h + i);
-                ss = fmaf(q.x, q.x, ss); ss = fmaf(q.y, q.y, ss); ss = fmaf(q.z, q.z, ss); ss = fmaf(q.w, q.w, ss);
+                const float4 v = *reinterpret_cast<const float4*>(h + i);
+                ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
             }
             ss = wave_sum(ss);
-            if (lane == 0) s_inv[t] = 1.0f / sqrtf(ss / (float)d + 1e-6f);
+            if (lane == 0) s_inv[q] = 1.0f / sqrtf(ss / (float)d + 1e-6f);
         }
         __syncthreads();
+        if (blockIdx.x == 0)
+            for (int q = 0; q < nt; ++q)
+                for (int i = threadIdx.x; i < d; i += blockDim.x) {
+                    const float v = reinterpret_cast<const float*>(p.x)[(int64_t)(t0 + q) * d + i] * s_inv[q];
+                    io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)(t0 + q) * d + i, v);
+                }
     }
     const int e = blockIdx.x * 4 + wv;
-    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)(e < p.E ? e : 0) * d;
-    float acc[DEC_MAX_T];
+    if (e >= p.E) return;
+    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)e * d;
+    float acc[8];
 #pragma unroll
-    for (int t = 0; t < DEC_MAX_T; ++t) acc[t] = 0.0f;
-    for (int k0 = 0; k0 < d; k0 += KT) {
-        const int kt = min(KT, d - k0);
-        // stage x[:, k0:k0+kt]; with the stack input, normalise and round as the FFN will see it
-        __syncthreads();
-        for (int i = threadIdx.x; i < T * kt; i += blockDim.x) {
-            const int t = i / kt, c = i - t * kt;
-            if (p.prenorm) {
-                const float v = reinterpret_cast<const float*>(p.x)[(int64_t)t * d + k0 + c] * s_inv[t];
-                io<A>::st(s_x, t * KT + c, v);
-                if (blockIdx.x == 0) io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)t * d + k0 + c, v);
-            } else {
-                s_x[t * KT + c] = reinterpret_cast<const A*>(p.x)[(int64_t)t * d + k0 + c];
-            }
-        }
-        __syncthreads();
-        if (e < p.E) {
-            for (int c = lane * V; c < kt; c += MOE_WAVE * V) {
-                float wvv[V];
-                rvec<A>::load(w + k0 + c, wvv);
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int i = lane * V; i < d; i += MOE_WAVE * V) {
+        float wvv[V], xv[8][V];
+        rvec<A>::load(w + i, wvv);
 #pragma unroll
-                for (int t = 0; t < DEC_MAX_T; ++t) {
-                    if (t < T) {
-                        float xv[V];
-                        rvec<A>::load(s_x + t * KT + c, xv);
-#pragma unroll
-                        for (int v = 0; v < V; ++v) acc[t] = fmaf(wvv[v], xv[v], acc[t]);
+        for (int q = 0; q < 8; ++q) {
+            if (q < nt) {
+                if (p.prenorm) {
+                    const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d + i;
+                    float hv[V];
+                    if (V == 8) {
+                        const float4 a = reinterpret_cast<const float4*>(h)[0], b = reinterpret_cast<const float4*>(h)[1];
+                        hv[0] = a.x; hv[1] = a.y; hv[2] = a.z; hv[3] = a.w;
+                        hv[4 % V] = b.x; hv[5 % V] = b.y; hv[6 % V] = b.z; hv[7 % V] = b.w;
+                    } else {
+                        const float4 a = reinterpret_cast<const float4*>(h)[0];
+                        hv[0] = a.x; hv[1] = a.y; hv[2 % V] = a.z; hv[3 % V] = a.w;
                     }
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        const float x = hv[v] * s_inv[q];
+                        xv[q][v] = sizeof(A) == 2 ? bf16_to_f32(f32_to_bf16(x)) : x;  // the value the FFN reads
+                    }
+                } else {
+                    rvec<A>::load(reinterpret_cast<const A*>(p.x) + (int64_t)(t0 + q) * d + i, xv[q]);
                 }
             }
         }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q < nt)
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[q] = fmaf(wvv[v], xv[q][v], acc[q]);
     }
-    if (e >= p.E) return;
     const float bias = p.b ? p.b[e] : 0.0f;
 #pragma unroll
-    for (int t = 0; t < DEC_MAX_T; ++t) {
-        if (t < T) {
-            const float sum = wave_sum(acc[t]);
-            if (lane == 0) p.logits[(int64_t)t * p.E + e] = sum + bias;
+    for (int q = 0; q < 8; ++q) {
+        if (q < nt) {
+            const float sum = wave_sum(acc[q]);
+            if (lane == 0) p.logits[(int64_t)(t0 + q) * p.E + e] = sum + bias;
         }
     }
 }
@@ -504,7 +513,7 @@ bool dec_supported(int T, int E, int k) {
 hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
                              int T, int d, int E, bool prenorm, hipStream_t st) {
     DecLogitsArgs p{x, wr, b, logits, xn, T, d, E, prenorm ? 1 : 0};
-    const dim3 grid((E + 3) / 4), block(256);
+    const dim3 grid((E + 3) / 4, (T + 7) / 8), block(256);
     if (act_dtype == 0) hipLaunchKernelGGL((dec_logits<float>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((dec_logits<uint16_t>), grid, block, 0, st, p);
     return hipGetLastError();
@@ -535,9 +544,10 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
         const int64_t items = max_slots * ((f + RV - 1) / RV) + (n_shared ? (fs + RV - 1) / RV : 0);             \
         hipLaunchKernelGGL((dec_w13<WTV, RV, UV>), dim3(dec_grid(items)), dim3(512), lds, st, p);               \
     } while (0)
+    // about 8 16-byte loads per lane in flight per item (HBM streams best at 4-8 per lane)
     if (wt == 0) MOE_DW13(0, 2, 1);
-    else if (wt == 1) MOE_DW13(1, 4, 4);
-    else MOE_DW13(2, 4, 2);
+    else if (wt == 1) MOE_DW13(1, 1, 4);
+    else MOE_DW13(2, 2, 2);
 #undef MOE_DW13
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -550,8 +560,8 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
         else hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                         \
     } while (0)
     if (wt == 0) MOE_DW2(0, 4, 1);
-    else if (wt == 1) MOE_DW2(1, 8, 2);
-    else MOE_DW2(2, 16, 1);
+    else if (wt == 1) MOE_DW2(1, 4, 2);
+    else MOE_DW2(2, 8, 1);
 #undef MOE_DW2
     return hipGetLastError();
 }

@@ -73,38 +73,47 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     return r;
 }
 
-// BK: K depth of one LDS stage (64, or 32 for the split down projection).
+// Tile: BM = 128 token rows x BN weight rows x BK = 32 of K per LDS stage, 256 threads as 2 x 2
+// wavefronts, each owning 64 x BN/2 with v_mfma_f32_32x32x16_bf16 (A lane l: row l%32,
+// k = 8*(l/32)..+7; B lane l: column l%32, same k; accumulator j of lane l: row
+// 8*(j/4) + 4*(l/32) + j%4, column l%32).  Wave tiles of 64 x 128 (gate/up) read 6 KB of LDS
+// fragments per 8 MFMAs, 3/4 of the LDS port at full MFMA rate.
 // SPLIT: the A operand comes as two bf16 planes a = hi + lo (lo = a - hi rounded to bf16), and
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
-template <int MODE, int WT, int BK, bool SPLIT>
-__global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
-    constexpr int LDP = BK + 8;          // padded LDS row pitch (bf16 elements)
-    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
-    constexpr int RPP = 256 / CPR;       // tile rows covered by one pass of the workgroup
-    constexpr int NP = TBM / RPP;        // passes per 128-row tile
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int MODE, int WT, int BN, bool SPLIT>
+__global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
+    constexpr int BM = TBM, BK = 32;
+    constexpr int LDP = BK + 8;          // padded LDS row pitch (bf16): 80 B, conflict-free fragment reads
+    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row (4)
+    constexpr int NPA = BM * CPR / 256;  // A chunks per thread (2)
+    constexpr int NPB = BN * CPR / 256;  // B chunks per thread (bf16: 2 or 4)
     constexpr int NPL = SPLIT ? 2 : 1;   // A planes
-    constexpr int C4 = BK / 32;          // MXFP4: 16-byte code chunks per tile row
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][NPL][TBM * LDP];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][TBN * LDP];
+    constexpr int WN = BN / 2;           // wave tile columns
+    constexpr int NT32 = WN / 32;        // 32-wide MFMA column tiles per wave (2 or 4)
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][NPL][BM * LDP];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDP];
     __shared__ int s_pref[MOE_MAX_E + 2];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
     const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
     const int P = p.T * p.k;
 
-    // ---- flat tile list: tiles of group g = ceil(rows_g / 128) * ntiles_g
+    // ---- flat tile list: tiles of group g = ceil(rows_g / BM) * ntiles_g
     auto tiles_of = [&](int g) -> int {
         int rows, nt;
         if (MODE == MODE_ROUTER) {
             rows = p.T;
-            nt = (p.E + TBN - 1) / TBN;
+            nt = (p.E + BN - 1) / BN;
         } else {
             const bool sh = g == p.E;
             rows = sh ? p.T : p.offsets[g + 1] - p.offsets[g];
-            nt = (MODE == MODE_W13) ? (sh ? p.fs : p.f) / 64 : (p.d + TBN - 1) / TBN;
+            nt = (MODE == MODE_W13) ? (sh ? p.fs : p.f) / (BN / 2) : (p.d + BN - 1) / BN;
         }
-        return ((rows + TBM - 1) / TBM) * nt;
+        return ((rows + BM - 1) / BM) * nt;
     };
     if (wv == 0) {
         const int per = (G + 63) / 64;
@@ -145,31 +154,29 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
     const uint8_t* W;
     const uint8_t* WS;
     if (MODE == MODE_ROUTER) {
-        rows_g = p.T; base = 0; K = p.d; N = p.E; ntiles = (p.E + TBN - 1) / TBN;
+        rows_g = p.T; base = 0; K = p.d; N = p.E; ntiles = (p.E + BN - 1) / BN;
         W = p.w; WS = nullptr;
     } else {
         rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
         base = shared ? 0 : p.offsets[g];
-        if (MODE == MODE_W13) { K = p.d; N = 2 * fg; ntiles = fg / 64; }
-        else { K = fg; N = p.d; ntiles = (p.d + TBN - 1) / TBN; }
+        if (MODE == MODE_W13) { K = p.d; N = 2 * fg; ntiles = fg / (BN / 2); }
+        else { K = fg; N = p.d; ntiles = (p.d + BN - 1) / BN; }
         const int64_t rb = row_bytes(WT, K), sb = K / 32;
         W = shared ? p.sw : p.w + (int64_t)g * N * rb;
         WS = (WT == 2) ? (shared ? p.swsc : p.wsc + (int64_t)g * N * sb) : nullptr;
     }
     const int local = L - s_pref[g];
     const int mt = local / ntiles, nt = local % ntiles;
-    const int m0 = mt * TBM;
-    const int mrows = min(TBM, rows_g - m0);
+    const int m0 = mt * BM;
+    const int mrows = min(BM, rows_g - m0);
     const int64_t wrb = row_bytes(WT, K), wsb = K / 32;
 
     // ---- this thread's global source rows for the A and B tiles
-    const int kc = tid % CPR;  // 16-byte chunk within a BK-wide K slice (bf16)
-    const uint16_t* arow[NP];
-    const uint8_t* brow[NP];
-    const uint8_t* bsrow = nullptr;
+    const int kc = tid % CPR;  // 16-byte chunk within the BK slice
+    const uint16_t* arow[NPA];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int r = tid / CPR + RPP * i;
+    for (int i = 0; i < NPA; ++i) {
+        const int r = tid / CPR + (256 / CPR) * i;
         if (r < mrows) {
             int64_t src;
             if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
@@ -180,35 +187,40 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
             arow[i] = nullptr;
         }
     }
-    auto wrow_of = [&](int n) -> int {  // LDS B row -> weight row (or -1)
+    // LDS B row n -> weight row.  Gate/up: each wavefront column holds BN/4 gate rows and the
+    // matching BN/4 up rows, so SwiGLU pairs meet in the same lane.
+    auto wrow_of = [&](int n) -> int {
         if (MODE == MODE_W13) {
-            const int j0 = nt * 64, h = n >> 6, w = n & 63;
-            return w < 32 ? j0 + h * 32 + w : fg + j0 + h * 32 + (w - 32);
+            constexpr int H = BN / 4;
+            const int j0 = nt * (BN / 2), h = n / (2 * H), w = n % (2 * H);
+            return w < H ? j0 + h * H + w : fg + j0 + h * H + (w - H);
         }
-        const int r = nt * TBN + n;
+        const int r = nt * BN + n;
         return r < N ? r : -1;
     };
+    const uint8_t* brow[NPB];
+    const uint8_t* bsrow = nullptr;
     if (WT == 1) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int wr = wrow_of(tid / CPR + RPP * i);
+        for (int i = 0; i < NPB; ++i) {
+            const int wr = wrow_of(tid / CPR + (256 / CPR) * i);
             brow[i] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) brow[i] = nullptr;
-        if (tid < TBN * C4) {
-            const int wr = wrow_of(tid / C4);
+        for (int i = 0; i < NPB; ++i) brow[i] = nullptr;
+        if (tid < BN) {  // one 16-byte code chunk (32 elements = BK) and its scale per B row
+            const int wr = wrow_of(tid);
             brow[0] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
             bsrow = wr >= 0 ? WS + (int64_t)wr * wsb : nullptr;
         }
     }
 
-    uint4 ra[NPL][NP], rb[NP];
+    uint4 ra[NPL][NPA], rb[NPB];
     uint32_t rs = 127u;
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
+        for (int i = 0; i < NPA; ++i) {
             ra[0][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
             if (SPLIT)
                 ra[NPL - 1][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + p.lo_off + k0 + kc * 8)
@@ -216,30 +228,28 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
         }
         if (WT == 1) {
 #pragma unroll
-            for (int i = 0; i < NP; ++i)
+            for (int i = 0; i < NPB; ++i)
                 rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + (int64_t)(k0 + kc * 8) * 2) : make_uint4(0, 0, 0, 0);
         } else {
-            const int half = tid % C4;
-            rb[0] = brow[0] ? *reinterpret_cast<const uint4*>(brow[0] + k0 / 2 + half * 16) : make_uint4(0, 0, 0, 0);
-            rs = bsrow ? bsrow[k0 / 32 + half] : 127u;
+            rb[0] = brow[0] ? *reinterpret_cast<const uint4*>(brow[0] + k0 / 2) : make_uint4(0, 0, 0, 0);
+            rs = bsrow ? bsrow[k0 / 32] : 127u;
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int r = tid / CPR + RPP * i;
+        for (int i = 0; i < NPA; ++i) {
+            const int r = tid / CPR + (256 / CPR) * i;
 #pragma unroll
             for (int pl = 0; pl < NPL; ++pl) *reinterpret_cast<uint4*>(&sA[buf][pl][r * LDP + kc * 8]) = ra[pl][i];
         }
         if (WT == 1) {
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int n = tid / CPR + RPP * i;
+            for (int i = 0; i < NPB; ++i) {
+                const int n = tid / CPR + (256 / CPR) * i;
                 *reinterpret_cast<uint4*>(&sB[buf][n * LDP + kc * 8]) = rb[i];
             }
-        } else if (tid < TBN * C4) {
-            const int n = tid / C4, half = tid % C4;
-            uint16_t* dst = &sB[buf][n * LDP + half * 32];
+        } else if (tid < BN) {
+            uint16_t* dst = &sB[buf][tid * LDP];
             *reinterpret_cast<uint4*>(dst + 0) = fp4x8_to_bf16(rb[0].x, rs);
             *reinterpret_cast<uint4*>(dst + 8) = fp4x8_to_bf16(rb[0].y, rs);
             *reinterpret_cast<uint4*>(dst + 16) = fp4x8_to_bf16(rb[0].z, rs);
@@ -247,11 +257,13 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
         }
     };
 
-    f32x4_t acc[4][4];
+    f32x16_t acc[2][NT32];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int b = 0; b < NT32; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.0f;
 
     const int nk = K / BK;
     gload(0);
@@ -261,64 +273,64 @@ __global__ void __launch_bounds__(256) ggemm(GemmArgs p) {
         const int buf = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            bf16x8_t bfr[4];
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8v bfr[NT32];
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
-                bfr[ns] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    &sB[buf][(wn * 64 + ns * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+            for (int ns = 0; ns < NT32; ++ns)
+                bfr[ns] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(
+                    &sB[buf][(wn * WN + ns * 32 + (lane & 31)) * LDP + kk * 16 + (lane >> 5) * 8]));
 #pragma unroll
             for (int pl = 0; pl < NPL; ++pl) {
-                bf16x8_t af[4];
+                bf16x8v af[2];
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
-                    af[ms] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                        &sA[buf][pl][(wm * 64 + ms * 16 + (lane & 15)) * LDP + kk * 32 + (lane >> 4) * 8]));
+                for (int ms = 0; ms < 2; ++ms)
+                    af[ms] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(
+                        &sA[buf][pl][(wm * 64 + ms * 32 + (lane & 31)) * LDP + kk * 16 + (lane >> 5) * 8]));
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
+                for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-                    for (int ns = 0; ns < 4; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+                    for (int ns = 0; ns < NT32; ++ns)
+                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
             }
         }
         if (kt + 1 < nk) sstore(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue
+    // ---- epilogue: accumulator j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms) {
+    for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = wm * 64 + ms * 16 + (lane >> 4) * 4 + jj;
+        for (int j = 0; j < 16; ++j) {
+            const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
             if (r >= mrows) continue;
             const int row = m0 + r;
             if (MODE == MODE_W13) {
                 uint16_t* o = reinterpret_cast<uint16_t*>(p.out) +
                               (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f);
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    const int j = nt * 64 + wn * 32 + ns * 16 + (lane & 15);
-                    const float gt = acc[ms][ns][jj], up = acc[ms][ns + 2][jj];
+                for (int ns = 0; ns < NT32 / 2; ++ns) {
+                    const int jc = nt * (BN / 2) + wn * (BN / 4) + ns * 32 + (lane & 31);
+                    const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
                     const float av = gt / (1.0f + expf(-gt)) * up;
                     const uint16_t hi = f32_to_bf16(av);
-                    o[j] = hi;
-                    o[p.lo_off + j] = f32_to_bf16(av - bf16_to_f32(hi));
+                    o[jc] = hi;
+                    o[p.lo_off + jc] = f32_to_bf16(av - bf16_to_f32(hi));
                 }
             } else if (MODE == MODE_W2) {
                 uint16_t* o = shared ? p.out_sh + (int64_t)row * p.d
                                      : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d;
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns) {
-                    const int n = nt * TBN + wn * 64 + ns * 16 + (lane & 15);
-                    if (n < N) o[n] = f32_to_bf16(acc[ms][ns][jj]);
+                for (int ns = 0; ns < NT32; ++ns) {
+                    const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
+                    if (n < N) o[n] = f32_to_bf16(acc[ms][ns][j]);
                 }
             } else {
                 float* o = reinterpret_cast<float*>(p.out) + (int64_t)row * p.E;
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns) {
-                    const int n = nt * TBN + wn * 64 + ns * 16 + (lane & 15);
-                    if (n < N) o[n] = acc[ms][ns][jj] + (p.bias ? p.bias[n] : 0.0f);
+                for (int ns = 0; ns < NT32; ++ns) {
+                    const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
+                    if (n < N) o[n] = acc[ms][ns][j] + (p.bias ? p.bias[n] : 0.0f);
                 }
             }
         }
@@ -338,8 +350,8 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     p.bias = b;
     p.out = logits;
     p.T = T; p.d = d; p.E = E; p.k = 1;
-    const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + TBN - 1) / TBN);
-    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 64, false>), dim3(grid8(tiles)), dim3(256), 0, st, p);
+    const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + 127) / 128);
+    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false>), dim3(grid8(tiles)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -361,9 +373,10 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
-    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / 64, n_shared ? fs / 64 : 0));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1, 64, false>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W13, 2, 64, false>), dim3(grid), dim3(256), 0, st, p);
+    constexpr int BN = 256;  // 128 gate/up column pairs per tile
+    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W13, 2, BN, false>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -373,10 +386,11 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
-    const int nt = (d + TBN - 1) / TBN;
+    constexpr int BN = 128;
+    const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1, 32, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W2, 2, 32, true>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1, BN, true>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((ggemm<MODE_W2, 2, BN, true>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
