@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         } else {
             const bool sh = g == p.E;
             rows = sh ? p.T : p.offsets[g + 1] - p.offsets[g];
-            nt = (MODE == MODE_W13) ? (sh ? p.fs : p.f) / (BN / 2) : (p.d + BN - 1) / BN;
+            nt = (MODE == MODE_W13) ? ((sh ? p.fs : p.f) + BN / 2 - 1) / (BN / 2) : (p.d + BN - 1) / BN;
         }
         return ((rows + BM - 1) / BM) * nt;
     };
@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     } else {
         rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
         base = shared ? 0 : p.offsets[g];
-        if (MODE == MODE_W13) { K = p.d; N = 2 * fg; ntiles = fg / (BN / 2); }
+        if (MODE == MODE_W13) { K = p.d; N = 2 * fg; ntiles = (fg + BN / 2 - 1) / (BN / 2); }
         else { K = fg; N = p.d; ntiles = (p.d + BN - 1) / BN; }
         const int64_t rb = row_bytes(WT, K), sb = K / 32;
         W = shared ? p.sw : p.w + (int64_t)g * N * rb;
@@ -193,7 +193,9 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         if (MODE == MODE_W13) {
             constexpr int H = BN / 4;
             const int j0 = nt * (BN / 2), h = n / (2 * H), w = n % (2 * H);
-            return w < H ? j0 + h * H + w : fg + j0 + h * H + (w - H);
+            const int j = j0 + h * H + (w < H ? w : w - H);
+            if (j >= fg) return -1;
+            return w < H ? j : fg + j;
         }
         const int r = nt * BN + n;
         return r < N ? r : -1;
@@ -311,6 +313,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
 #pragma unroll
                 for (int ns = 0; ns < NT32 / 2; ++ns) {
                     const int jc = nt * (BN / 2) + wn * (BN / 4) + ns * 32 + (lane & 31);
+                    if (jc >= fg) continue;
                     const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
                     const float av = gt / (1.0f + expf(-gt)) * up;
                     const uint16_t hi = f32_to_bf16(av);
@@ -374,7 +377,7 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
     constexpr int BN = 256;  // 128 gate/up column pairs per tile
-    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
+    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
     if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
     else hipLaunchKernelGGL((ggemm<MODE_W13, 2, BN, false>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
