@@ -18,6 +18,7 @@ constexpr size_t ALIGN = 256;
 size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int ptr_ok(const void* p) { return p && aligned16(p); }
 
 int act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
@@ -93,8 +94,10 @@ int check_shape(const moe_shape* s) {
 
 // The MFMA kernels tile K by 64 and the gate/up columns by 64.
 bool gemm_shape_ok(const moe_shape* s) {
-    const int fs = s->n_shared ? s->shared_d_ff : 64;
-    return s->act_dtype == MOE_BF16 && s->d_model % 64 == 0 && s->d_ff % 64 == 0 && fs % 64 == 0;
+    // K steps of 32; MXFP4 scales move four 32-element blocks (one dword) at a time
+    const int q = s->weight_dtype == MOE_MXFP4 ? 128 : 64;
+    const int fs = s->n_shared ? s->shared_d_ff : q;
+    return s->act_dtype == MOE_BF16 && s->d_model % q == 0 && s->d_ff % q == 0 && fs % q == 0;
 }
 
 // Which FFN kernels run: grouped GEMV (decode) or grouped MFMA GEMM (prefill).
@@ -108,15 +111,14 @@ bool use_gemm(const moe_shape* s) {
 int check_weights(const moe_shape* s, const moe_weights* w) {
     if (!w || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w->w13) || !aligned16(w->w2)) return MOE_ERR_INVALID_ARG;
-    if (s->weight_dtype == MOE_MXFP4 && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (s->weight_dtype == MOE_MXFP4 && (!ptr_ok(w->w13_scale) || !ptr_ok(w->w2_scale))) return MOE_ERR_INVALID_ARG;
     if (s->n_shared) {
         if (!w->s13 || !w->s2 || !aligned16(w->s13) || !aligned16(w->s2)) return MOE_ERR_INVALID_ARG;
-        if (s->weight_dtype == MOE_MXFP4 && (!w->s13_scale || !w->s2_scale)) return MOE_ERR_INVALID_ARG;
+        if (s->weight_dtype == MOE_MXFP4 && (!ptr_ok(w->s13_scale) || !ptr_ok(w->s2_scale))) return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
 }
 
-int ptr_ok(const void* p) { return p && aligned16(p); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 

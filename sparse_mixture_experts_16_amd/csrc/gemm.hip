@@ -32,7 +32,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int TBM = 128, TBN = 128;
+constexpr int TBM = 128;
 enum { MODE_W13 = 0, MODE_W2 = 1, MODE_ROUTER = 2 };
 
 struct GemmArgs {
@@ -73,30 +73,58 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     return r;
 }
 
-// Tile: BM = 128 token rows x BN weight rows x BK = 32 of K per LDS stage, 256 threads as 2 x 2
-// wavefronts, each owning 64 x BN/2 with v_mfma_f32_32x32x16_bf16 (A lane l: row l%32,
+// Tile: BM = 128 token rows x BN weight rows, K in steps of BK = 32, 256 threads as 2 x 2
+// wavefronts each owning 64 x BN/2 with v_mfma_f32_32x32x16_bf16 (A lane l: row l%32,
 // k = 8*(l/32)..+7; B lane l: column l%32, same k; accumulator j of lane l: row
-// 8*(j/4) + 4*(l/32) + j%4, column l%32).  Wave tiles of 64 x 128 (gate/up) read 6 KB of LDS
-// fragments per 8 MFMAs, 3/4 of the LDS port at full MFMA rate.
+// 8*(j/4) + 4*(l/32) + j%4, column l%32).
+//
+// K pipeline: a ring of three LDS stages filled straight from HBM by global_load_lds_dwordx4
+// (each lane's 16 bytes land at the wave's LDS base + 16 * lane; no register staging).  While
+// stage kt is consumed, stages kt+1 and kt+2 are in flight; the wait for stage kt is a
+// vmcnt(n) that still lets the next stage's loads be outstanding, followed by a bare
+// s_barrier, so the compiler's full vmcnt(0) of __syncthreads never drains the pipe.
+// Tile rows are 64 bytes (32 bf16) unpadded; 16-byte chunk c of row r sits at physical chunk
+// c ^ (((r >> 1) ^ (r >> 2)) & 3), which spreads every 8 (and 16) consecutive rows' fragment
+// reads over distinct banks.
+// MXFP4 weights: the 16 code bytes of a row's 32-element block go to LDS as they are, one
+// chunk per row; each B fragment (8 codes, one dword) is expanded at read time with the
+// scaled bf16 converts (exact: E2M1 x 2^k fits bf16).  The E8M0 scales travel as one dword
+// (4 consecutive blocks) per row every fourth stage into a double-buffered LDS row list.
 // SPLIT: the A operand comes as two bf16 planes a = hi + lo (lo = a - hi rounded to bf16), and
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// s_waitcnt immediate: vmcnt(n) (n < 16), expcnt untouched, lgkmcnt(0).
+#define VM_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4))
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0); }
+__device__ __forceinline__ void dma4(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0); }
+__device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 template <int MODE, int WT, int BN, bool SPLIT>
 __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
-    constexpr int BM = TBM, BK = 32;
-    constexpr int LDP = BK + 8;          // padded LDS row pitch (bf16): 80 B, conflict-free fragment reads
-    constexpr int CPR = BK / 8;          // 16-byte chunks per tile row (4)
-    constexpr int NPA = BM * CPR / 256;  // A chunks per thread (2)
-    constexpr int NPB = BN * CPR / 256;  // B chunks per thread (bf16: 2 or 4)
-    constexpr int NPL = SPLIT ? 2 : 1;   // A planes
-    constexpr int WN = BN / 2;           // wave tile columns
-    constexpr int NT32 = WN / 32;        // 32-wide MFMA column tiles per wave (2 or 4)
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][NPL][BM * LDP];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDP];
-    __shared__ int s_pref[MOE_MAX_E + 2];
+    constexpr int BM = TBM, BK = 32, NS = 3;
+    constexpr int NPL = SPLIT ? 2 : 1;              // A planes
+    constexpr int WN = BN / 2;                      // wave tile columns
+    constexpr int NT32 = WN / 32;                   // 32-wide MFMA column tiles per wave (2 or 4)
+    constexpr int ROWE = BK;                        // bf16 elements per LDS tile row (64 B)
+    constexpr int BROW = (WT == 1) ? 32 : 8;        // uint16 per LDS B row (bf16: 64 B, MXFP4 codes: 16 B)
+    constexpr int NA = BM * 4 / 256;                // A chunks per thread per plane (2)
+    constexpr int NB = (WT == 1) ? BN * 4 / 256 : (BN + 255) / 256;  // B chunks per thread (max)
+    // vector-memory ops one stage adds per thread, counted for the wave that issues the fewest
+    constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BN >= 256 ? 1 : 0));
+    static_assert(OPS < 16, "vmcnt immediate");
+    // One LDS object carved by offsets: with a single object the compiler's wait insertion
+    // leaves LDS-DMA completion to the explicit vmcnt waits below instead of draining the
+    // whole ring before every fragment read.
+    constexpr int SZ_A = NS * NPL * BM * ROWE * 2, SZ_B = NS * BN * BROW * 2, SZ_S = (WT == 2 ? 2 * BN * 4 : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ_A + SZ_B + SZ_S + (MOE_MAX_E + 2) * 4];
+    auto sA = reinterpret_cast<uint16_t(*)[NPL][BM * ROWE]>(smem);
+    auto sB = reinterpret_cast<uint16_t(*)[BN * BROW]>(smem + SZ_A);
+    auto sS = reinterpret_cast<uint32_t(*)[BN]>(smem + SZ_A + SZ_B);
+    int* s_pref = reinterpret_cast<int*>(smem + SZ_A + SZ_B + SZ_S);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
     const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
@@ -171,91 +199,71 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     const int mrows = min(BM, rows_g - m0);
     const int64_t wrb = row_bytes(WT, K), wsb = K / 32;
 
-    // ---- this thread's global source rows for the A and B tiles
-    const int kc = tid % CPR;  // 16-byte chunk within the BK slice
-    const uint16_t* arow[NPA];
+    // ---- this thread's global sources.  A chunk slot s = i*256 + tid holds row s/4 at physical
+    // chunk s%4; rows past the group's end re-read the tile's first row (their results are
+    // never stored).
+    const int pc = tid & 3;
+    const uint16_t* asrc[NA];
 #pragma unroll
-    for (int i = 0; i < NPA; ++i) {
-        const int r = tid / CPR + (256 / CPR) * i;
-        if (r < mrows) {
-            int64_t src;
-            if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
-            else if (MODE == MODE_W2) src = shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
-            else src = (int64_t)(m0 + r) * p.d;
-            arow[i] = p.A + src;
-        } else {
-            arow[i] = nullptr;
-        }
+    for (int i = 0; i < NA; ++i) {
+        int r = i * 64 + (tid >> 2);
+        const int c = pc ^ chunk_swz(r);
+        if (r >= mrows) r = 0;
+        int64_t src;
+        if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
+        else if (MODE == MODE_W2) src = shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
+        else src = (int64_t)(m0 + r) * p.d;
+        asrc[i] = p.A + src + c * 8;
     }
     // LDS B row n -> weight row.  Gate/up: each wavefront column holds BN/4 gate rows and the
-    // matching BN/4 up rows, so SwiGLU pairs meet in the same lane.
+    // matching BN/4 up rows, so SwiGLU pairs meet in the same lane.  Rows past the end map to
+    // weight row 0 (their columns are never stored).
     auto wrow_of = [&](int n) -> int {
         if (MODE == MODE_W13) {
             constexpr int H = BN / 4;
             const int j0 = nt * (BN / 2), h = n / (2 * H), w = n % (2 * H);
             const int j = j0 + h * H + (w < H ? w : w - H);
-            if (j >= fg) return -1;
+            if (j >= fg) return 0;
             return w < H ? j : fg + j;
         }
         const int r = nt * BN + n;
-        return r < N ? r : -1;
+        return r < N ? r : 0;
     };
-    const uint8_t* brow[NPB];
-    const uint8_t* bsrow = nullptr;
+    const uint8_t* bsrc[NB];
+    const uint8_t* ssrc = nullptr;
+    bool b_on = true, s_on = false;
     if (WT == 1) {
 #pragma unroll
-        for (int i = 0; i < NPB; ++i) {
-            const int wr = wrow_of(tid / CPR + (256 / CPR) * i);
-            brow[i] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
+        for (int i = 0; i < NB; ++i) {
+            const int n = i * 64 + (tid >> 2);
+            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (pc ^ chunk_swz(n)) * 16;
         }
     } else {
-#pragma unroll
-        for (int i = 0; i < NPB; ++i) brow[i] = nullptr;
-        if (tid < BN) {  // one 16-byte code chunk (32 elements = BK) and its scale per B row
-            const int wr = wrow_of(tid);
-            brow[0] = wr >= 0 ? W + (int64_t)wr * wrb : nullptr;
-            bsrow = wr >= 0 ? WS + (int64_t)wr * wsb : nullptr;
-        }
+        // one 16-byte code chunk (the 32-element block) per B row; BN = 128 uses waves 0-1
+        b_on = tid < BN;
+        s_on = tid < BN;
+        const int wr = wrow_of(b_on ? tid : 0);
+        bsrc[0] = W + (int64_t)wr * wrb;
+        ssrc = WS + (int64_t)wr * wsb;
     }
 
-    uint4 ra[NPL][NPA], rb[NPB];
-    uint32_t rs = 127u;
-    auto gload = [&](int k0) {
+    auto issue = [&](int kt) {
+        const int st = kt % NS;
+        const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < NPA; ++i) {
-            ra[0][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-            if (SPLIT)
-                ra[NPL - 1][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + p.lo_off + k0 + kc * 8)
-                                         : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < NA; ++i) {
+            uint16_t* dA = &sA[st][0][(i * 256 + wv * 64) * 8];
+            dma16(asrc[i] + k0, dA);
+            if (SPLIT) dma16(asrc[i] + p.lo_off + k0, &sA[st][NPL - 1][(i * 256 + wv * 64) * 8]);
         }
         if (WT == 1) {
 #pragma unroll
-            for (int i = 0; i < NPB; ++i)
-                rb[i] = brow[i] ? *reinterpret_cast<const uint4*>(brow[i] + (int64_t)(k0 + kc * 8) * 2) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < NB; ++i)
+                dma16(bsrc[i] + (int64_t)k0 * 2, &sB[st][(i * 256 + wv * 64) * 8]);
         } else {
-            rb[0] = brow[0] ? *reinterpret_cast<const uint4*>(brow[0] + k0 / 2) : make_uint4(0, 0, 0, 0);
-            rs = bsrow ? bsrow[k0 / 32] : 127u;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NPA; ++i) {
-            const int r = tid / CPR + (256 / CPR) * i;
-#pragma unroll
-            for (int pl = 0; pl < NPL; ++pl) *reinterpret_cast<uint4*>(&sA[buf][pl][r * LDP + kc * 8]) = ra[pl][i];
-        }
-        if (WT == 1) {
-#pragma unroll
-            for (int i = 0; i < NPB; ++i) {
-                const int n = tid / CPR + (256 / CPR) * i;
-                *reinterpret_cast<uint4*>(&sB[buf][n * LDP + kc * 8]) = rb[i];
-            }
-        } else if (tid < BN) {
-            uint16_t* dst = &sB[buf][tid * LDP];
-            *reinterpret_cast<uint4*>(dst + 0) = fp4x8_to_bf16(rb[0].x, rs);
-            *reinterpret_cast<uint4*>(dst + 8) = fp4x8_to_bf16(rb[0].y, rs);
-            *reinterpret_cast<uint4*>(dst + 16) = fp4x8_to_bf16(rb[0].z, rs);
-            *reinterpret_cast<uint4*>(dst + 24) = fp4x8_to_bf16(rb[0].w, rs);
+            if (b_on) dma16(bsrc[0] + k0 / 2, &sB[st][wv * 64 * 8]);
+            if (s_on && (kt & 3) == 0)
+                dma4(ssrc + kt, &sS[(kt >> 2) & 1][wv * 64]);
         }
     };
 
@@ -267,27 +275,49 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.0f;
 
+    // fragment addresses: rows r = (multiple of 32) + lane%32 all share chunk_swz(lane%32)
+    const int l32 = lane & 31, hk = lane >> 5;
+    const int fc0 = ((0 + hk) ^ chunk_swz(l32)) * 8, fc1 = ((2 + hk) ^ chunk_swz(l32)) * 8;
+
     const int nk = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    issue(0);
+    if (nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+        const int st = kt % NS;
+        asm volatile("" ::: "memory");
+        if (kt + 1 < nk) VM_WAIT(OPS);
+        else VM_WAIT(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + 2 < nk) issue(kt + 2);
+
+        uint32_t sc_w[NT32];
+        if (WT == 2) {
+#pragma unroll
+            for (int ns = 0; ns < NT32; ++ns) sc_w[ns] = sS[(kt >> 2) & 1][wn * WN + ns * 32 + l32];
+        }
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
+            const int fc = kk ? fc1 : fc0;
             bf16x8v bfr[NT32];
 #pragma unroll
-            for (int ns = 0; ns < NT32; ++ns)
-                bfr[ns] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(
-                    &sB[buf][(wn * WN + ns * 32 + (lane & 31)) * LDP + kk * 16 + (lane >> 5) * 8]));
+            for (int ns = 0; ns < NT32; ++ns) {
+                const int n = wn * WN + ns * 32 + l32;
+                if (WT == 1) {
+                    bfr[ns] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&sB[st][n * BROW + fc]));
+                } else {
+                    const uint32_t cw = *reinterpret_cast<const uint32_t*>(&sB[st][n * BROW + kk * 4 + hk * 2]);
+                    const uint32_t s8 = (sc_w[ns] >> (8 * (kt & 3))) & 0xFFu;
+                    bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(cw, s8));
+                }
+            }
 #pragma unroll
             for (int pl = 0; pl < NPL; ++pl) {
                 bf16x8v af[2];
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms)
                     af[ms] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(
-                        &sA[buf][pl][(wm * 64 + ms * 32 + (lane & 31)) * LDP + kk * 16 + (lane >> 5) * 8]));
+                        &sA[st][pl][(wm * 64 + ms * 32 + l32) * ROWE + fc]));
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
@@ -295,8 +325,6 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
                         acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
             }
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
     }
 
     // ---- epilogue: accumulator j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32

@@ -26,7 +26,7 @@ SMALL = [
     mi.LayerSpec("g_bf16", 333, 256, 128, 16, 4, 1, 192, "bf16", "bf16", 1.0, 0.05, 0.05, seed=21),
     mi.LayerSpec("g_bf16_noshared", 200, 512, 192, 24, 3, 0, 0, "bf16", "bf16", 1.0, 0.05, 0.05, seed=22),
     mi.LayerSpec("g_mxfp4", 257, 256, 128, 12, 2, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=23),
-    mi.LayerSpec("g_mxfp4_shared", 64, 192, 64, 8, 8, 1, 64, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=24),
+    mi.LayerSpec("g_mxfp4_shared", 64, 256, 128, 8, 8, 1, 128, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=24),
 ]
 
 
