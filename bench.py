@@ -297,9 +297,8 @@ def main():
     def run(name, steps, warmup):
         print(f"[bench] {name} ...", file=sys.stderr, flush=True)
         if name == "c4_stack":
-            return run_stack_workload(hip, max(steps // 5, 5), max(warmup // 5, 2))
-        big = WORKLOADS[name][1] > 32
-        return run_layer_workload(hip, name, max(steps // 5, 5) if big else steps, max(warmup // 5, 2) if big else warmup)
+            return run_stack_workload(hip, steps, warmup)
+        return run_layer_workload(hip, name, steps, warmup)
 
     head = run(args.workload, args.steps, args.warmup)
     sweep = {}
@@ -325,8 +324,9 @@ def main():
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": head["desc"], "name": head["workload"], "experts_hit_per_step": head["experts_hit_per_step"],
-                   "step_GBps": head.get("step_GBps"), "step_frac_hbm": head.get("step_frac_hbm")},
+        "config": {"workload": head["desc"], "name": head["workload"], "T": head["T"],
+                   **{key: head[key] for key in ("experts_hit_per_step", "step_GBps", "step_frac_hbm",
+                                                 "step_TFLOPs", "step_frac_mfma") if key in head}},
         "roofline": roof, "cpu_baseline": cpu, "sweep": sweep,
     }
     print(json.dumps(line))

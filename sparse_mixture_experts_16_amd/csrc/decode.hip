@@ -5,9 +5,9 @@
 // experts' weight rows from HBM and everything else is latency.  The launches are arranged so
 // that no workgroup ever waits for another one inside a kernel:
 //
-//   dec_logits  one wavefront per router row computes the logits of every token (with the
-//               residual stack, every workgroup also RMS-normalises its tokens itself and
-//               workgroup 0 stores the normalised input for the FFN kernels).
+//   dec_logits  one wavefront per (router row, token) computes a logit (with the residual
+//               stack, every wavefront also RMS-normalises its token itself and the first
+//               workgroup of each token stores the normalised input for the FFN kernels).
 //   dec_w13     every workgroup first redoes the routing from the logits in LDS -- top-k and
 //               gates per token, grouping by expert into a slot table (expert, first sorted
 //               position, pairs, token mask) -- then computes its share of
@@ -26,17 +26,6 @@ namespace moe {
 
 constexpr int DEC_MAX_T = 32;
 constexpr int DEC_MAX_TE = 8192;  // logits held in LDS by every gate/up workgroup
-
-__device__ __forceinline__ uint64_t dec_key(float v, int e) {
-    uint32_t ord;
-    if (v != v) {
-        ord = 0u;
-    } else {
-        uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
-        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
 
 template <typename A> struct rvec;
 template <> struct rvec<float> {
@@ -67,82 +56,99 @@ struct DecLogitsArgs {
     int T, d, E, prenorm;
 };
 
-// One wavefront per (router row, group of 8 tokens): grid = (E/4, T/8).  The row and the
-// tokens' x chunks are loaded together before any arithmetic so their latencies overlap.
+// One wavefront per (router row, token): grid = (E/4, T).  Every load of a pass (up to 8
+// 16-byte chunks of the row and of the token per lane) is issued before any arithmetic, so a
+// wavefront waits for one round trip per pass.  With the residual stack (prenorm) each
+// wavefront first takes its token's RMS from h (fp32) and reads x = bf16(h * inv_rms), the value
+// the FFN kernels read; the workgroups of column 0 store that normalised input.
+template <typename A>
+__device__ __forceinline__ float dot_chunk(uint4 w, uint4 x);
+template <>
+__device__ __forceinline__ float dot_chunk<uint16_t>(uint4 w, uint4 x) {
+    float a = 0.0f;
+    a = fmaf(bf16_lo(w.x), bf16_lo(x.x), a); a = fmaf(bf16_hi(w.x), bf16_hi(x.x), a);
+    a = fmaf(bf16_lo(w.y), bf16_lo(x.y), a); a = fmaf(bf16_hi(w.y), bf16_hi(x.y), a);
+    a = fmaf(bf16_lo(w.z), bf16_lo(x.z), a); a = fmaf(bf16_hi(w.z), bf16_hi(x.z), a);
+    a = fmaf(bf16_lo(w.w), bf16_lo(x.w), a); a = fmaf(bf16_hi(w.w), bf16_hi(x.w), a);
+    return a;
+}
+template <>
+__device__ __forceinline__ float dot_chunk<float>(uint4 w, uint4 x) {
+    float a = 0.0f;
+    a = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), a);
+    a = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), a);
+    a = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), a);
+    a = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), a);
+    return a;
+}
+// x chunk (V elements) from the fp32 residual stream: bf16(h * inv) (or fp32 h * inv), packed
+// like a chunk of the act dtype.
+template <typename A>
+__device__ __forceinline__ uint4 norm_chunk(const float* h, int c, float inv);
+template <>
+__device__ __forceinline__ uint4 norm_chunk<uint16_t>(const float* h, int c, float inv) {
+    const float4 a = reinterpret_cast<const float4*>(h)[2 * c], b = reinterpret_cast<const float4*>(h)[2 * c + 1];
+    return make_uint4(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv),
+                      pack_bf16x2(b.x * inv, b.y * inv), pack_bf16x2(b.z * inv, b.w * inv));
+}
+template <>
+__device__ __forceinline__ uint4 norm_chunk<float>(const float* h, int c, float inv) {
+    const float4 a = reinterpret_cast<const float4*>(h)[c];
+    return make_uint4(__float_as_uint(a.x * inv), __float_as_uint(a.y * inv), __float_as_uint(a.z * inv),
+                      __float_as_uint(a.w * inv));
+}
+
 template <typename A>
 __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
-    constexpr int V = rvec<A>::N;
-    __shared__ float s_inv[8];
+    constexpr int V = rvec<A>::N;  // elements per 16-byte chunk
+    constexpr int NB = 8;          // chunks per lane per pass
     const int lane = lane_id(), wv = wave_id();
-    const int T = p.T, d = p.d;
-    const int t0 = blockIdx.y * 8;
-    const int nt = min(8, T - t0);
+    const int t = blockIdx.y, d = p.d, NC = d / V;
+    const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * d;
+    float inv = 1.0f;
     if (p.prenorm) {
-        for (int q = wv; q < nt; q += 4) {
-            const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d;
-            float ss = 0.0f;
-            for (int i = lane * 4; i < d; i += MOE_WAVE * 4) {
-                const float4 v = *reinterpret_cast<const float4*>(h + i);
-                ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss); ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+        float ss = 0.0f;
+        for (int c0 = 0; c0 < d / 4; c0 += MOE_WAVE * NB) {
+            float4 v[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int c = c0 + lane + MOE_WAVE * b;
+                v[b] = c < d / 4 ? reinterpret_cast<const float4*>(h)[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
-            ss = wave_sum(ss);
-            if (lane == 0) s_inv[q] = 1.0f / sqrtf(ss / (float)d + 1e-6f);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                ss = fmaf(v[b].x, v[b].x, ss); ss = fmaf(v[b].y, v[b].y, ss);
+                ss = fmaf(v[b].z, v[b].z, ss); ss = fmaf(v[b].w, v[b].w, ss);
+            }
         }
-        __syncthreads();
+        ss = wave_sum(ss);
+        inv = 1.0f / sqrtf(ss / (float)d + 1e-6f);
         if (blockIdx.x == 0)
-            for (int q = 0; q < nt; ++q)
-                for (int i = threadIdx.x; i < d; i += blockDim.x) {
-                    const float v = reinterpret_cast<const float*>(p.x)[(int64_t)(t0 + q) * d + i] * s_inv[q];
-                    io<A>::st(reinterpret_cast<A*>(p.xn), (int64_t)(t0 + q) * d + i, v);
-                }
+            for (int c = threadIdx.x; c < NC; c += blockDim.x)
+                reinterpret_cast<uint4*>(reinterpret_cast<A*>(p.xn) + (int64_t)t * d)[c] = norm_chunk<A>(h, c, inv);
     }
     const int e = blockIdx.x * 4 + wv;
     if (e >= p.E) return;
-    const A* w = reinterpret_cast<const A*>(p.wr) + (int64_t)e * d;
-    float acc[8];
+    const uint4* w = reinterpret_cast<const uint4*>(reinterpret_cast<const A*>(p.wr) + (int64_t)e * d);
+    const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const A*>(p.x) + (int64_t)t * d);
+    float acc = 0.0f;
+    for (int c0 = 0; c0 < NC; c0 += MOE_WAVE * NB) {
+        uint4 wc[NB], xc[NB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int i = lane * V; i < d; i += MOE_WAVE * V) {
-        float wvv[V], xv[8][V];
-        rvec<A>::load(w + i, wvv);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (q < nt) {
-                if (p.prenorm) {
-                    const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)(t0 + q) * d + i;
-                    float hv[V];
-                    if (V == 8) {
-                        const float4 a = reinterpret_cast<const float4*>(h)[0], b = reinterpret_cast<const float4*>(h)[1];
-                        hv[0] = a.x; hv[1] = a.y; hv[2] = a.z; hv[3] = a.w;
-                        hv[4 % V] = b.x; hv[5 % V] = b.y; hv[6 % V] = b.z; hv[7 % V] = b.w;
-                    } else {
-                        const float4 a = reinterpret_cast<const float4*>(h)[0];
-                        hv[0] = a.x; hv[1] = a.y; hv[2 % V] = a.z; hv[3 % V] = a.w;
-                    }
-#pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        const float x = hv[v] * s_inv[q];
-                        xv[q][v] = sizeof(A) == 2 ? bf16_to_f32(f32_to_bf16(x)) : x;  // the value the FFN reads
-                    }
-                } else {
-                    rvec<A>::load(reinterpret_cast<const A*>(p.x) + (int64_t)(t0 + q) * d + i, xv[q]);
-                }
+        for (int b = 0; b < NB; ++b) {
+            const int c = c0 + lane + MOE_WAVE * b;
+            if (c < NC) {
+                wc[b] = w[c];
+                xc[b] = p.prenorm ? norm_chunk<A>(h, c, inv) : x[c];
+            } else {
+                wc[b] = xc[b] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (q < nt)
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[q] = fmaf(wvv[v], xv[q][v], acc[q]);
+        for (int b = 0; b < NB; ++b) acc += dot_chunk<A>(wc[b], xc[b]);
     }
-    const float bias = p.b ? p.b[e] : 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        if (q < nt) {
-            const float sum = wave_sum(acc[q]);
-            if (lane == 0) p.logits[(int64_t)(t0 + q) * p.E + e] = sum + bias;
-        }
-    }
+    acc = wave_sum(acc);
+    if (lane == 0) p.logits[(int64_t)t * p.E + e] = acc + (p.b ? p.b[e] : 0.0f);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -174,6 +180,18 @@ struct DecRouteIO {
     int T, E, k, n_shared, no_renorm;
 };
 
+template <int KPL>
+__device__ __forceinline__ int dec_select(const float* l, int E, int k) {
+    uint32_t key[KPL];
+    const int lane = lane_id();
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int e = lane * KPL + j;
+        key[j] = e < E ? sel_ord(l[e]) : 0u;
+    }
+    return wave_topk<KPL>(key, k);
+}
+
 __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
@@ -188,25 +206,13 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     // top-k + gates, a wavefront per token
     for (int t = wv; t < T; t += NW) {
         const float* l = s_logits + t * E;
-        uint64_t key[MOE_MAX_E / MOE_WAVE];
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j) {
-            const int e = lane + MOE_WAVE * j;
-            key[j] = e < E ? dec_key(l[e], e) : 0ull;
-        }
-        int my_sel = 0;
-        for (int r = 0; r < k; ++r) {
-            uint64_t best = 0ull;
-#pragma unroll
-            for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j) best = key[j] > best ? key[j] : best;
-            best = wave_max_u64(best);
-            const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-#pragma unroll
-            for (int j = 0; j < MOE_MAX_E / MOE_WAVE; ++j)
-                if (lane + MOE_WAVE * j == e) key[j] = 0ull;
-            if (lane == r) my_sel = e;
-        }
-        const float m = l[__shfl(my_sel, 0, MOE_WAVE)];
+        int my_sel;
+        if (E <= 64) my_sel = dec_select<1>(l, E, k);
+        else if (E <= 128) my_sel = dec_select<2>(l, E, k);
+        else if (E <= 256) my_sel = dec_select<4>(l, E, k);
+        else if (E <= 512) my_sel = dec_select<8>(l, E, k);
+        else my_sel = dec_select<16>(l, E, k);
+        const float m = l[__builtin_amdgcn_readlane(my_sel, 0)];
         const float term = (lane < k) ? expf(l[my_sel] - m) : 0.0f;
         float den;
         if (io.no_renorm) {
@@ -240,15 +246,7 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
             sc += s_cnt[e];
             sa += s_cnt[e] > 0;
         }
-        int ic = sc, ia = sa;
-#pragma unroll
-        for (int o = 1; o < MOE_WAVE; o <<= 1) {
-            const int u = __shfl_up(ic, o, MOE_WAVE), w = __shfl_up(ia, o, MOE_WAVE);
-            if (lane >= o) {
-                ic += u;
-                ia += w;
-            }
-        }
+        const int ic = wave_incl_scan(sc), ia = wave_incl_scan(sa);
         int pc = ic - sc, pa = ia - sa;
         for (int e = lo; e < hi; ++e) {
             const int c = s_cnt[e];
@@ -513,7 +511,7 @@ bool dec_supported(int T, int E, int k) {
 hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
                              int T, int d, int E, bool prenorm, hipStream_t st) {
     DecLogitsArgs p{x, wr, b, logits, xn, T, d, E, prenorm ? 1 : 0};
-    const dim3 grid((E + 3) / 4, (T + 7) / 8), block(256);
+    const dim3 grid((E + 3) / 4, T), block(256);
     if (act_dtype == 0) hipLaunchKernelGGL((dec_logits<float>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((dec_logits<uint16_t>), grid, block, 0, st, p);
     return hipGetLastError();

@@ -14,16 +14,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        int u = __shfl_up(v, o, MOE_WAVE);
-        if (lane >= o) v += u;
-    }
-    return v;
-}
-
 // Wave 0 of the block: from LDS counts s_cnt[0..E), write counts/offsets, the ascending list of
 // experts with tokens, the per-expert tile offsets (ceil(count/bm) tiles each) and meta
 // (meta[0] = active experts, meta[1] = tiles); leaves s_cur[e] = offsets[e].

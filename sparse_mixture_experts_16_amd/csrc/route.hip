@@ -67,22 +67,10 @@ __global__ void __launch_bounds__(256) route_logits_gemv(const A* __restrict__ x
 }
 
 // ------------------------------------------------------------------------------------------------
-// Top-k + gates: one wavefront per token.  Each lane holds EPL logits (expert lane + 64 j) as
-// 64-bit keys that order the logits totally: high word = order-preserving image of the fp32
-// value (NaN lowest, -0 mapped to +0), low word = ~expert so that equal values prefer the
-// lower expert.  k rounds of a wave-wide max pick the experts in selection order.
+// Top-k + gates: one wavefront per token.  Lane l holds the EPL logits of experts l*EPL ..
+// l*EPL+EPL-1 as order-preserving 32-bit keys (NaN lowest, -0 equal to +0); k rounds of a
+// wave-wide max, ties to the lowest expert, pick the experts in selection order.
 // ------------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t select_key(float v, int e) {
-    uint32_t ord;
-    if (v != v) {
-        ord = 0u;
-    } else {
-        uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
-        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    }
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
 template <int EPL>
 __global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logits, int T, int E, int k,
                                                   uint32_t no_renorm, int32_t* __restrict__ idx_out,
@@ -91,33 +79,22 @@ __global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logi
     if (t >= T) return;
     const int lane = lane_id();
     const float* l = logits + (int64_t)t * E;
-    uint64_t key[EPL];
+    uint32_t key[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-        int e = lane + MOE_WAVE * j;
-        key[j] = (e < E) ? select_key(l[e], e) : 0ull;
+        const int e = lane * EPL + j;
+        key[j] = (e < E) ? sel_ord(l[e]) : 0u;
     }
-    int my_sel = 0;
-    for (int r = 0; r < k; ++r) {
-        uint64_t best = 0ull;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-#pragma unroll
-        for (int j = 0; j < EPL; ++j)
-            if (lane + MOE_WAVE * j == e) key[j] = 0ull;
-        if (lane == r) my_sel = e;
-    }
+    const int my_sel = wave_topk<EPL>(key, k);
     // Gates: exp(l - m) with m the first (largest) selected logit.
-    const float m = l[__shfl(my_sel, 0, MOE_WAVE)];
+    const float m = l[__builtin_amdgcn_readlane(my_sel, 0)];
     const float term = (lane < k) ? expf(l[my_sel] - m) : 0.0f;
     float den;
     if (no_renorm) {
         float part = 0.0f;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
-            int e = lane + MOE_WAVE * j;
+            const int e = lane * EPL + j;
             if (e < E) part += expf(l[e] - m);
         }
         den = wave_sum(part);
