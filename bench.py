@@ -50,6 +50,53 @@ WORKLOADS = {
 HEADLINE = "c1_decode_T1"
 POOL = 256
 
+# HBM traffic of the roofline kernel, from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, averaged over the dispatches of the bench command) scaled by
+# what the same counters read for a plain device-to-device copy of 256 MiB.  Each entry names
+# the digest of the kernel sources it was taken on; a different digest reports null.
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "common.h", "wchunk.h"],
+    "gemm": ["gemm.hip", "common.h", "wchunk.h"],
+}
+COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
+TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
+    "c1_decode_T1": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=27742.3, write_kib=27.3),
+    "c3_decode_T1": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=26254.8, write_kib=50.9),
+    "c4_stack": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=26254.1, write_kib=50.6),
+    "c2_prefill": dict(src="gemm:b209a7bae128a13c", fetch_kib=804629.1, write_kib=111068.6),
+    "c3_prefill": dict(src="gemm:b209a7bae128a13c", fetch_kib=1435668.2, write_kib=393546.4),
+}
+
+
+def source_digest(kind: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return f"{kind}:{h.hexdigest()[:16]}"
+
+
+def traffic_bytes(workload: str):
+    t = TRAFFIC.get(workload)
+    if not t or not COPY_CAL or t["src"] != source_digest(t["src"].split(":")[0]):
+        return None
+    return t["fetch_kib"] * 1024 * COPY_CAL["fetch_factor"] + t["write_kib"] * 1024 * COPY_CAL["write_factor"]
+
+
+def copy_calibration():
+    """A plain 256 MiB device-to-device copy, 5 times (the counters' reference)."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+
 
 def expert_bytes(s, f=None):
     """Bytes of one expert's weights (w13 + w2), split (up, down)."""
@@ -284,12 +331,17 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep-list", default="")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 256 MiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(the layer's multi-GPU sharding is a design note, not built)"}))
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import sparse_mixture_experts_16_amd  # noqa: F401  (fails loudly without the HIP library)
     hip = Hip()
     torch.cuda.init()
@@ -313,11 +365,11 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline()
     if head["bound"] == "hbm":
         roof = dict(bound="hbm", achieved=head["ffn_up_GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=head["ffn_up_frac"], traffic=None, kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
+                    frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
                     alg_bytes_per_launch=head["ffn_up_alg_bytes"], avg_launch_us=head["ffn_up_us"])
     else:
         roof = dict(bound="mfma", achieved=head["ffn_up_TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=head["ffn_up_frac"], traffic=None, kernel="FFN gate/up + SwiGLU (prefill grouped MFMA GEMM)",
+                    frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (prefill grouped MFMA GEMM)",
                     alg_flops_per_launch=head["ffn_up_alg_flops"], avg_launch_us=head["ffn_up_us"])
     line = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA util %",

@@ -164,8 +164,10 @@ int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const 
 int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out,
                       void* stream);
 
-/* Timing aid for benchmarks: while set, every launch of the given kernel class is
-   bracketed by hipEventRecord(ev_start) / hipEventRecord(ev_stop) on the call's stream.
+/* Timing aid for benchmarks: while set, every launch of the given kernel class carries
+   ev_start / ev_stop on its own dispatch (hipExtLaunchKernel), so the events hold that
+   kernel's start and end timestamps; with several such launches in one call (the stack),
+   the last one's remain.
    kernel: MOE_KERNEL_FFN_UP (gate/up projection + SwiGLU, the largest byte/flop share),
    MOE_KERNEL_FFN_DOWN (down projection), or -1 to switch the hook off (events ignored).
    ev_start/ev_stop are hipEvent_t handles owned by the caller.  The setting is

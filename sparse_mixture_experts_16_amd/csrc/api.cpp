@@ -128,15 +128,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
         if (_e != hipSuccess) return MOE_ERR_HIP;      \
     } while (0)
 
-// Optional timing hook (moe_profile_kernel): events recorded around one kernel class.
+// Optional timing hook (moe_profile_kernel): the events ride on the profiled class's launch.
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 int g_prof_kernel = -1;
-
-inline hipError_t prof_mark(int kernel, bool start, hipStream_t st) {
-    if (kernel != g_prof_kernel) return hipSuccess;
-    hipEvent_t ev = start ? g_prof_start : g_prof_stop;
-    return ev ? hipEventRecord(ev, st) : hipSuccess;
-}
+static_assert(MOE_KERNEL_FFN_UP == PROF_FFN_UP && MOE_KERNEL_FFN_DOWN == PROF_FFN_DOWN, "kernel classes");
 
 // Routed + shared FFNs given ws-resident permute results; writes either the fused combine into
 // `out` (decode, T <= 64) or y_sorted / y_shared.
@@ -147,28 +142,20 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
     const int fs = s->n_shared ? s->shared_d_ff : 0;
     if (use_gemm(s)) {
         uint16_t* a = at<uint16_t>(ws, L.a);
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
         MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
                                  w->s13, w->s13_scale, a, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
                                  s->n_shared, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
         MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale,
                                 (uint16_t*)y_sorted, (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
                                 s->n_experts, s->n_shared, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
         return MOE_OK;
     }
     float* a = at<float>(ws, L.a);
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
     MOE_TRY(launch_gemv_w13(wt, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13, w->s13_scale, a,
                             s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, st));
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
     MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
                                   w->s2, w->s2_scale, y_sorted, y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
                                   s->n_experts, s->n_shared, st));
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
     return MOE_OK;
 }
 
@@ -180,16 +167,13 @@ int run_decode(const moe_shape* s, const void* x, const void* w_router, const fl
     void* xn = at<void>(ws, L.xn);
     MOE_TRY(launch_dec_logits(s->act_dtype, x, w_router, b, at<float>(ws, L.logits), xn, s->T, s->d_model,
                               s->n_experts, prenorm, st));
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
     hipError_t e = launch_dec_ffn(
         s->weight_dtype, out_dtype == MOE_BF16, prenorm ? xn : x, at<float>(ws, L.logits), at<int32_t>(ws, L.topk_idx),
         at<float>(ws, L.topk_w), idx_out, at<int32_t>(ws, L.meta), at<int4>(ws, L.slots), at<float>(ws, L.pos_gate),
         (s->flags & MOE_F_NO_RENORM) != 0, w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2,
         w->s2_scale, at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
-        s->n_experts, s->n_shared, accumulate, st, g_prof_kernel == MOE_KERNEL_FFN_UP ? g_prof_stop : nullptr,
-        g_prof_kernel == MOE_KERNEL_FFN_DOWN ? g_prof_start : nullptr);
+        s->n_experts, s->n_shared, accumulate, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
     return MOE_OK;
 }
 
@@ -224,15 +208,11 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
     if (!gemm && T <= 64) {
         float* a = at<float>(ws, L.a);
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, true, st));
         MOE_TRY(launch_gemv_w13(s->weight_dtype, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13,
                                 w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_UP, false, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, true, st));
         MOE_TRY(launch_gemv_w2_combine(s->weight_dtype, out_dtype == MOE_BF16, a, perm, offsets, act_list, meta, g,
                                        w->w2, w->w2_scale, w->s2, w->s2_scale, out, T, d, s->d_ff, fs, k,
                                        s->n_shared, accumulate, st));
-        MOE_TRY(prof_mark(MOE_KERNEL_FFN_DOWN, false, st));
         return MOE_OK;
     }
     void* y = at<void>(ws, L.y);
@@ -245,6 +225,15 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
 }
 
 }  // namespace
+
+namespace moe {
+void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop) {
+    if (cls == g_prof_kernel) {
+        *start = g_prof_start;
+        *stop = g_prof_stop;
+    }
+}
+}  // namespace moe
 
 extern "C" {
 

@@ -529,8 +529,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
-                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st,
-                          hipEvent_t ev_up_done, hipEvent_t ev_down_start) {
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st) {
     const int fmax = (n_shared && fs > f) ? fs : f;
     DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0};
     DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
@@ -540,7 +539,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
 #define MOE_DW13(WTV, RV, UV)                                                                                    \
     do {                                                                                                         \
         const int64_t items = max_slots * ((f + RV - 1) / RV) + (n_shared ? (fs + RV - 1) / RV : 0);             \
-        hipLaunchKernelGGL((dec_w13<WTV, RV, UV>), dim3(dec_grid(items)), dim3(512), lds, st, p);               \
+        MOE_LAUNCH(PROF_FFN_UP, (dec_w13<WTV, RV, UV>), dim3(dec_grid(items)), dim3(512), lds, st, p);         \
     } while (0)
     // about 8 16-byte loads per lane in flight per item (HBM streams best at 4-8 per lane)
     if (wt == 0) MOE_DW13(0, 2, 1);
@@ -549,13 +548,11 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
 #undef MOE_DW13
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev_up_done && (e = hipEventRecord(ev_up_done, st)) != hipSuccess) return e;
-    if (ev_down_start && (e = hipEventRecord(ev_down_start, st)) != hipSuccess) return e;
 #define MOE_DW2(WTV, RV, UV)                                                                                     \
     do {                                                                                                         \
         const dim3 grid((d + RV - 1) / RV);                                                                      \
-        if (out_bf16) hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, true>), grid, dim3(512), 0, st, p);                 \
-        else hipLaunchKernelGGL((dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                         \
+        if (out_bf16) MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c<WTV, RV, UV, true>), grid, dim3(512), 0, st, p);         \
+        else MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                 \
     } while (0)
     if (wt == 0) MOE_DW2(0, 4, 1);
     else if (wt == 1) MOE_DW2(1, 4, 2);

@@ -373,15 +373,15 @@ hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int
     if (wt == 0) {
         constexpr int R = 1;
         int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((gemv_w13<0, R, 4, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
+        MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<0, R, 4, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
     } else if (wt == 1) {
         constexpr int R = 1;
         int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((gemv_w13<1, R, 4, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
+        MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<1, R, 4, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
     } else {
         constexpr int R = 2;
         int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
-        hipLaunchKernelGGL((gemv_w13<2, R, 2, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
+        MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<2, R, 2, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }
@@ -396,9 +396,9 @@ hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const i
     do {                                                                                                  \
         int64_t items = (d + RV - 1) / RV;                                                                \
         if (out_bf16)                                                                                     \
-            hipLaunchKernelGGL((gemv_w2_combine<WTV, RV, UV, true>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
+            MOE_LAUNCH(PROF_FFN_DOWN, (gemv_w2_combine<WTV, RV, UV, true>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
         else                                                                                              \
-            hipLaunchKernelGGL((gemv_w2_combine<WTV, RV, UV, false>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
+            MOE_LAUNCH(PROF_FFN_DOWN, (gemv_w2_combine<WTV, RV, UV, false>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
     } while (0)
     if (wt == 0) MOE_W2C(0, 1, 2);
     else if (wt == 1) MOE_W2C(1, 2, 2);
@@ -418,9 +418,9 @@ hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int3
     do {                                                                                                  \
         int64_t items = max_act * ((d + RV - 1) / RV);                                                    \
         if (y_bf16)                                                                                       \
-            hipLaunchKernelGGL((gemv_w2_sorted<WTV, RV, UV, true>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
+            MOE_LAUNCH(PROF_FFN_DOWN, (gemv_w2_sorted<WTV, RV, UV, true>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
         else                                                                                              \
-            hipLaunchKernelGGL((gemv_w2_sorted<WTV, RV, UV, false>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
+            MOE_LAUNCH(PROF_FFN_DOWN, (gemv_w2_sorted<WTV, RV, UV, false>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p); \
     } while (0)
     if (wt == 0) MOE_W2S(0, 1, 2);
     else if (wt == 1) MOE_W2S(1, 2, 2);

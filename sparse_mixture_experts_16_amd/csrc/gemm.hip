@@ -406,8 +406,8 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
     constexpr int BN = 256;  // 128 gate/up column pairs per tile
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W13, 2, BN, false>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -420,8 +420,8 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
     constexpr int BN = 128;
     const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-    if (wt == 1) hipLaunchKernelGGL((ggemm<MODE_W2, 1, BN, true>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((ggemm<MODE_W2, 2, BN, true>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true>), dim3(grid), dim3(256), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Host-side launchers of the gfx950 kernels (internal to libmoe.so).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #define MOE_MAX_E 1024
@@ -10,6 +11,17 @@
 #define GEMM_BM 128  // token rows per grouped-GEMM tile (tile list granularity)
 
 namespace moe {
+
+// Timing hook: the launch of the kernel class being profiled carries the caller's start/stop
+// events on its own dispatch packet (hipExtLaunchKernel), so they time that kernel alone.
+enum { PROF_FFN_UP = 0, PROF_FFN_DOWN = 1 };
+void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop);
+#define MOE_LAUNCH(CLS, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                  \
+    do {                                                                                          \
+        hipEvent_t moe_e0_ = nullptr, moe_e1_ = nullptr;                                          \
+        ::moe::prof_events(CLS, &moe_e0_, &moe_e1_);                                              \
+        hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, moe_e0_, moe_e1_, 0, __VA_ARGS__); \
+    } while (0)
 
 hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
                                int T, int d, int E, hipStream_t st);
@@ -56,8 +68,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
-                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st,
-                          hipEvent_t ev_up_done, hipEvent_t ev_down_start);
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st);
 
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
                           const void* ysh, void* out, int T, int d, int k, bool accumulate, hipStream_t st);
