@@ -106,6 +106,53 @@ __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
     const int t = blockIdx.y, d = p.d, NC = d / V;
     const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * d;
     float inv = 1.0f;
+    const int e = blockIdx.x * 4 + wv;
+    if (p.prenorm && NC <= MOE_WAVE * NB) {
+        // The wavefront's lanes hold the whole row of h between them: its chunks give the RMS
+        // (one wave-wide sum) and then x, from a single round trip together with W_r's row.
+        const uint4* w = reinterpret_cast<const uint4*>(reinterpret_cast<const A*>(p.wr) + (int64_t)min(e, p.E - 1) * d);
+        constexpr int HF = V / 4;  // float4 of h per chunk
+        float4 hv[NB][HF];
+        uint4 wc[NB];
+        float ss = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int c = lane + MOE_WAVE * b;
+#pragma unroll
+            for (int q = 0; q < HF; ++q)
+                hv[b][q] = c < NC ? reinterpret_cast<const float4*>(h)[HF * c + q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            wc[b] = c < NC ? w[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < HF; ++q) {
+                ss = fmaf(hv[b][q].x, hv[b][q].x, ss); ss = fmaf(hv[b][q].y, hv[b][q].y, ss);
+                ss = fmaf(hv[b][q].z, hv[b][q].z, ss); ss = fmaf(hv[b][q].w, hv[b][q].w, ss);
+            }
+        inv = 1.0f / sqrtf(wave_sum(ss) / (float)d + 1e-6f);
+        float acc = 0.0f;
+        uint4* xo = reinterpret_cast<uint4*>(reinterpret_cast<A*>(p.xn) + (int64_t)t * d);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int c = lane + MOE_WAVE * b;
+            if (c < NC) {
+                uint4 xc;
+                if constexpr (V == 8)
+                    xc = make_uint4(pack_bf16x2(hv[b][0].x * inv, hv[b][0].y * inv), pack_bf16x2(hv[b][0].z * inv, hv[b][0].w * inv),
+                                    pack_bf16x2(hv[b][HF - 1].x * inv, hv[b][HF - 1].y * inv),
+                                    pack_bf16x2(hv[b][HF - 1].z * inv, hv[b][HF - 1].w * inv));
+                else
+                    xc = make_uint4(__float_as_uint(hv[b][0].x * inv), __float_as_uint(hv[b][0].y * inv),
+                                    __float_as_uint(hv[b][0].z * inv), __float_as_uint(hv[b][0].w * inv));
+                acc += dot_chunk<A>(wc[b], xc);
+                if (blockIdx.x == 0 && wv == 0) xo[c] = xc;
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && e < p.E) p.logits[(int64_t)t * p.E + e] = acc + (p.b ? p.b[e] : 0.0f);
+        return;
+    }
     if (p.prenorm) {
         float ss = 0.0f;
         for (int c0 = 0; c0 < d / 4; c0 += MOE_WAVE * NB) {
@@ -127,7 +174,6 @@ __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
             for (int c = threadIdx.x; c < NC; c += blockDim.x)
                 reinterpret_cast<uint4*>(reinterpret_cast<A*>(p.xn) + (int64_t)t * d)[c] = norm_chunk<A>(h, c, inv);
     }
-    const int e = blockIdx.x * 4 + wv;
     if (e >= p.E) return;
     const uint4* w = reinterpret_cast<const uint4*>(reinterpret_cast<const A*>(p.wr) + (int64_t)e * d);
     const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const A*>(p.x) + (int64_t)t * d);
@@ -293,6 +339,7 @@ struct DecFfnArgs {
     float* a;               // [P + T, fmax] fp32
     void* out;              // [T, d] (f32 or bf16)
     int T, d, f, fs, fmax, k, accumulate;
+    int slot_bound;          // routed slots can number at most min(T*k, E), plus the shared one
 };
 
 template <int WT> struct DecAct { using T = uint16_t; };
@@ -420,11 +467,11 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
     __shared__ int4 s_slot[MOE_MAX_E + 1];
     __shared__ int s_n;
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    // the slot count and the slot table (up to its bound) in one round trip
     if (tid == 0) s_n = p.rt.meta[0];
+    for (int s = tid; s < p.slot_bound; s += blockDim.x) s_slot[s] = p.rt.slots[s];
     __syncthreads();
     const int n_slots = s_n;
-    for (int s = tid; s < n_slots; s += blockDim.x) s_slot[s] = p.rt.slots[s];
-    __syncthreads();
     const int T = p.T;
     const int i0 = blockIdx.x * R;
     float o[R];
@@ -532,9 +579,10 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st) {
     const int fmax = (n_shared && fs > f) ? fs : f;
     DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0};
-    DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
-                 (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0};
     const int64_t max_slots = (int64_t)(T * k < E ? T * k : E);
+    DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
+                 (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0,
+                 (int)max_slots + n_shared};
     const size_t lds = dec_route_lds_bytes(T, E, k);
 #define MOE_DW13(WTV, RV, UV)                                                                                    \
     do {                                                                                                         \
@@ -556,7 +604,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     } while (0)
     if (wt == 0) MOE_DW2(0, 4, 1);
     else if (wt == 1) MOE_DW2(1, 4, 2);
-    else MOE_DW2(2, 8, 1);
+    else MOE_DW2(2, 16, 1);
 #undef MOE_DW2
     return hipGetLastError();
 }
