@@ -120,11 +120,15 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     // leaves LDS-DMA completion to the explicit vmcnt waits below instead of draining the
     // whole ring before every fragment read.
     constexpr int SZ_A = NS * NPL * BM * ROWE * 2, SZ_B = NS * BN * BROW * 2, SZ_S = (WT == 2 ? 2 * BN * 4 : 0);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ_A + SZ_B + SZ_S + (MOE_MAX_E + 2) * 4];
+    // output staging after the K loop (reuses the ring): bf16 rows of NCOL columns, pitch OP
+    constexpr int NCOL = (MODE == MODE_W13) ? BN / 2 : BN, OP = NCOL + 8;
+    constexpr int SZ_O = (MODE == MODE_ROUTER) ? 0 : ((MODE == MODE_W13) ? 2 : 1) * BM * OP * 2;
+    constexpr int SZ_RING = (SZ_A + SZ_B + SZ_S) > SZ_O ? (SZ_A + SZ_B + SZ_S) : SZ_O;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ_RING + (MOE_MAX_E + 2) * 4];
     auto sA = reinterpret_cast<uint16_t(*)[NPL][BM * ROWE]>(smem);
     auto sB = reinterpret_cast<uint16_t(*)[BN * BROW]>(smem + SZ_A);
     auto sS = reinterpret_cast<uint32_t(*)[BN]>(smem + SZ_A + SZ_B);
-    int* s_pref = reinterpret_cast<int*>(smem + SZ_A + SZ_B + SZ_S);
+    int* s_pref = reinterpret_cast<int*>(smem + SZ_RING);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
     const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
@@ -328,41 +332,64 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     }
 
     // ---- epilogue: accumulator j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32
+    if constexpr (MODE == MODE_ROUTER) {
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+        for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-            if (r >= mrows) continue;
-            const int row = m0 + r;
-            if (MODE == MODE_W13) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) +
-                              (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f);
-#pragma unroll
-                for (int ns = 0; ns < NT32 / 2; ++ns) {
-                    const int jc = nt * (BN / 2) + wn * (BN / 4) + ns * 32 + (lane & 31);
-                    if (jc >= fg) continue;
-                    const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
-                    const float av = gt / (1.0f + expf(-gt)) * up;
-                    const uint16_t hi = f32_to_bf16(av);
-                    o[jc] = hi;
-                    o[p.lo_off + jc] = f32_to_bf16(av - bf16_to_f32(hi));
-                }
-            } else if (MODE == MODE_W2) {
-                uint16_t* o = shared ? p.out_sh + (int64_t)row * p.d
-                                     : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d;
-#pragma unroll
-                for (int ns = 0; ns < NT32; ++ns) {
-                    const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
-                    if (n < N) o[n] = f32_to_bf16(acc[ms][ns][j]);
-                }
-            } else {
-                float* o = reinterpret_cast<float*>(p.out) + (int64_t)row * p.E;
+            for (int j = 0; j < 16; ++j) {
+                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+                if (r >= mrows) continue;
+                float* o = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + r) * p.E;
 #pragma unroll
                 for (int ns = 0; ns < NT32; ++ns) {
                     const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
                     if (n < N) o[n] = acc[ms][ns][j] + (p.bias ? p.bias[n] : 0.0f);
                 }
+            }
+    } else {
+        // Stage the tile's bf16 outputs in LDS (the ring is free once every wavefront is past
+        // its last fragment read), then store whole 16-byte row chunks.
+        __syncthreads();
+        uint16_t* o_hi = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* o_lo = o_hi + BM * OP;
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+                if constexpr (MODE == MODE_W13) {
+#pragma unroll
+                    for (int ns = 0; ns < NT32 / 2; ++ns) {
+                        const int c = wn * (BN / 4) + ns * 32 + (lane & 31);
+                        const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
+                        const float av = gt / (1.0f + expf(-gt)) * up;
+                        const uint16_t hi = f32_to_bf16(av);
+                        o_hi[r * OP + c] = hi;
+                        o_lo[r * OP + c] = f32_to_bf16(av - bf16_to_f32(hi));
+                    }
+                } else {
+#pragma unroll
+                    for (int ns = 0; ns < NT32; ++ns) o_hi[r * OP + wn * WN + ns * 32 + (lane & 31)] = f32_to_bf16(acc[ms][ns][j]);
+                }
+            }
+        __syncthreads();
+        constexpr int CH = NCOL / 8;  // 16-byte chunks per staged row
+        const int col0 = nt * NCOL;
+        const int lim = (MODE == MODE_W13) ? fg : N;  // columns of this group's output rows
+        for (int i = tid; i < BM * CH; i += 256) {
+            const int r = i / CH, ch = i % CH;
+            if (r >= mrows || col0 + ch * 8 >= lim) continue;
+            const int row = m0 + r;
+            const uint4 v = *reinterpret_cast<const uint4*>(&o_hi[r * OP + ch * 8]);
+            if constexpr (MODE == MODE_W13) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) +
+                              (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f) + col0 + ch * 8;
+                *reinterpret_cast<uint4*>(o) = v;
+                *reinterpret_cast<uint4*>(o + p.lo_off) = *reinterpret_cast<const uint4*>(&o_lo[r * OP + ch * 8]);
+            } else {
+                uint16_t* o = (shared ? p.out_sh + (int64_t)row * p.d
+                                      : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+                *reinterpret_cast<uint4*>(o) = v;
             }
         }
     }
