@@ -149,6 +149,18 @@ int moe_layer_forward(const moe_shape* shape, const void* x, const void* w_route
                       const moe_weights* weights, void* out, int32_t* topk_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Partial layer (the exact merge of partial expert sums; FreeToken/dothoosh, "Architecture and
+   the sparsity puzzle", mechanism 1: the GPU's and the CPU's partial results add up to the
+   whole): moe_layer_forward with the combine restricted to the experts whose byte in
+   expert_mask is nonzero.  expert_mask: DEVICE, E + 1 bytes (routed experts 0..E-1, then the
+   shared expert), 16-byte aligned.  Routing (selection and gates) is over all E experts as in
+   the full layer; the FFNs of masked-out experts are not computed.  With MOE_F_ACCUMULATE,
+   calls over disjoint masks whose union is every expert sum to the full layer (up to fp32
+   rounding of the additions).  Errors as moe_layer_forward; a NULL mask is INVALID_ARG. */
+int moe_layer_forward_masked(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                             const moe_weights* weights, const uint8_t* expert_mask, void* out,
+                             int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Residual stack of n_layers MoE layers (step a9) on the fp32 residual stream
    h [T, d_model]: for each layer l, x = act(h / sqrt(mean(h^2) + 1e-6)) rounded to
    the act dtype, then h += layer_l(x) in fp32.  w_router, b_router and weights are

@@ -27,7 +27,8 @@ MAX_EXPERTS, MAX_TOPK = 1024, 64
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_layer_forward", "moe_stack_forward", "moe_mxfp4_dequant", "moe_profile_kernel"]
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_masked", "moe_stack_forward", "moe_mxfp4_dequant",
+           "moe_profile_kernel"]
 KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
 
 
@@ -56,6 +57,7 @@ _lib.moe_permute.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_grouped_ffn.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_combine.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
 _lib.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
@@ -168,6 +170,15 @@ def layer_forward_raw(shape: Shape, x, w_router, b_router, weights: Weights, out
     _check(_lib.moe_layer_forward(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
                                   ctypes.byref(weights), _ptr(out), _ptr(topk_idx_out), _ptr(ws), ws.numel(),
                                   _stream(stream)), "moe_layer_forward")
+
+
+def layer_forward_masked_raw(shape: Shape, x, w_router, b_router, weights: Weights, expert_mask, out,
+                             topk_idx_out=None, ws=None, stream=None):
+    """moe_layer_forward_masked: expert_mask is a device uint8 tensor of E + 1 bytes."""
+    ws = workspace(shape) if ws is None else ws
+    _check(_lib.moe_layer_forward_masked(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
+                                         ctypes.byref(weights), _ptr(expert_mask), _ptr(out), _ptr(topk_idx_out),
+                                         _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward_masked")
 
 
 def stack_forward(shape: Shape, h, w_routers, b_routers, weights_list, ws=None, stream=None):

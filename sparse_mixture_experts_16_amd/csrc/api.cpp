@@ -137,17 +137,17 @@ static_assert(MOE_KERNEL_FFN_UP == PROF_FFN_UP && MOE_KERNEL_FFN_DOWN == PROF_FF
 // `out` (decode, T <= 64) or y_sorted / y_shared.
 int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* act_list,
             const int32_t* tile_off, const int32_t* meta, const moe_weights* w, void* ws, const Layout& L,
-            void* y_sorted, void* y_shared, hipStream_t st) {
+            void* y_sorted, void* y_shared, const uint8_t* mask, hipStream_t st) {
     const int wt = s->weight_dtype;
     const int fs = s->n_shared ? s->shared_d_ff : 0;
     if (use_gemm(s)) {
         uint16_t* a = at<uint16_t>(ws, L.a);
         MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
                                  w->s13, w->s13_scale, a, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
-                                 s->n_shared, st));
+                                 s->n_shared, mask, st));
         MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale,
                                 (uint16_t*)y_sorted, (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
-                                s->n_experts, s->n_shared, st));
+                                s->n_experts, s->n_shared, mask, st));
         return MOE_OK;
     }
     float* a = at<float>(ws, L.a);
@@ -163,7 +163,7 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
 // prenorm: x is the fp32 residual stream, normalised by the logits kernel into ws.xn.
 int run_decode(const moe_shape* s, const void* x, const void* w_router, const float* b, const moe_weights* w,
                void* out, int out_dtype, bool accumulate, int32_t* idx_out, bool prenorm, void* ws, const Layout& L,
-               hipStream_t st) {
+               const uint8_t* mask, hipStream_t st) {
     void* xn = at<void>(ws, L.xn);
     MOE_TRY(launch_dec_logits(s->act_dtype, x, w_router, b, at<float>(ws, L.logits), xn, s->T, s->d_model,
                               s->n_experts, prenorm, st));
@@ -172,7 +172,7 @@ int run_decode(const moe_shape* s, const void* x, const void* w_router, const fl
         at<float>(ws, L.topk_w), idx_out, at<int32_t>(ws, L.meta), at<int4>(ws, L.slots), at<float>(ws, L.pos_gate),
         (s->flags & MOE_F_NO_RENORM) != 0, w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2,
         w->s2_scale, at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
-        s->n_experts, s->n_shared, accumulate, st);
+        s->n_experts, s->n_shared, accumulate, mask, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -184,7 +184,7 @@ bool use_decode(const moe_shape* s) {
 // The whole layer on x; out has dtype out_dtype (act dtype for the layer API, f32 for the stack).
 int run_layer(const moe_shape* s, const void* x, const void* w_router, const float* b, const moe_weights* w,
               void* out, int out_dtype, bool accumulate, int32_t* idx_out, void* ws, const Layout& L,
-              hipStream_t st) {
+              const uint8_t* mask, hipStream_t st) {
     const int T = s->T, E = s->n_experts, k = s->top_k, d = s->d_model, P = T * k;
     const int fs = s->n_shared ? s->shared_d_ff : 0;
     float* logits = at<float>(ws, L.logits);
@@ -199,14 +199,14 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     int32_t* meta = at<int32_t>(ws, L.meta);
     int32_t* blk = at<int32_t>(ws, L.blk);
     const bool gemm = use_gemm(s);
-    if (use_decode(s)) return run_decode(s, x, w_router, b, w, out, out_dtype, accumulate, idx_out, false, ws, L, st);
+    if (use_decode(s)) return run_decode(s, x, w_router, b, w, out, out_dtype, accumulate, idx_out, false, ws, L, mask, st);
     if (gemm && T > DECODE_MAX_T)
         MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, st));
     else
         MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b, logits, T, d, E, st));
     MOE_TRY(launch_route_topk(logits, T, E, k, (s->flags & MOE_F_NO_RENORM) != 0, idx, g, idx_out, st));
     MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
-    if (!gemm && T <= 64) {
+    if (!gemm && T <= 64 && !mask) {
         float* a = at<float>(ws, L.a);
         MOE_TRY(launch_gemv_w13(s->weight_dtype, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13,
                                 w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, st));
@@ -217,10 +217,10 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     }
     void* y = at<void>(ws, L.y);
     void* ysh = s->n_shared ? at<void>(ws, L.ysh) : nullptr;
-    int rc = run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y, ysh, st);
+    int rc = run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y, ysh, mask, st);
     if (rc != MOE_OK) return rc;
     MOE_TRY(launch_combine(s->act_dtype == MOE_BF16 ? 1 : 0, out_dtype == MOE_BF16 ? 1 : 0, y, inv, g, ysh, out, T,
-                           d, k, accumulate, st));
+                           d, k, accumulate, idx, mask, E, st));
     return MOE_OK;
 }
 
@@ -315,7 +315,7 @@ int moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* perm, cons
     int32_t* tile_off = at<int32_t>(ws, L.tile_off);
     int32_t* meta = at<int32_t>(ws, L.meta);
     MOE_TRY(launch_active_from_offsets(offsets, s->n_experts, GEMM_BM, act_list, tile_off, meta, st));
-    return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, st);
+    return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, nullptr, st);
 }
 
 int moe_combine(const moe_shape* s, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
@@ -327,15 +327,16 @@ int moe_combine(const moe_shape* s, const void* y_sorted, const int32_t* inv_per
     if (y_shared && !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
     const int dt = s->act_dtype == MOE_BF16 ? 1 : 0;
     MOE_TRY(launch_combine(dt, dt, y_sorted, inv_perm, topk_w, y_shared, out, s->T, s->d_model, s->top_k,
-                           (s->flags & MOE_F_ACCUMULATE) != 0, (hipStream_t)stream));
+                           (s->flags & MOE_F_ACCUMULATE) != 0, nullptr, nullptr, s->n_experts, (hipStream_t)stream));
     return MOE_OK;
 }
 
-int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
-                      const moe_weights* w, void* out, int32_t* topk_idx_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+static int layer_entry(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                       const moe_weights* w, const uint8_t* expert_mask, bool masked, void* out,
+                       int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
+    if (masked && !ptr_ok(expert_mask)) return MOE_ERR_INVALID_ARG;
     if (s->T == 0) return MOE_OK;
     if ((rc = check_weights(s, w)) != MOE_OK) return rc;
     if (!ptr_ok(x) || !ptr_ok(w_router) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
@@ -343,7 +344,19 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, c
     const Layout L = layout(s);
     if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     return run_layer(s, x, w_router, b_router, w, out, s->act_dtype, (s->flags & MOE_F_ACCUMULATE) != 0,
-                     topk_idx_out, ws, L, (hipStream_t)stream);
+                     topk_idx_out, ws, L, masked ? expert_mask : nullptr, (hipStream_t)stream);
+}
+
+int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                      const moe_weights* w, void* out, int32_t* topk_idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+    return layer_entry(s, x, w_router, b_router, w, nullptr, false, out, topk_idx_out, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_masked(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                             const moe_weights* w, const uint8_t* expert_mask, void* out, int32_t* topk_idx_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+    return layer_entry(s, x, w_router, b_router, w, expert_mask, true, out, topk_idx_out, ws, ws_bytes, stream);
 }
 
 int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void* const* w_router,
@@ -366,7 +379,7 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
         // decode: the logits kernel normalises h itself and leaves x for the FFN kernels
         for (int l = 0; l < n_layers; ++l) {
             rc = run_decode(s, h, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr,
-                            true, ws, L, st);
+                            true, ws, L, nullptr, st);
             if (rc != MOE_OK) return rc;
         }
         return MOE_OK;
@@ -374,7 +387,7 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
     for (int l = 0; l < n_layers; ++l) {
         MOE_TRY(launch_rmsnorm(s->act_dtype == MOE_BF16 ? 1 : 0, h, xn, s->T, s->d_model, 1e-6f, st));
         rc = run_layer(s, xn, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr, ws,
-                       L, st);
+                       L, nullptr, st);
         if (rc != MOE_OK) return rc;
     }
     return MOE_OK;

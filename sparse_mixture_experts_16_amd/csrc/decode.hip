@@ -212,7 +212,7 @@ struct DecRoute {
 
 // Dynamic LDS carve-up of the routing prologue: slots, logits, gates, experts, counts, masks.
 __host__ __device__ inline size_t dec_route_lds_bytes(int T, int E, int k) {
-    return (size_t)(E + 1) * 16 + (size_t)T * E * 4 + (size_t)T * k * 8 + (size_t)E * 8 + 16;
+    return (size_t)(E + 1) * 16 + (size_t)T * E * 4 + (size_t)T * k * 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 16;
 }
 
 struct DecRouteIO {
@@ -224,6 +224,7 @@ struct DecRouteIO {
     int4* slots;
     float* pos_gate;     // [P + T]
     int T, E, k, n_shared, no_renorm;
+    const uint8_t* emask;  // nullable [E + 1]: experts (and the shared one, last) left out when 0
 };
 
 template <int KPL>
@@ -238,7 +239,7 @@ __device__ __forceinline__ int dec_select(const float* l, int E, int k) {
     return wave_topk<KPL>(key, k);
 }
 
-__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask) {
+__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
@@ -248,6 +249,7 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
         s_cnt[e] = 0;
         s_mask[e] = 0;
     }
+    for (int e = tid; e <= E; e += blockDim.x) s_on[e] = io.emask ? io.emask[e] : 1;
     __syncthreads();
     // top-k + gates, a wavefront per token
     for (int t = wv; t < T; t += NW) {
@@ -290,19 +292,20 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
         int sc = 0, sa = 0;
         for (int e = lo; e < hi; ++e) {
             sc += s_cnt[e];
-            sa += s_cnt[e] > 0;
+            sa += s_cnt[e] > 0 && s_on[e];
         }
         const int ic = wave_incl_scan(sc), ia = wave_incl_scan(sa);
         int pc = ic - sc, pa = ia - sa;
         for (int e = lo; e < hi; ++e) {
             const int c = s_cnt[e];
-            if (c > 0) R.slot[pa++] = make_int4(e, pc, c, s_mask[e]);
+            if (c > 0 && s_on[e]) R.slot[pa++] = make_int4(e, pc, c, s_mask[e]);
             pc += c;
         }
         if (lane == MOE_WAVE - 1) {
             R.n_routed = pa;
-            R.n_slots = pa + io.n_shared;
-            if (io.n_shared) R.slot[pa] = make_int4(E, P, T, (int)(T >= 32 ? 0xFFFFFFFFu : ((1u << T) - 1u)));
+            const int shared_on = io.n_shared && s_on[E];
+            R.n_slots = pa + shared_on;
+            if (shared_on) R.slot[pa] = make_int4(E, P, T, (int)(T >= 32 ? 0xFFFFFFFFu : ((1u << T) - 1u)));
         }
     }
     __syncthreads();
@@ -360,8 +363,9 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
         rs.gate = reinterpret_cast<float*>(q); q += (size_t)T * k * 4;
         rs.sel = reinterpret_cast<int*>(q); q += (size_t)T * k * 4;
         int* s_cnt = reinterpret_cast<int*>(q); q += (size_t)E * 4;
-        int* s_mask = reinterpret_cast<int*>(q);
-        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask);
+        int* s_mask = reinterpret_cast<int*>(q); q += (size_t)E * 4;
+        int* s_on = reinterpret_cast<int*>(q);
+        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask, s_on);
     }
 
     const int lane = lane_id();
@@ -576,9 +580,10 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
-                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st) {
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate,
+                          const uint8_t* mask, hipStream_t st) {
     const int fmax = (n_shared && fs > f) ? fs : f;
-    DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0};
+    DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0, mask};
     const int64_t max_slots = (int64_t)(T * k < E ? T * k : E);
     DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
                  (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0,

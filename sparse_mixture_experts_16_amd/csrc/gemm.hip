@@ -48,6 +48,7 @@ struct GemmArgs {
     uint16_t* out_sh;         // W2: y_shared [T, d]
     int64_t lo_off;           // elements from the a hi plane to the a lo plane
     int T, d, f, fs, k, E, n_shared;
+    const uint8_t* mask;      // nullable [E + 1]: groups whose byte is 0 get no tiles
 };
 
 __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
@@ -142,7 +143,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
             nt = (p.E + BN - 1) / BN;
         } else {
             const bool sh = g == p.E;
-            rows = sh ? p.T : p.offsets[g + 1] - p.offsets[g];
+            rows = (p.mask && !p.mask[g]) ? 0 : (sh ? p.T : p.offsets[g + 1] - p.offsets[g]);
             nt = (MODE == MODE_W13) ? ((sh ? p.fs : p.f) + BN / 2 - 1) / (BN / 2) : (p.d + BN - 1) / BN;
         }
         return ((rows + BM - 1) / BM) * nt;
@@ -428,9 +429,9 @@ static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int sha
 hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                             const int32_t*, const int32_t*, const void* w13, const uint8_t* w13s, const void* s13,
                             const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k, int E, int n_shared,
-                            hipStream_t st) {
+                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
-               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask};
     constexpr int BN = 256;  // 128 gate/up column pairs per tile
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
     if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
@@ -441,9 +442,9 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
 hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t*, const int32_t*,
                            const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y,
                            uint16_t* y_shared, int T, int d, int f, int fs, int k, int E, int n_shared,
-                           hipStream_t st) {
+                           const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
-               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask};
     constexpr int BN = 128;
     const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));

@@ -50,14 +50,15 @@ hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int3
                                  int fs, int k, int E, int n_shared, hipStream_t st);
 
 // Prefill grouped GEMM (MFMA).  a_bf16: routed [P, f] then shared [T, fs].
+// mask (nullable, E + 1 bytes): groups whose byte is 0 get no tiles.
 hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                             const int32_t* tile_off, const int32_t* meta, const void* w13, const uint8_t* w13s,
                             const void* s13, const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k,
-                            int E, int n_shared, hipStream_t st);
+                            int E, int n_shared, const uint8_t* mask, hipStream_t st);
 hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t* tile_off,
                            const int32_t* meta, const void* w2, const uint8_t* w2s, const void* s2,
                            const uint8_t* s2s, uint16_t* y, uint16_t* y_shared, int T, int d, int f, int fs, int k,
-                           int E, int n_shared, hipStream_t st);
+                           int E, int n_shared, const uint8_t* mask, hipStream_t st);
 
 // Decode path (T <= 32, T*E <= 8192): router logits, then the FFN kernels (the gate/up kernel
 // redoes the routing per workgroup in LDS; workgroup 0 publishes it).
@@ -68,10 +69,13 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           float* topk_w, int32_t* idx_out, int32_t* meta, int4* slots, float* pos_gate,
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
-                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate, hipStream_t st);
+                          int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate,
+                          const uint8_t* mask, hipStream_t st);
 
+// mask (nullable, E + 1 bytes; needs idx): terms of experts whose byte is 0 are left out.
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
-                          const void* ysh, void* out, int T, int d, int k, bool accumulate, hipStream_t st);
+                          const void* ysh, void* out, int T, int d, int k, bool accumulate, const int32_t* idx,
+                          const uint8_t* mask, int E, hipStream_t st);
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, float* out, int64_t rows, int64_t K,
                                 hipStream_t st);
 hipError_t launch_rmsnorm(int x_dtype, const float* h, void* x, int T, int d, float eps, hipStream_t st);

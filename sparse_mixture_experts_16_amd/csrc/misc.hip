@@ -16,15 +16,21 @@ namespace moe {
 template <typename Y, typename O>
 __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ topk_w, const Y* __restrict__ ysh,
-                                                      O* __restrict__ out, int d, int k, int accumulate) {
+                                                      O* __restrict__ out, int d, int k, int accumulate,
+                                                      const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
+                                                      int E) {
     __shared__ int s_pos[MOE_MAX_K];
     __shared__ float s_g[MOE_MAX_K];
     const int t = blockIdx.x;
     if (threadIdx.x == 0) {
         // insertion sort of the token's pairs by sorted position
         for (int j = 0; j < k; ++j) {
-            const int pos = inv[(int64_t)t * k + j];
+            int pos = inv[(int64_t)t * k + j];
             const float g = topk_w[(int64_t)t * k + j];
+            if (mask) {
+                const int e = idx[(int64_t)t * k + j];
+                if (e < 0 || e >= E || !mask[e]) pos = -1;  // expert outside this partial layer
+            }
             int q = j;
             while (q > 0 && s_pos[q - 1] > pos) {
                 s_pos[q] = s_pos[q - 1];
@@ -50,7 +56,7 @@ __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, c
             for (int v = 0; v < 8; ++v)
                 if (v < nv) acc[v] = fmaf(g, io<Y>::ld(yr, v), acc[v]);
         }
-        if (ysh) {
+        if (ysh && (!mask || mask[E])) {
             const Y* sr = ysh + (int64_t)t * d + i0;
 #pragma unroll
             for (int v = 0; v < 8; ++v)
@@ -67,20 +73,21 @@ __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, c
 }
 
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
-                          const void* ysh, void* out, int T, int d, int k, bool accumulate, hipStream_t st) {
+                          const void* ysh, void* out, int T, int d, int k, bool accumulate, const int32_t* idx,
+                          const uint8_t* mask, int E, hipStream_t st) {
     const int acc = accumulate ? 1 : 0;
     if (y_dtype == 0 && out_dtype == 0)
         hipLaunchKernelGGL((combine_gather<float, float>), dim3(T), dim3(256), 0, st, (const float*)y, inv, topk_w,
-                           (const float*)ysh, (float*)out, d, k, acc);
+                           (const float*)ysh, (float*)out, d, k, acc, idx, mask, E);
     else if (y_dtype == 1 && out_dtype == 1)
         hipLaunchKernelGGL((combine_gather<uint16_t, uint16_t>), dim3(T), dim3(256), 0, st, (const uint16_t*)y, inv,
-                           topk_w, (const uint16_t*)ysh, (uint16_t*)out, d, k, acc);
+                           topk_w, (const uint16_t*)ysh, (uint16_t*)out, d, k, acc, idx, mask, E);
     else if (y_dtype == 1 && out_dtype == 0)
         hipLaunchKernelGGL((combine_gather<uint16_t, float>), dim3(T), dim3(256), 0, st, (const uint16_t*)y, inv,
-                           topk_w, (const uint16_t*)ysh, (float*)out, d, k, acc);
+                           topk_w, (const uint16_t*)ysh, (float*)out, d, k, acc, idx, mask, E);
     else
         hipLaunchKernelGGL((combine_gather<float, uint16_t>), dim3(T), dim3(256), 0, st, (const float*)y, inv,
-                           topk_w, (const float*)ysh, (uint16_t*)out, d, k, acc);
+                           topk_w, (const float*)ysh, (uint16_t*)out, d, k, acc, idx, mask, E);
     return hipGetLastError();
 }
 

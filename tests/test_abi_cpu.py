@@ -112,6 +112,14 @@ def test_other_entry_points_validate():
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert L.moe_stack_forward(ctypes.byref(s), -1, FAKE, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE + 8, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    # the partial layer needs its expert mask, 16-byte aligned, and validates like the full layer
+    masked = lambda s_, m, out=FAKE: L.moe_layer_forward_masked(ctypes.byref(s_), FAKE, FAKE, None, ctypes.byref(W), m,
+                                                               out, None, FAKE, 1 << 40, None)
+    assert masked(s, None) == moe.MOE_ERR_INVALID_ARG
+    assert masked(s, FAKE + 1) == moe.MOE_ERR_INVALID_ARG
+    assert masked(s, FAKE, out=None) == moe.MOE_ERR_INVALID_ARG
+    assert masked(_shape(top_k=0), FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert masked(_shape(T=0), FAKE) == moe.MOE_OK
 
 
 def test_status_strings():
