@@ -97,7 +97,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (MOE_WAVE - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / MOE_WAVE; }
+// The wavefront's index in its workgroup, as a wave-uniform (scalar) value, so that loops and
+// addresses derived from it stay on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE); }
 
 // Lanes below this one in the wave.
 __device__ __forceinline__ uint64_t lanemask_lt() {

@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     auto sS = reinterpret_cast<uint32_t(*)[BN]>(smem + SZ_A + SZ_B);
     int* s_pref = reinterpret_cast<int*>(smem + SZ_RING);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv >> 1, wn = wv & 1;
     const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
     const int P = p.T * p.k;
 
