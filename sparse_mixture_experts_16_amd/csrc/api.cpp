@@ -55,7 +55,7 @@ Layout layout(const moe_shape* s) {
     // fp32 rows of width fmax at decode, two bf16 planes at prefill
     const size_t a_dec = (P + T) * fmax * 4, a_pre = (P * f + T * fs) * 4;
     L.a = o; o = up(o + (a_dec > a_pre ? a_dec : a_pre));
-    L.y = o; o = up(o + P * d * ab);
+    L.y = o; o = up(o + P * d * ab);  // also the router K-split scratch (written only after routing)
     L.ysh = o; o = up(o + T * d * ab);
     L.xn = o; o = up(o + T * d * ab);
     L.total = o;
@@ -201,7 +201,7 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     const bool gemm = use_gemm(s);
     if (use_decode(s)) return run_decode(s, x, w_router, b, w, out, out_dtype, accumulate, idx_out, false, ws, L, mask, st);
     if (gemm && T > DECODE_MAX_T)
-        MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, st));
+        MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, at<float>(ws, L.y), L.ysh - L.y, st));
     else
         MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b, logits, T, d, E, st));
     MOE_TRY(launch_route_topk(logits, T, E, k, (s->flags & MOE_F_NO_RENORM) != 0, idx, g, idx_out, st));
@@ -274,7 +274,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
     if (!logits_in) {
         float* dst = logits_out ? logits_out : at<float>(ws, L.logits);
         if (use_gemm(s) && T > DECODE_MAX_T)
-            MOE_TRY(launch_route_logits_mfma(x, w_router, b_router, dst, T, s->d_model, E, st));
+            MOE_TRY(launch_route_logits_mfma(x, w_router, b_router, dst, T, s->d_model, E, at<float>(ws, L.y),
+                                             L.ysh - L.y, st));
         else
             MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b_router, dst, T, s->d_model, E, st));
         logits = dst;

@@ -49,6 +49,7 @@ struct GemmArgs {
     int64_t lo_off;           // elements from the a hi plane to the a lo plane
     int T, d, f, fs, k, E, n_shared;
     const uint8_t* mask;      // nullable [E + 1]: groups whose byte is 0 get no tiles
+    int ksplit;               // ROUTER: K split over this many workgroups (fp32 partials, no bias) when > 1
 };
 
 __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         int rows, nt;
         if (MODE == MODE_ROUTER) {
             rows = p.T;
-            nt = (p.E + BN - 1) / BN;
+            nt = (p.E + BN - 1) / BN * p.ksplit;
         } else {
             const bool sh = g == p.E;
             rows = (p.mask && !p.mask[g]) ? 0 : (sh ? p.T : p.offsets[g + 1] - p.offsets[g]);
@@ -198,11 +199,17 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         W = shared ? p.sw : p.w + (int64_t)g * N * rb;
         WS = (WT == 2) ? (shared ? p.swsc : p.wsc + (int64_t)g * N * sb) : nullptr;
     }
-    const int local = L - s_pref[g];
+    int local = L - s_pref[g];
+    int ks = 0;
+    if (MODE == MODE_ROUTER && p.ksplit > 1) {
+        ks = local % p.ksplit;
+        local /= p.ksplit;
+        K /= p.ksplit;
+    }
     const int mt = local / ntiles, nt = local % ntiles;
     const int m0 = mt * BM;
     const int mrows = min(BM, rows_g - m0);
-    const int64_t wrb = row_bytes(WT, K), wsb = K / 32;
+    const int64_t wrb = row_bytes(WT, K * (MODE == MODE_ROUTER ? p.ksplit : 1)), wsb = K / 32;
 
     // ---- this thread's global sources.  A chunk slot s = i*256 + tid holds row s/4 at physical
     // chunk s%4; rows past the group's end re-read the tile's first row (their results are
@@ -218,7 +225,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
         else if (MODE == MODE_W2) src = shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
         else src = (int64_t)(m0 + r) * p.d;
-        asrc[i] = p.A + src + c * 8;
+        asrc[i] = p.A + src + (int64_t)ks * K + c * 8;
     }
     // LDS B row n -> weight row.  Gate/up: each wavefront column holds BN/4 gate rows and the
     // matching BN/4 up rows, so SwiGLU pairs meet in the same lane.  Rows past the end map to
@@ -241,7 +248,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int n = i * 64 + (tid >> 2);
-            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (pc ^ chunk_swz(n)) * 16;
+            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (int64_t)ks * K * 2 + (pc ^ chunk_swz(n)) * 16;
         }
     } else {
         // one 16-byte code chunk (the 32-element block) per B row; BN = 128 uses waves 0-1
@@ -340,11 +347,12 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
             for (int j = 0; j < 16; ++j) {
                 const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
                 if (r >= mrows) continue;
-                float* o = reinterpret_cast<float*>(p.out) + (int64_t)(m0 + r) * p.E;
+                float* o = reinterpret_cast<float*>(p.out) + ((int64_t)ks * p.T + m0 + r) * p.E;
+                const bool part = p.ksplit > 1;
 #pragma unroll
                 for (int ns = 0; ns < NT32; ++ns) {
                     const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
-                    if (n < N) o[n] = acc[ms][ns][j] + (p.bias ? p.bias[n] : 0.0f);
+                    if (n < N) o[n] = acc[ms][ns][j] + (!part && p.bias ? p.bias[n] : 0.0f);
                 }
             }
     } else {
@@ -401,16 +409,38 @@ static unsigned grid8(int64_t tiles) {
     return (unsigned)(g < 8 ? 8 : g);
 }
 
+// Router partial sums of a K split, added in split order (then the bias): deterministic.
+__global__ void __launch_bounds__(256) router_reduce(const float* __restrict__ part, const float* __restrict__ b,
+                                                     float* __restrict__ logits, int64_t n, int E, int ks) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float v = 0.0f;
+        for (int q = 0; q < ks; ++q) v += part[(int64_t)q * n + i];
+        logits[i] = v + (b ? b[i % E] : 0.0f);
+    }
+}
+
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
-                                    int E, hipStream_t st) {
+                                    int E, float* part, size_t part_bytes, hipStream_t st) {
+    // T/128 x E/128 tiles alone leave most CUs idle: split K (>= 4 steps of 32 each) over up to 8
+    // workgroups when the partials fit the scratch given.
+    const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + 127) / 128);
+    int ks = 1;
+    while (ks < 8 && tiles * ks * 2 <= 2048 && d % (32 * ks * 2) == 0 && d / (ks * 2) >= 128 &&
+           (size_t)ks * 2 * T * E * 4 <= part_bytes)
+        ks *= 2;
     GemmArgs p{};
     p.A = (const uint16_t*)x;
     p.w = (const uint8_t*)wr;
     p.bias = b;
-    p.out = logits;
+    p.out = ks > 1 ? (void*)part : (void*)logits;
     p.T = T; p.d = d; p.E = E; p.k = 1;
-    const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + 127) / 128);
-    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false>), dim3(grid8(tiles)), dim3(256), 0, st, p);
+    p.ksplit = ks;
+    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ks == 1) return e;
+    const int64_t n = (int64_t)T * E;
+    const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(router_reduce, dim3(grid), dim3(256), 0, st, part, b, logits, n, E, ks);
     return hipGetLastError();
 }
 
@@ -431,7 +461,7 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k, int E, int n_shared,
                             const uint8_t* mask, hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
-               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
     constexpr int BN = 256;  // 128 gate/up column pairs per tile
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
     if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
@@ -444,7 +474,7 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            uint16_t* y_shared, int T, int d, int f, int fs, int k, int E, int n_shared,
                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
-               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask};
+               a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
     constexpr int BN = 128;
     const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));

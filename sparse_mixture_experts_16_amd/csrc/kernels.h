@@ -25,8 +25,9 @@ void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop);
 
 hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
                                int T, int d, int E, hipStream_t st);
+// part: scratch for the K-split partial sums (part_bytes of it; 0 = no split)
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
-                                    int E, hipStream_t st);
+                                    int E, float* part, size_t part_bytes, hipStream_t st);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, bool no_renorm, int32_t* idx, float* w,
                              int32_t* idx2, hipStream_t st);
 

@@ -13,6 +13,30 @@ namespace moe {
 // architecture and the sparsity puzzle", mechanism 1).  One workgroup per token, 8 columns per
 // thread with 16-byte loads.
 // ------------------------------------------------------------------------------------------------
+// 8 consecutive values as 16-byte loads/stores (bf16: one, f32: two)
+template <typename T> struct vec8;
+template <> struct vec8<uint16_t> {
+    __device__ __forceinline__ static void load(const uint16_t* p, float* v) {
+        const uint4 q = *reinterpret_cast<const uint4*>(p);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+    __device__ __forceinline__ static void store(uint16_t* p, const float* v) {
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+};
+template <> struct vec8<float> {
+    __device__ __forceinline__ static void load(const float* p, float* v) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    __device__ __forceinline__ static void store(float* p, const float* v) {
+        reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+};
+
 template <typename Y, typename O>
 __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ topk_w, const Y* __restrict__ ysh,
@@ -44,6 +68,43 @@ __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, c
     __syncthreads();
     for (int i0 = threadIdx.x * 8; i0 < d; i0 += blockDim.x * 8) {
         const int nv = min(8, d - i0);  // d is a multiple of 4 (f32) or 8 (bf16)
+        if (nv == 8) {
+            // 8 columns as whole 16-byte loads, 8 pairs' rows in flight at a time
+            float acc[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
+            for (int q0 = 0; q0 < k; q0 += 8) {
+                float rv[8][8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int pos = q0 + j < k ? s_pos[q0 + j] : -1;
+                    if (pos >= 0) vec8<Y>::load(y + (int64_t)pos * d + i0, rv[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int pos = q0 + j < k ? s_pos[q0 + j] : -1;
+                    if (pos < 0) continue;
+                    const float g = s_g[q0 + j];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) acc[v] = fmaf(g, rv[j][v], acc[v]);
+                }
+            }
+            if (ysh && (!mask || mask[E])) {
+                float sv[8];
+                vec8<Y>::load(ysh + (int64_t)t * d + i0, sv);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[v] += sv[v];
+            }
+            O* orow = out + (int64_t)t * d + i0;
+            if (accumulate) {
+                float pv[8];
+                vec8<O>::load(orow, pv);
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[v] += pv[v];
+            }
+            vec8<O>::store(orow, acc);
+            continue;
+        }
         float acc[8];
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
