@@ -34,7 +34,8 @@ Layout layout(const moe_shape* s) {
     const size_t f = (size_t)s->d_ff, fs = s->n_shared ? (size_t)s->shared_d_ff : 0;
     const size_t P = T * k;
     const size_t ab = (size_t)act_bytes(s->act_dtype);
-    const size_t nblk = P > PERMUTE_SMALL_MAX ? (P + PERMUTE_CHUNK - 1) / PERMUTE_CHUNK : 0;
+    const size_t pc = (size_t)permute_chunk((int64_t)P, (int)E);
+    const size_t nblk = P > PERMUTE_SMALL_MAX ? (P + pc - 1) / pc : 0;
     const size_t fmax = fs > f ? fs : f;
     size_t o = 0;
     L.ticket = o; o = up(o + 4);   // zero while no call runs (see moe_workspace_size)

@@ -7,10 +7,21 @@
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 64
 #define PERMUTE_SMALL_MAX 4096
-#define PERMUTE_CHUNK 2048
+#define PERMUTE_SCAN_LDS 16384  // chunk counts (ints) the one-workgroup scan holds in LDS
 #define GEMM_BM 128  // token rows per grouped-GEMM tile (tile list granularity)
 
 namespace moe {
+
+// Pairs per chunk of the large-P permute: as many chunks as the scan can hold in LDS (at most
+// 256), each a multiple of 64 pairs (one wavefront scatters a chunk).
+inline int permute_chunk(int64_t P, int E) {
+    int64_t nmax = PERMUTE_SCAN_LDS / (E > 0 ? E : 1);
+    if (nmax > 256) nmax = 256;
+    if (nmax < 1) nmax = 1;
+    int64_t c = (P + nmax - 1) / nmax;
+    c = (c + 63) / 64 * 64;
+    return (int)(c < 256 ? 256 : c);
+}
 
 // Timing hook: the launch of the kernel class being profiled carries the caller's start/stop
 // events on its own dispatch packet (hipExtLaunchKernel), so they time that kernel alone.

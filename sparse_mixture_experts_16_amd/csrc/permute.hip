@@ -116,28 +116,65 @@ __global__ void __launch_bounds__(256) permute_hist(const int32_t* __restrict__ 
 }
 
 // Large P, pass 2 (one workgroup): totals, offsets, lists, and each chunk's starting cursor
-// blk[b][e] = offsets[e] + (pairs of expert e in chunks before b).
-__global__ void __launch_bounds__(256) permute_scan(int32_t* __restrict__ blk, int nblk, int E, int bm,
-                                                    int32_t* counts, int32_t* offsets, int32_t* act_list,
-                                                    int32_t* tile_off, int32_t* meta) {
+// blk[b][e] = offsets[e] + (pairs of expert e in chunks before b).  The nblk x E counts are
+// staged in LDS with coalesced loads; each expert's chunks are split into segments, one thread
+// per (expert, segment) sums its segment, the segment sums are scanned per expert, and each
+// thread writes its chunks' running sums.
+__global__ void __launch_bounds__(1024) permute_scan(int32_t* __restrict__ blk, int nblk, int E, int bm,
+                                                     int32_t* counts, int32_t* offsets, int32_t* act_list,
+                                                     int32_t* tile_off, int32_t* meta) {
+    __shared__ int s_blk[PERMUTE_SCAN_LDS];
+    __shared__ int s_seg[1024];
     __shared__ int s_cnt[MOE_MAX_E];
     __shared__ int s_cur[MOE_MAX_E];
+    const int n = nblk * E;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * blockDim.x) {  // 8 loads in flight per thread
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * blockDim.x;
+            v[j] = i < n ? blk[i] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * blockDim.x;
+            if (i < n) s_blk[i] = v[j];
+        }
+    }
+    const int nseg = E >= (int)blockDim.x ? 1 : (int)blockDim.x / E;
+    const int seg_len = (nblk + nseg - 1) / nseg;
+    __syncthreads();
+    for (int t = threadIdx.x; t < E * nseg; t += blockDim.x) {
+        const int e = t % E, sg = t / E;
+        const int b0 = sg * seg_len, b1 = min(b0 + seg_len, nblk);
+        int sum = 0;
+        for (int b = b0; b < b1; ++b) sum += s_blk[b * E + e];
+        s_seg[t] = sum;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int run = 0;
-        for (int b = 0; b < nblk; ++b) {
-            int c = blk[(int64_t)b * E + e];
-            blk[(int64_t)b * E + e] = run;
+        for (int sg = 0; sg < nseg; ++sg) {
+            const int c = s_seg[sg * E + e];
+            s_seg[sg * E + e] = run;
             run += c;
         }
         s_cnt[e] = run;
     }
     __syncthreads();
+    for (int t = threadIdx.x; t < E * nseg; t += blockDim.x) {
+        const int e = t % E, sg = t / E;
+        const int b0 = sg * seg_len, b1 = min(b0 + seg_len, nblk);
+        int run = s_seg[t];
+        for (int b = b0; b < b1; ++b) {
+            const int c = s_blk[b * E + e];
+            s_blk[b * E + e] = run;
+            run += c;
+        }
+    }
     if (wave_id() == 0) scan_counts_wave0(s_cnt, s_cur, E, bm, counts, offsets, act_list, tile_off, meta);
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const int off = s_cur[e];
-        for (int b = 0; b < nblk; ++b) blk[(int64_t)b * E + e] += off;
-    }
+    for (int i = threadIdx.x; i < n; i += blockDim.x) blk[i] = s_blk[i] + s_cur[i % E];
 }
 
 // Large P, pass 3: one wavefront per chunk scatters its pairs stably from its cursors.
@@ -177,11 +214,12 @@ hipError_t launch_permute(const int32_t* idx, int P, int E, int bm, int32_t* cou
                            act_list, tile_off, meta);
         return hipGetLastError();
     }
-    const int nblk = (P + PERMUTE_CHUNK - 1) / PERMUTE_CHUNK;
-    hipLaunchKernelGGL(permute_hist, dim3(nblk), dim3(256), 0, st, idx, P, E, PERMUTE_CHUNK, blk);
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(256), 0, st, blk, nblk, E, bm, counts, offsets, act_list,
+    const int chunk = permute_chunk(P, E);
+    const int nblk = (P + chunk - 1) / chunk;
+    hipLaunchKernelGGL(permute_hist, dim3(nblk), dim3(256), 0, st, idx, P, E, chunk, blk);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, st, blk, nblk, E, bm, counts, offsets, act_list,
                        tile_off, meta);
-    hipLaunchKernelGGL(permute_scatter, dim3(nblk), dim3(64), 0, st, idx, P, E, PERMUTE_CHUNK, blk, perm, inv);
+    hipLaunchKernelGGL(permute_scatter, dim3(nblk), dim3(64), 0, st, idx, P, E, chunk, blk, perm, inv);
     return hipGetLastError();
 }
 
