@@ -105,18 +105,20 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) { __builtin_amdg
 __device__ __forceinline__ void dma4(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0); }
 __device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-template <int MODE, int WT, int BN, bool SPLIT>
-__global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
+template <int MODE, int WT, int BN, bool SPLIT, int NWN>
+__global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 waves per SIMD: <= 256 registers
     constexpr int BM = TBM, BK = 32, NS = 3;
+    constexpr int THREADS = 128 * NWN;              // 2 wavefronts along M x NWN along N
     constexpr int NPL = SPLIT ? 2 : 1;              // A planes
-    constexpr int WN = BN / 2;                      // wave tile columns
+    constexpr int WN = BN / NWN;                    // wave tile columns
     constexpr int NT32 = WN / 32;                   // 32-wide MFMA column tiles per wave (2 or 4)
     constexpr int ROWE = BK;                        // bf16 elements per LDS tile row (64 B)
     constexpr int BROW = (WT == 1) ? 32 : 8;        // uint16 per LDS B row (bf16: 64 B, MXFP4 codes: 16 B)
-    constexpr int NA = BM * 4 / 256;                // A chunks per thread per plane (2)
-    constexpr int NB = (WT == 1) ? BN * 4 / 256 : (BN + 255) / 256;  // B chunks per thread (max)
+    constexpr int NA = BM * 4 / THREADS;            // A chunks per thread per plane
+    constexpr int NB = (WT == 1) ? BN * 4 / THREADS : (BN + THREADS - 1) / THREADS;  // B chunks per thread (max)
+    static_assert(NA >= 1 && (WT != 1 || NB >= 1), "tile / thread count");
     // vector-memory ops one stage adds per thread, counted for the wave that issues the fewest
-    constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BN >= 256 ? 1 : 0));
+    constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BN >= THREADS ? 1 : 0));
     static_assert(OPS < 16, "vmcnt immediate");
     // One LDS object carved by offsets: with a single object the compiler's wait insertion
     // leaves LDS-DMA completion to the explicit vmcnt waits below instead of draining the
@@ -124,7 +126,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     constexpr int SZ_A = NS * NPL * BM * ROWE * 2, SZ_B = NS * BN * BROW * 2, SZ_S = (WT == 2 ? 2 * BN * 4 : 0);
     // output staging after the K loop (reuses the ring): bf16 rows of NCOL columns, pitch OP
     constexpr int NCOL = (MODE == MODE_W13) ? BN / 2 : BN, OP = NCOL + 8;
-    constexpr int SZ_O = (MODE == MODE_ROUTER) ? 0 : ((MODE == MODE_W13) ? 2 : 1) * BM * OP * 2;
+    constexpr int SZ_O = (MODE == MODE_ROUTER) ? 0 : BM * OP * 2;  // one bf16 plane at a time
     constexpr int SZ_RING = (SZ_A + SZ_B + SZ_S) > SZ_O ? (SZ_A + SZ_B + SZ_S) : SZ_O;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SZ_RING + (MOE_MAX_E + 2) * 4];
     auto sA = reinterpret_cast<uint16_t(*)[NPL][BM * ROWE]>(smem);
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     auto sS = reinterpret_cast<uint32_t(*)[BN]>(smem + SZ_A + SZ_B);
     int* s_pref = reinterpret_cast<int*>(smem + SZ_RING);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv >> 1, wn = wv & 1;
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv / NWN, wn = wv % NWN;
     const int G = (MODE == MODE_ROUTER) ? 1 : p.E + p.n_shared;
     const int P = p.T * p.k;
 
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     const uint16_t* asrc[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        int r = i * 64 + (tid >> 2);
+        int r = i * (THREADS / 4) + (tid >> 2);
         const int c = pc ^ chunk_swz(r);
         if (r >= mrows) r = 0;
         int64_t src;
@@ -232,7 +234,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     // weight row 0 (their columns are never stored).
     auto wrow_of = [&](int n) -> int {
         if (MODE == MODE_W13) {
-            constexpr int H = BN / 4;
+            constexpr int H = BN / (2 * NWN);
             const int j0 = nt * (BN / 2), h = n / (2 * H), w = n % (2 * H);
             const int j = j0 + h * H + (w < H ? w : w - H);
             if (j >= fg) return 0;
@@ -247,7 +249,7 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
     if (WT == 1) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int n = i * 64 + (tid >> 2);
+            const int n = i * (THREADS / 4) + (tid >> 2);
             bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (int64_t)ks * K * 2 + (pc ^ chunk_swz(n)) * 16;
         }
     } else {
@@ -264,14 +266,14 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
         const int k0 = kt * BK;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            uint16_t* dA = &sA[st][0][(i * 256 + wv * 64) * 8];
+            uint16_t* dA = &sA[st][0][(i * THREADS + wv * 64) * 8];
             dma16(asrc[i] + k0, dA);
-            if (SPLIT) dma16(asrc[i] + p.lo_off + k0, &sA[st][NPL - 1][(i * 256 + wv * 64) * 8]);
+            if (SPLIT) dma16(asrc[i] + p.lo_off + k0, &sA[st][NPL - 1][(i * THREADS + wv * 64) * 8]);
         }
         if (WT == 1) {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
-                dma16(bsrc[i] + (int64_t)k0 * 2, &sB[st][(i * 256 + wv * 64) * 8]);
+                dma16(bsrc[i] + (int64_t)k0 * 2, &sB[st][(i * THREADS + wv * 64) * 8]);
         } else {
             if (b_on) dma16(bsrc[0] + k0 / 2, &sB[st][wv * 64 * 8]);
             if (s_on && (kt & 3) == 0)
@@ -357,47 +359,57 @@ __global__ void __launch_bounds__(256, 2) ggemm(GemmArgs p) {
             }
     } else {
         // Stage the tile's bf16 outputs in LDS (the ring is free once every wavefront is past
-        // its last fragment read), then store whole 16-byte row chunks.
-        __syncthreads();
-        uint16_t* o_hi = reinterpret_cast<uint16_t*>(smem);
-        uint16_t* o_lo = o_hi + BM * OP;
+        // its last fragment read), one plane at a time, then store whole 16-byte row chunks.
+        uint16_t* o_st = reinterpret_cast<uint16_t*>(smem);
+        if constexpr (MODE == MODE_W13) {
+            // SwiGLU in place of the gate accumulators
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+            for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-                if constexpr (MODE == MODE_W13) {
+                for (int ns = 0; ns < NT32 / 2; ++ns)
 #pragma unroll
-                    for (int ns = 0; ns < NT32 / 2; ++ns) {
-                        const int c = wn * (BN / 4) + ns * 32 + (lane & 31);
+                    for (int j = 0; j < 16; ++j) {
                         const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
-                        const float av = gt / (1.0f + expf(-gt)) * up;
-                        const uint16_t hi = f32_to_bf16(av);
-                        o_hi[r * OP + c] = hi;
-                        o_lo[r * OP + c] = f32_to_bf16(av - bf16_to_f32(hi));
+                        acc[ms][ns][j] = gt / (1.0f + expf(-gt)) * up;
                     }
-                } else {
-#pragma unroll
-                    for (int ns = 0; ns < NT32; ++ns) o_hi[r * OP + wn * WN + ns * 32 + (lane & 31)] = f32_to_bf16(acc[ms][ns][j]);
-                }
-            }
-        __syncthreads();
+        }
         constexpr int CH = NCOL / 8;  // 16-byte chunks per staged row
         const int col0 = nt * NCOL;
         const int lim = (MODE == MODE_W13) ? fg : N;  // columns of this group's output rows
-        for (int i = tid; i < BM * CH; i += 256) {
-            const int r = i / CH, ch = i % CH;
-            if (r >= mrows || col0 + ch * 8 >= lim) continue;
-            const int row = m0 + r;
-            const uint4 v = *reinterpret_cast<const uint4*>(&o_hi[r * OP + ch * 8]);
-            if constexpr (MODE == MODE_W13) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(p.out) +
-                              (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f) + col0 + ch * 8;
-                *reinterpret_cast<uint4*>(o) = v;
-                *reinterpret_cast<uint4*>(o + p.lo_off) = *reinterpret_cast<const uint4*>(&o_lo[r * OP + ch * 8]);
-            } else {
-                uint16_t* o = (shared ? p.out_sh + (int64_t)row * p.d
-                                      : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+#pragma unroll
+        for (int pl = 0; pl < (MODE == MODE_W13 ? 2 : 1); ++pl) {
+            __syncthreads();
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+                    if constexpr (MODE == MODE_W13) {
+#pragma unroll
+                        for (int ns = 0; ns < NT32 / 2; ++ns) {
+                            const float av = acc[ms][ns][j];
+                            const uint16_t hi = f32_to_bf16(av);
+                            o_st[r * OP + wn * (WN / 2) + ns * 32 + (lane & 31)] =
+                                pl == 0 ? hi : f32_to_bf16(av - bf16_to_f32(hi));
+                        }
+                    } else {
+#pragma unroll
+                        for (int ns = 0; ns < NT32; ++ns) o_st[r * OP + wn * WN + ns * 32 + (lane & 31)] = f32_to_bf16(acc[ms][ns][j]);
+                    }
+                }
+            __syncthreads();
+            for (int i = tid; i < BM * CH; i += THREADS) {
+                const int r = i / CH, ch = i % CH;
+                if (r >= mrows || col0 + ch * 8 >= lim) continue;
+                const int row = m0 + r;
+                const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
+                uint16_t* o;
+                if constexpr (MODE == MODE_W13)
+                    o = reinterpret_cast<uint16_t*>(p.out) + (pl ? p.lo_off : 0) +
+                        (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f) + col0 + ch * 8;
+                else
+                    o = (shared ? p.out_sh + (int64_t)row * p.d
+                                : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
                 *reinterpret_cast<uint4*>(o) = v;
             }
         }
@@ -435,7 +447,7 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     p.out = ks > 1 ? (void*)part : (void*)logits;
     p.T = T; p.d = d; p.E = E; p.k = 1;
     p.ksplit = ks;
-    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false, 2>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ks == 1) return e;
     const int64_t n = (int64_t)T * E;
@@ -462,10 +474,10 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             const uint8_t* mask, hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
-    constexpr int BN = 256;  // 128 gate/up column pairs per tile
+    constexpr int BN = 256, NWN = 2;  // 128 gate/up column pairs per tile, 4 wavefronts
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
-    if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false>), dim3(grid), dim3(256), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
     return hipGetLastError();
 }
 
@@ -475,11 +487,11 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
-    constexpr int BN = 128;
+    constexpr int BN = 128, NWN = 2;
     const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-    if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true>), dim3(grid), dim3(256), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true>), dim3(grid), dim3(256), 0, st, p);
+    if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
     return hipGetLastError();
 }
 
