@@ -124,12 +124,12 @@ class LayerSpec:
     n_shared: int     # 0 or 1 always-on shared expert
     f_shared: int
     act: str          # 'f32' | 'bf16'
-    wt: str           # 'f32' | 'bf16' | 'mxfp4'
+    wt: str           # 'f32' | 'bf16' | 'mxfp4' | 'nvfp4'
     sigma_x: float
     sigma_w: float
     sigma_r: float
     bias: str = "zero"   # 'zero' | 'zipf'
-    scale_lo: int = 119  # MXFP4 E8M0 scale byte range (2^-8 .. 2^0)
+    scale_lo: int = 119  # scale byte range: MXFP4 E8M0 119..127 = 2^-8 .. 2^0 (NVFP4 E4M3: 0x20..0x3F)
     scale_hi: int = 127
     seed: int = 1000
     n_layers: int = 1
@@ -151,6 +151,9 @@ CONFIGS = {
     "c3": LayerSpec("c3", 1, 4096, 2048, 256, 6, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.02, seed=1003),
     # 43-layer stack of c3's layer.
     "c4": LayerSpec("c4", 1, 4096, 2048, 256, 6, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.02, seed=1004, n_layers=43),
+    # c3's layer with NVFP4 expert weights (E2M1 + one E4M3 scale per 16 + an fp32 tensor scale).
+    "c3nv": LayerSpec("c3nv", 1, 4096, 2048, 256, 6, 0, 0, "bf16", "nvfp4", 1.0, 0.0, 0.02, scale_lo=0x20,
+                      scale_hi=0x3F, seed=1005),
 }
 
 
@@ -224,6 +227,12 @@ def router_bias(s: LayerSpec, layer: int = 0) -> np.ndarray:
     return np.array([-1.1 * math.log(v) for v in r], np.float32)
 
 
+# NVFP4 tensor scales (fp32, one per weight tensor) of the synthetic layers: gate/up, down.
+NVFP4_GSCALE = (0.3, 0.6)
+# NVFP4 block-scale bytes are drawn uniformly over E4M3 codes 0x20..0x3F: 2^-3 .. 1.875.
+NVFP4_SCALE_LO, NVFP4_SCALE_HI = 0x20, 0x3F
+
+
 def host_experts(s: LayerSpec, layer: int = 0, experts: Optional[Sequence[int]] = None, shared: bool = False):
     """Expert weights for the listed experts (all when None), stacked in that order.
 
@@ -266,6 +275,19 @@ def host_experts(s: LayerSpec, layer: int = 0, experts: Optional[Sequence[int]] 
             lib.mg_fill_scale_bytes_experts(_ptr(w13s[i]), w13s[i].size, e, 1, k13s, s.scale_lo, s.scale_hi)
             lib.mg_fill_scale_bytes_experts(_ptr(w2s[i]), w2s[i].size, e, 1, k2s, s.scale_lo, s.scale_hi)
         out.update(w13=w13, w2=w2, w13_scale=w13s, w2_scale=w2s)
+    elif s.wt == "nvfp4":
+        assert d % 32 == 0 and f % 32 == 0
+        w13 = np.empty((n, 2 * f, d // 2), np.uint8)
+        w2 = np.empty((n, d, f // 2), np.uint8)
+        w13s = np.empty((n, 2 * f, d // 16), np.uint8)
+        w2s = np.empty((n, d, f // 16), np.uint8)
+        for i, e in enumerate(experts):
+            lib.mg_fill_bytes_experts(_ptr(w13[i]), w13[i].size, e, 1, k13)
+            lib.mg_fill_bytes_experts(_ptr(w2[i]), w2[i].size, e, 1, k2)
+            lib.mg_fill_scale_bytes_experts(_ptr(w13s[i]), w13s[i].size, e, 1, k13s, s.scale_lo, s.scale_hi)
+            lib.mg_fill_scale_bytes_experts(_ptr(w2s[i]), w2s[i].size, e, 1, k2s, s.scale_lo, s.scale_hi)
+        out.update(w13=w13, w2=w2, w13_scale=w13s, w2_scale=w2s, w13_gscale=NVFP4_GSCALE[0],
+                   w2_gscale=NVFP4_GSCALE[1])
     else:
         raise ValueError(s.wt)
     return out
@@ -308,15 +330,18 @@ def device_experts(s: LayerSpec, layer: int = 0, shared: bool = False, device="c
         _check(fill(w2.data_ptr(), d * f, 0, n, k2, c, 1, st))
         out["w13"], out["w2"] = w13, w2
     else:
+        blk = 16 if s.wt == "nvfp4" else 32  # elements per scale byte
         w13 = torch.empty((n, 2 * f, d // 2), dtype=torch.uint8, device=device)
         w2 = torch.empty((n, d, f // 2), dtype=torch.uint8, device=device)
-        w13s = torch.empty((n, 2 * f, d // 32), dtype=torch.uint8, device=device)
-        w2s = torch.empty((n, d, f // 32), dtype=torch.uint8, device=device)
+        w13s = torch.empty((n, 2 * f, d // blk), dtype=torch.uint8, device=device)
+        w2s = torch.empty((n, d, f // blk), dtype=torch.uint8, device=device)
         _check(lib.mgd_fill_bytes(w13.data_ptr(), w13[0].numel(), 0, n, k13, 1, st))
         _check(lib.mgd_fill_bytes(w2.data_ptr(), w2[0].numel(), 0, n, k2, 1, st))
         _check(lib.mgd_fill_scale_bytes(w13s.data_ptr(), w13s[0].numel(), 0, n, k13s, s.scale_lo, s.scale_hi, 1, st))
         _check(lib.mgd_fill_scale_bytes(w2s.data_ptr(), w2s[0].numel(), 0, n, k2s, s.scale_lo, s.scale_hi, 1, st))
         out.update(w13=w13, w2=w2, w13_scale=w13s, w2_scale=w2s)
+        if s.wt == "nvfp4":
+            out.update(w13_gscale=NVFP4_GSCALE[0], w2_gscale=NVFP4_GSCALE[1])
     return out
 
 

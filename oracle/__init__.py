@@ -19,9 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # MOE_REF_LIB lets the mutation test load a deliberately broken build of the oracle.
 LIB_PATH = os.environ.get("MOE_REF_LIB") or os.path.join(_HERE, "libmoe_ref.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
 NO_RENORM, ACCUMULATE = 1, 2
-_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4}
+_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "nvfp4": NVFP4}
 
 
 class Shape(ctypes.Structure):
@@ -31,7 +31,8 @@ class Shape(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w13", "w2", "w13_scale", "w2_scale", "s13", "s2", "s13_scale", "s2_scale")]
+    _fields_ = ([(n, ctypes.c_void_p) for n in ("w13", "w2", "w13_scale", "w2_scale", "s13", "s2", "s13_scale", "s2_scale")]
+                + [(n, ctypes.c_float) for n in ("w13_gscale", "w2_gscale", "s13_gscale", "s2_gscale")])
 
 
 _lib = None
@@ -47,6 +48,8 @@ def lib():
         wp = ctypes.POINTER(Weights)
         L.moe_ref_num_threads.restype = ctypes.c_int
         L.moe_ref_mxfp4_dequant.argtypes = [vp, vp, i64, i64, vp]
+        L.moe_ref_e4m3_to_f32.argtypes = [vp, i64, vp]
+        L.moe_ref_nvfp4_dequant.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
         L.moe_ref_router_logits.argtypes = [sp, vp, vp, vp, vp, vp]
         L.moe_ref_topk.argtypes = [sp, vp, vp, vp]
         L.moe_ref_permute.argtypes = [sp, vp, vp, vp, vp, vp]
@@ -81,14 +84,33 @@ def weights(w: dict, shared: Optional[dict] = None) -> Weights:
     W = Weights()
     W.w13, W.w2 = _p(w["w13"]), _p(w["w2"])
     W.w13_scale, W.w2_scale = _p(w.get("w13_scale")), _p(w.get("w2_scale"))
+    W.w13_gscale, W.w2_gscale = float(w.get("w13_gscale", 1.0)), float(w.get("w2_gscale", 1.0))
     if shared is not None:
         W.s13, W.s2 = _p(shared["w13"]), _p(shared["w2"])
         W.s13_scale, W.s2_scale = _p(shared.get("w13_scale")), _p(shared.get("w2_scale"))
+        W.s13_gscale, W.s2_gscale = float(shared.get("w13_gscale", 1.0)), float(shared.get("w2_gscale", 1.0))
     return W
 
 
 def num_threads() -> int:
     return int(lib().moe_ref_num_threads())
+
+
+def e4m3_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, np.uint8)
+    out = np.empty(b.shape, np.float32)
+    _rc(lib().moe_ref_e4m3_to_f32(_p(b), b.size, _p(out)), "e4m3_to_f32")
+    return out
+
+
+def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, gscale: float) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, half_k = codes.shape[0], codes.shape[1]
+    K = 2 * half_k
+    out = np.empty((rows, K), np.float32)
+    _rc(lib().moe_ref_nvfp4_dequant(_p(codes), _p(scales), ctypes.c_float(gscale), rows, K, _p(out)), "nvfp4_dequant")
+    return out
 
 
 def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -82,21 +82,64 @@ int moe_ref_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t r
     return 0;
 }
 
-/* Row n of a [N, K] weight matrix of expert e (tensor holds E_or_1 such matrices), upcast to fp64. */
-static void weight_row(int32_t dtype, const void* w, const uint8_t* scale, int64_t e, int64_t N, int64_t K,
-                       int64_t n, double* row) {
+/* OCP FP8 E4M3 ("fn": no infinities, one NaN pattern per sign), from its bit fields. */
+static double e4m3_value(uint8_t b) {
+    int sgn = b >> 7, ex = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (ex == 15 && m == 7) return NAN;
+    if (ex == 0) v = ldexp((double)m, -9);              /* m/8 * 2^-6 */
+    else v = ldexp((double)(8 + m), ex - 10);           /* (1 + m/8) * 2^(ex-7) */
+    return sgn ? -v : v;
+}
+
+int moe_ref_e4m3_to_f32(const uint8_t* b, int64_t n, float* out) {
+    if (!b || !out || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = (float)e4m3_value(b[i]);
+    return 0;
+}
+
+/* One NVFP4 element: E2M1 value * E4M3 block scale * tensor scale, exact in fp64. */
+static double nvfp4_value(uint8_t code, uint8_t scale, float gscale) {
+    double m = (double)kE2M1[code & 7];
+    if (code & 8) m = -m;
+    return m * e4m3_value(scale) * (double)gscale;
+}
+
+int moe_ref_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, int64_t rows, int64_t K,
+                          float* out) {
+    if (!codes || !scales || !out || rows < 0 || K < 0 || K % 16 != 0) return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < K; ++j) {
+            uint8_t byte = codes[r * (K / 2) + j / 2];
+            uint8_t code = (j % 2 == 0) ? (uint8_t)(byte & 0xF) : (uint8_t)(byte >> 4);
+            out[r * K + j] = (float)nvfp4_value(code, scales[r * (K / 16) + j / 16], gscale);
+        }
+    return 0;
+}
+
+/* Row n of a [N, K] weight matrix of expert e (tensor holds E_or_1 such matrices), upcast to fp64.
+   gscale: the NVFP4 tensor scale (unused otherwise). */
+static void weight_row(int32_t dtype, const void* w, const uint8_t* scale, float gscale, int64_t e, int64_t N,
+                       int64_t K, int64_t n, double* row) {
     if (dtype == MOE_REF_F32) {
         const float* p = (const float*)w + (e * N + n) * K;
         for (int64_t j = 0; j < K; ++j) row[j] = (double)p[j];
     } else if (dtype == MOE_REF_BF16) {
         const uint16_t* p = (const uint16_t*)w + (e * N + n) * K;
         for (int64_t j = 0; j < K; ++j) row[j] = (double)bf16_bits_to_f32(p[j]);
-    } else {
+    } else if (dtype == MOE_REF_MXFP4) {
         const uint8_t* c = (const uint8_t*)w + (e * N + n) * (K / 2);
         const uint8_t* sc = scale + (e * N + n) * (K / 32);
         for (int64_t j = 0; j < K; ++j) {
             uint8_t code = (j % 2 == 0) ? (uint8_t)(c[j / 2] & 0xF) : (uint8_t)(c[j / 2] >> 4);
             row[j] = (double)mxfp4_value(code, sc[j / 32]);
+        }
+    } else {
+        const uint8_t* c = (const uint8_t*)w + (e * N + n) * (K / 2);
+        const uint8_t* sc = scale + (e * N + n) * (K / 16);
+        for (int64_t j = 0; j < K; ++j) {
+            uint8_t code = (j % 2 == 0) ? (uint8_t)(c[j / 2] & 0xF) : (uint8_t)(c[j / 2] >> 4);
+            row[j] = nvfp4_value(code, sc[j / 16], gscale);
         }
     }
 }
@@ -122,7 +165,7 @@ static int shape_ok(const moe_ref_shape* s) {
     if (!s) return 0;
     if (s->T < 0 || s->d < 1 || s->E < 1 || s->k < 1 || s->k > s->E) return 0;
     if (s->act_dtype != MOE_REF_F32 && s->act_dtype != MOE_REF_BF16) return 0;
-    if (s->wt_dtype < MOE_REF_F32 || s->wt_dtype > MOE_REF_MXFP4) return 0;
+    if (s->wt_dtype < MOE_REF_F32 || s->wt_dtype > MOE_REF_NVFP4) return 0;
     if (s->n_shared < 0 || s->n_shared > 1) return 0;
     return 1;
 }
@@ -229,8 +272,9 @@ int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* co
 
 /* SwiGLU expert on n tokens (xs [n][d] fp64): ys [n][d] = W2 (silu(Wg x) * (Wu x)).
    Weight tensors hold several experts; `e` picks one; f is this expert's d_ff. */
-static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, const void* w2, const uint8_t* w2s,
-                       int64_t e, int64_t d, int64_t f, const double* xs, int64_t n, double* ys) {
+static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g13, const void* w2,
+                       const uint8_t* w2s, float g2, int64_t e, int64_t d, int64_t f, const double* xs, int64_t n,
+                       double* ys) {
     double* a = (double*)malloc(sizeof(double) * (size_t)(n * f + 1));
     /* Gate and up projections, then the SwiGLU activation. */
 #pragma omp parallel
@@ -239,8 +283,8 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, const v
         double* ru = (double*)malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(static)
         for (int64_t j = 0; j < f; ++j) {
-            weight_row(wt, w13, w13s, e, 2 * f, d, j, rg);
-            weight_row(wt, w13, w13s, e, 2 * f, d, f + j, ru);
+            weight_row(wt, w13, w13s, g13, e, 2 * f, d, j, rg);
+            weight_row(wt, w13, w13s, g13, e, 2 * f, d, f + j, ru);
             for (int64_t t = 0; t < n; ++t) {
                 double hg = dot(rg, xs + t * d, d);
                 double hu = dot(ru, xs + t * d, d);
@@ -256,7 +300,7 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, const v
         double* rd = (double*)malloc(sizeof(double) * (size_t)f);
 #pragma omp for schedule(static)
         for (int64_t i = 0; i < d; ++i) {
-            weight_row(wt, w2, w2s, e, d, f, i, rd);
+            weight_row(wt, w2, w2s, g2, e, d, f, i, rd);
             for (int64_t t = 0; t < n; ++t) ys[t * d + i] = dot(rd, a + t * f, f);
         }
         free(rd);
@@ -269,21 +313,24 @@ int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* pe
     if (!shape_ok(s) || !w || !offsets) return -1;
     const int64_t T = s->T, d = s->d, f = s->f, E = s->E, k = s->k;
     if (s->wt_dtype == MOE_REF_MXFP4 && (d % 32 || f % 32 || !w->w13_scale || !w->w2_scale)) return -1;
+    if (s->wt_dtype == MOE_REF_NVFP4 && (d % 16 || f % 16 || !w->w13_scale || !w->w2_scale)) return -1;
     if (T > 0 && (!x || !perm || !y_sorted || !w->w13 || !w->w2)) return -1;
     double* xs = (double*)malloc(sizeof(double) * (size_t)(T * d + 1));
     for (int64_t e = 0; e < E; ++e) {
         int64_t n = offsets[e + 1] - offsets[e];
         if (n == 0) continue;
         for (int64_t i = 0; i < n; ++i) act_row(s->act_dtype, x, d, perm[offsets[e] + i] / k, xs + i * d);
-        expert_ffn(s->wt_dtype, w->w13, w->w13_scale, w->w2, w->w2_scale, e, d, f, xs, n,
-                   y_sorted + (int64_t)offsets[e] * d);
+        expert_ffn(s->wt_dtype, w->w13, w->w13_scale, w->w13_gscale, w->w2, w->w2_scale, w->w2_gscale, e, d, f, xs,
+                   n, y_sorted + (int64_t)offsets[e] * d);
     }
     if (y_shared) {
         if (s->n_shared != 1 || !w->s13 || !w->s2) { free(xs); return -1; }
         if (s->wt_dtype == MOE_REF_MXFP4 && (s->f_shared % 32 || !w->s13_scale || !w->s2_scale)) { free(xs); return -1; }
+        if (s->wt_dtype == MOE_REF_NVFP4 && (s->f_shared % 16 || !w->s13_scale || !w->s2_scale)) { free(xs); return -1; }
         for (int64_t t = 0; t < T; ++t) act_row(s->act_dtype, x, d, t, xs + t * d);
         if (T > 0)
-            expert_ffn(s->wt_dtype, w->s13, w->s13_scale, w->s2, w->s2_scale, 0, d, s->f_shared, xs, T, y_shared);
+            expert_ffn(s->wt_dtype, w->s13, w->s13_scale, w->s13_gscale, w->s2, w->s2_scale, w->s2_gscale, 0, d,
+                       s->f_shared, xs, T, y_shared);
     }
     free(xs);
     return 0;

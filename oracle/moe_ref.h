@@ -34,29 +34,41 @@
 extern "C" {
 #endif
 
-enum { MOE_REF_F32 = 0, MOE_REF_BF16 = 1, MOE_REF_MXFP4 = 2 };
+enum { MOE_REF_F32 = 0, MOE_REF_BF16 = 1, MOE_REF_MXFP4 = 2, MOE_REF_NVFP4 = 3 };
 enum { MOE_REF_NO_RENORM = 1u << 0, MOE_REF_ACCUMULATE = 1u << 1 };
 
 typedef struct {
     int64_t T, d, f, E, k, n_shared, f_shared;
     int32_t act_dtype;   /* MOE_REF_F32 or MOE_REF_BF16 (bf16 given as raw uint16 bits) */
-    int32_t wt_dtype;    /* MOE_REF_F32, MOE_REF_BF16 or MOE_REF_MXFP4 */
+    int32_t wt_dtype;    /* MOE_REF_F32, MOE_REF_BF16, MOE_REF_MXFP4 or MOE_REF_NVFP4 */
     uint32_t flags;      /* MOE_REF_NO_RENORM, MOE_REF_ACCUMULATE */
 } moe_ref_shape;
 
 /* Routed weights w13 [E, 2f, d] (rows 0..f-1 gate, f..2f-1 up), w2 [E, d, f];
    for MXFP4, codes [E, N, K/2] (element 2i in the low nibble of byte i) and
-   scales [E, N, K/32] (one E8M0 byte per 32 consecutive elements of a row).
+   scales [E, N, K/32] (one E8M0 byte per 32 consecutive elements of a row);
+   for NVFP4, the same codes, scales [E, N, K/16] (one FP8 E4M3 byte per 16
+   consecutive elements) and one fp32 scale per tensor (*_gscale).
    Shared expert s13 [2 f_shared, d], s2 [d, f_shared] in the same format. */
 typedef struct {
     const void* w13; const void* w2; const uint8_t* w13_scale; const uint8_t* w2_scale;
     const void* s13; const void* s2; const uint8_t* s13_scale; const uint8_t* s2_scale;
+    float w13_gscale, w2_gscale, s13_gscale, s2_gscale;   /* NVFP4 only */
 } moe_ref_weights;
 
 int moe_ref_num_threads(void);
 
 /* MXFP4 -> fp32: out[r*K + j] = (-1)^b3 * M[code & 7] * 2^(s - 127), s = 255 -> NaN. */
 int moe_ref_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out);
+
+/* OCP FP8 E4M3 (the "fn" variant: no infinities) -> fp32, by its bit fields:
+   (-1)^s * (e == 0 ? m/8 * 2^-6 : (1 + m/8) * 2^(e-7)), NaN for e = 15, m = 7. */
+int moe_ref_e4m3_to_f32(const uint8_t* b, int64_t n, float* out);
+
+/* NVFP4 -> fp32: out[r*K + j] = E2M1(code) * E4M3(scales[r*(K/16) + j/16]) * gscale,
+   the exact product rounded once to fp32; codes [rows, K/2] as for MXFP4; K % 16 == 0. */
+int moe_ref_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, int64_t rows, int64_t K,
+                          float* out);
 
 /* Router logits l[t,e] = sum_i x[t,i] W_r[e,i] + b[e]; logits [T,E] fp32 (the fp64
    value rounded once); logits64 (nullable) keeps the fp64 value. b may be NULL. */

@@ -34,6 +34,11 @@ MUTANTS = {
     "pair_token_index": ("perm[offsets[e] + i] / k", "perm[offsets[e] + i] % k"),
     "mask_ignored": ("if (expert_mask && !expert_mask[e]) continue;", "(void)e;"),
     "x_upcast_truncated": ("row[i] = (double)bf16_bits_to_f32(p[i]);", "row[i] = (double)bf16_bits_to_f32(p[i] & 0xFFF0);"),
+    "e4m3_bias": ("ldexp((double)(8 + m), ex - 10)", "ldexp((double)(8 + m), ex - 11)"),
+    "e4m3_subnormal_step": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "nvfp4_block_32": ("scales[r * (K / 16) + j / 16]", "scales[r * (K / 16) + j / 32]"),
+    "nvfp4_rows_block_32": ("row[j] = nvfp4_value(code, sc[j / 16], gscale);", "row[j] = nvfp4_value(code, sc[j / 32], gscale);"),
+    "nvfp4_tensor_scale_dropped": ("return m * e4m3_value(scale) * (double)gscale;", "return m * e4m3_value(scale);"),
 }
 
 

@@ -104,6 +104,102 @@ def test_mxfp4_nibble_order_and_scale_blocks():
 
 
 # ---------------------------------------------------------------------------------------------
+# NVFP4 dequantisation: E2M1 x FP8 E4M3 block scale (16 elements) x fp32 tensor scale
+# ---------------------------------------------------------------------------------------------
+def _torch_e4m3(b: np.ndarray) -> np.ndarray:
+    """Independent decode of E4M3 bytes: torch's float8_e4m3fn dtype."""
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy()
+
+
+def test_e4m3_landmarks_of_the_ocp_fp8_spec():
+    with open(os.path.join(GOLDEN, "e4m3_ocp_fp8_v1.txt")) as fh:
+        rows = [l.split() for l in fh if l.strip() and not l.startswith("#")]
+    b = np.array([int(r[0], 16) for r in rows], np.uint8)
+    got = oracle.e4m3_to_f32(b)
+    for (hx, v), g in zip(rows, got):
+        want = float(v)
+        if math.isnan(want):
+            assert math.isnan(g), hx
+        else:
+            assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), (hx, g, want)
+
+
+def test_e4m3_all_bytes_against_torch_float8():
+    b = np.arange(256, dtype=np.uint8)
+    got, want = oracle.e4m3_to_f32(b), _torch_e4m3(b)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok].view(np.uint32), want[ok].view(np.uint32))
+
+
+def test_nvfp4_dequant_exhaustive_codes_by_scales():
+    """All 16 codes x 256 scale bytes x a non-power-of-two tensor scale, bit for bit: the exact
+    product E2M1 * E4M3 * g rounded once to fp32 (NaN for the E4M3 NaN bytes)."""
+    gold = _golden_e2m1()
+    g = 0.3
+    codes = np.array(list(range(16)), np.uint8)             # 16 elements: one scale block
+    packed = np.tile(_pack(codes), (256, 1))
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    out = oracle.nvfp4_dequant(packed, scales, g)
+    sv = _torch_e4m3(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    g32 = float(np.float32(g))
+    for s in range(256):
+        for j in range(16):
+            exact = Fraction(gold[j]) * Fraction(float(sv[s])) * Fraction(g32) if not np.isnan(sv[s]) else None
+            if exact is None:
+                assert np.isnan(out[s, j]), (s, j)
+                continue
+            want = np.float32(float(exact))  # exact rational -> nearest double -> fp32 (no double rounding: < 53 bits)
+            assert out[s, j].view(np.uint32) == want.view(np.uint32) or (want == 0 and out[s, j] == 0), (s, j, out[s, j], want)
+
+
+def test_nvfp4_scale_blocks_of_16_and_nibble_order():
+    row = np.zeros(16, np.uint8)
+    row[0] = 0x21  # element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    out = oracle.nvfp4_dequant(row[None, :], np.array([[0x38, 0x38]], np.uint8), 1.0)[0]
+    assert out[0] == 0.5 and out[1] == 1.0 and np.all(out[2:] == 0)
+    codes = np.full(32, 2, np.uint8)  # all 1.0; scales 0.5 (0x30) then 2.0 (0x40)
+    out = oracle.nvfp4_dequant(_pack(codes)[None, :], np.array([[0x30, 0x40]], np.uint8), 1.0)[0]
+    assert np.all(out[:16] == 0.5) and np.all(out[16:] == 2.0)
+
+
+def test_nvfp4_expert_ffn_matches_numpy_on_dequantised_weights():
+    """The oracle's NVFP4 grouped FFN equals a float64 numpy SwiGLU over weights decoded
+    independently (golden E2M1 table x torch's E4M3 x tensor scale)."""
+    s = mi.LayerSpec("nv_small", 5, 64, 32, 4, 2, 1, 32, "bf16", "nvfp4", 1.0, 0.0, 0.05,
+                     scale_lo=mi.NVFP4_SCALE_LO, scale_hi=mi.NVFP4_SCALE_HI, seed=71)
+    x = mi.host_x(s)
+    w = mi.host_experts(s)
+    sh = mi.host_experts(s, shared=True)
+    gold = _golden_e2m1()
+    table = np.array([gold[c] for c in range(16)], np.float64)
+
+    def deq(codes, sc, g):
+        c = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(*codes.shape[:-1], -1)
+        sv = _torch_e4m3(sc).astype(np.float64)
+        return table[c] * np.repeat(sv, 16, axis=-1) * float(np.float32(g))
+
+    xf = bf16_to_f64(x)
+    l32, _ = oracle.router_logits(s, x, *mi.host_router(s))
+    idx, _ = oracle.topk(s, l32)
+    _, off, perm, _ = oracle.permute(s, idx)
+    ys, ysh = oracle.grouped_ffn(s, x, perm, off, w, sh)
+    W13 = deq(w["w13"], w["w13_scale"], w["w13_gscale"])
+    W2 = deq(w["w2"], w["w2_scale"], w["w2_gscale"])
+    for i in range(s.T * s.k):
+        e = int(np.searchsorted(off, i, side="right") - 1)
+        want = _np_ffn(W13[e], W2[e], xf[perm[i] // s.k], s.f)
+        np.testing.assert_allclose(ys[i], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+    S13 = deq(sh["w13"], sh["w13_scale"], sh["w13_gscale"])[0]
+    S2 = deq(sh["w2"], sh["w2_scale"], sh["w2_gscale"])[0]
+    for t in range(s.T):
+        want = _np_ffn(S13, S2, xf[t], s.f_shared)
+        np.testing.assert_allclose(ysh[t], want, rtol=1e-12, atol=1e-14 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------------------------
 # Top-k selection and gates
 # ---------------------------------------------------------------------------------------------
 class _S:
