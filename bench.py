@@ -45,6 +45,8 @@ WORKLOADS = {
     "c3_decode_T8": ("c3", 8, 4, "decode, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c3_decode_T32": ("c3", 32, 4, "decode, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=32"),
     "c3_prefill": ("c3", 8192, 1, "prefill, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=8192"),
+    "c3nv_decode_T1": ("c3nv", 1, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=1"),
+    "c3nv_decode_T8": ("c3nv", 8, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c4_stack": ("c4", 1, 1, "43-layer MXFP4 stack of the E=256 top-6 layer, T=1, RMS-norm residual"),
 }
 HEADLINE = "c1_decode_T1"
@@ -101,9 +103,10 @@ def copy_calibration():
 def expert_bytes(s, f=None):
     """Bytes of one expert's weights (w13 + w2), split (up, down)."""
     f = s.f if f is None else f
-    if s.wt == "mxfp4":
-        up = 2 * f * s.d // 2 + 2 * f * s.d // 32
-        down = s.d * f // 2 + s.d * f // 32
+    if s.wt in ("mxfp4", "nvfp4"):
+        blk = 32 if s.wt == "mxfp4" else 16  # elements per scale byte
+        up = 2 * f * s.d // 2 + 2 * f * s.d // blk
+        down = s.d * f // 2 + s.d * f // blk
     else:
         eb = 4 if s.wt == "f32" else 2
         up, down = 2 * f * s.d * eb, s.d * f * eb

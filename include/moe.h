@@ -47,6 +47,14 @@
  *     byte i, E2M1 per the OCP Microscaling v1.0 specification; scales
  *     [.., N, K/32] uint8 E8M0 (2^(s-127); 0xFF = NaN), one per 32
  *     consecutive elements of a row.
+ *   NVFP4 weights (the 4-bit build named in the aihot.vn FreeToken article,
+ *     "Flags", and the dothoosh.com FreeToken article, "Editorial"; the pages
+ *     give no layout, so this library takes NVIDIA's published one): codes as
+ *     for MXFP4; scales [.., N, K/16] uint8 OCP FP8 E4M3 (no infinities;
+ *     0x7F/0xFF = NaN), one per 16 consecutive elements; one fp32 scale per
+ *     tensor (moe_weights.*_gscale).  Element value = E2M1 * E4M3 * gscale.
+ *     d_model, d_ff and shared_d_ff must be multiples of 32 for both 4-bit
+ *     formats.  NVFP4 weights take the grouped-GEMV kernels at every T.
  *   topk_idx [T, k] int32, topk_w [T, k] f32, logits [T, E] f32
  *   counts [E], offsets [E+1], perm [T*k], inv_perm [T*k] int32
  *   y_sorted [T*k, d_model], y_shared [T, d_model]  act dtype
@@ -69,7 +77,7 @@ typedef enum {
     MOE_ERR_HIP = -4           /* a HIP launch reported an error */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_NVFP4 = 3 } moe_dtype;
 
 enum {
     MOE_F_NO_RENORM = 1u << 0,   /* gates = full-softmax probabilities at the selected experts */
@@ -91,19 +99,20 @@ typedef struct {
     int32_t n_shared;     /* 0 or 1 always-on shared expert (weight 1, no gate) */
     int32_t shared_d_ff;
     int32_t act_dtype;    /* moe_dtype: MOE_F32 or MOE_BF16 */
-    int32_t weight_dtype; /* moe_dtype: MOE_F32 (with f32 act), MOE_BF16 or MOE_MXFP4 (with bf16 act) */
+    int32_t weight_dtype; /* moe_dtype: MOE_F32 (with f32 act); MOE_BF16, MOE_MXFP4 or MOE_NVFP4 (bf16 act) */
     uint32_t flags;       /* MOE_F_* */
 } moe_shape;
 
 typedef struct {
-    const void* w13;           /* [E, 2f, d] (MXFP4: codes [E, 2f, d/2]) */
-    const void* w2;            /* [E, d, f]  (MXFP4: codes [E, d, f/2]) */
-    const uint8_t* w13_scale;  /* MXFP4 only: [E, 2f, d/32] */
-    const uint8_t* w2_scale;   /* MXFP4 only: [E, d, f/32] */
+    const void* w13;           /* [E, 2f, d] (MXFP4/NVFP4: codes [E, 2f, d/2]) */
+    const void* w2;            /* [E, d, f]  (MXFP4/NVFP4: codes [E, d, f/2]) */
+    const uint8_t* w13_scale;  /* MXFP4: [E, 2f, d/32]; NVFP4: [E, 2f, d/16]; else unused */
+    const uint8_t* w2_scale;   /* MXFP4: [E, d, f/32];  NVFP4: [E, d, f/16];  else unused */
     const void* s13;           /* shared expert (n_shared = 1), else NULL */
     const void* s2;
     const uint8_t* s13_scale;
     const uint8_t* s2_scale;
+    float w13_gscale, w2_gscale, s13_gscale, s2_gscale; /* NVFP4 only: per-tensor fp32 scales */
 } moe_weights;
 
 /* Bytes of device workspace the calls below need for this shape (0 on an invalid shape).
@@ -175,6 +184,12 @@ int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const 
    NaN for s = 0xFF; codes [rows, K/2], scales [rows, K/32]; K % 32 == 0. */
 int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out,
                       void* stream);
+
+/* NVFP4 -> f32 dequantisation: out[r*K + j] = E2M1(code) * E4M3(scales[r*(K/16) + j/16])
+   * gscale, rounded once to f32 (NaN for a NaN scale); codes [rows, K/2], scales
+   [rows, K/16]; K % 32 == 0.  MOE_ERR_INVALID_ARG otherwise. */
+int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, int64_t rows, int64_t K,
+                      float* out, void* stream);
 
 /* Timing aid for benchmarks: while set, every launch of the given kernel class carries
    ev_start / ev_stop on its own dispatch (hipExtLaunchKernel), so the events hold that

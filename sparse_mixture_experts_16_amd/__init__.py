@@ -21,14 +21,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_NVFP4 = 0, 1, 2, 3
 F_NO_RENORM, F_ACCUMULATE, F_FORCE_GEMV, F_FORCE_GEMM = 1 << 0, 1 << 1, 1 << 3, 1 << 4
 MAX_EXPERTS, MAX_TOPK = 1024, 64
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4, "nvfp4": MOE_NVFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_masked", "moe_stack_forward", "moe_mxfp4_dequant",
-           "moe_profile_kernel"]
+           "moe_nvfp4_dequant", "moe_profile_kernel"]
 KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
 
 
@@ -40,7 +40,8 @@ class Shape(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w13", "w2", "w13_scale", "w2_scale", "s13", "s2", "s13_scale", "s2_scale")]
+    _fields_ = ([(n, ctypes.c_void_p) for n in ("w13", "w2", "w13_scale", "w2_scale", "s13", "s2", "s13_scale", "s2_scale")]
+                + [(n, ctypes.c_float) for n in ("w13_gscale", "w2_gscale", "s13_gscale", "s2_gscale")])
 
 
 if not os.path.exists(LIB_PATH):
@@ -60,6 +61,7 @@ _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, 
 _lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+_lib.moe_nvfp4_dequant.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp]
 _lib.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
 for _n in EXPORTS[2:]:
     getattr(_lib, _n).restype = ctypes.c_int
@@ -124,9 +126,12 @@ def make_weights(w: dict, shared: Optional[dict] = None) -> Weights:
     W = Weights()
     W.w13, W.w2 = _ptr(w["w13"]), _ptr(w["w2"])
     W.w13_scale, W.w2_scale = _ptr(w.get("w13_scale")), _ptr(w.get("w2_scale"))
+    W.w13_gscale, W.w2_gscale = float(w.get("w13_gscale", 1.0)), float(w.get("w2_gscale", 1.0))
+    W.s13_gscale = W.s2_gscale = 1.0
     if shared is not None:
         W.s13, W.s2 = _ptr(shared["w13"]), _ptr(shared["w2"])
         W.s13_scale, W.s2_scale = _ptr(shared.get("w13_scale")), _ptr(shared.get("w2_scale"))
+        W.s13_gscale, W.s2_gscale = float(shared.get("w13_gscale", 1.0)), float(shared.get("w2_gscale", 1.0))
     return W
 
 
@@ -196,6 +201,13 @@ def mxfp4_dequant(codes, scales, out, stream=None):
     rows = codes.numel() // half_k
     _check(_lib.moe_mxfp4_dequant(_ptr(codes), _ptr(scales), rows, 2 * half_k, _ptr(out), _stream(stream)),
            "moe_mxfp4_dequant")
+
+
+def nvfp4_dequant(codes, scales, gscale, out, stream=None):
+    half_k = codes.shape[-1]
+    rows = codes.numel() // half_k
+    _check(_lib.moe_nvfp4_dequant(_ptr(codes), _ptr(scales), float(gscale), rows, 2 * half_k, _ptr(out),
+                                  _stream(stream)), "moe_nvfp4_dequant")
 
 
 def profile_kernel(kernel: int, ev_start=None, ev_stop=None):

@@ -73,8 +73,9 @@ int check_shape(const moe_shape* s) {
     if (s->n_shared < 0 || s->n_shared > 1) return MOE_ERR_INVALID_ARG;
     if (s->n_shared == 1 && s->shared_d_ff < 1) return MOE_ERR_INVALID_ARG;
     const bool pair_ok = (s->act_dtype == MOE_F32 && s->weight_dtype == MOE_F32) ||
-                         (s->act_dtype == MOE_BF16 && (s->weight_dtype == MOE_BF16 || s->weight_dtype == MOE_MXFP4));
-    if (s->act_dtype < MOE_F32 || s->act_dtype > MOE_BF16 || s->weight_dtype < MOE_F32 || s->weight_dtype > MOE_MXFP4)
+                         (s->act_dtype == MOE_BF16 && (s->weight_dtype == MOE_BF16 || s->weight_dtype == MOE_MXFP4 ||
+                                                       s->weight_dtype == MOE_NVFP4));
+    if (s->act_dtype < MOE_F32 || s->act_dtype > MOE_BF16 || s->weight_dtype < MOE_F32 || s->weight_dtype > MOE_NVFP4)
         return MOE_ERR_INVALID_ARG;
     if (!pair_ok) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts > MOE_MAX_EXPERTS || s->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
@@ -82,7 +83,7 @@ int check_shape(const moe_shape* s) {
     // 16-byte vector loads along every contiguous dimension.
     const int vec = s->act_dtype == MOE_F32 ? 4 : 8;
     const int fs = s->n_shared ? s->shared_d_ff : 32 * vec;  // no shared expert: nothing to check
-    if (s->weight_dtype == MOE_MXFP4) {
+    if (s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4) {  // 32-element code chunks
         if (s->d_model % 32 || s->d_ff % 32 || fs % 32) return MOE_ERR_INVALID_ARG;
     } else {
         if (s->d_model % vec || s->d_ff % vec || fs % vec) return MOE_ERR_INVALID_ARG;
@@ -98,7 +99,9 @@ bool gemm_shape_ok(const moe_shape* s) {
     // K steps of 32; MXFP4 scales move four 32-element blocks (one dword) at a time
     const int q = s->weight_dtype == MOE_MXFP4 ? 128 : 64;
     const int fs = s->n_shared ? s->shared_d_ff : q;
-    return s->act_dtype == MOE_BF16 && s->d_model % q == 0 && s->d_ff % q == 0 && fs % q == 0;
+    // NVFP4 weights take the grouped-GEMV kernels at every T
+    return s->act_dtype == MOE_BF16 && s->weight_dtype != MOE_NVFP4 && s->d_model % q == 0 && s->d_ff % q == 0 &&
+           fs % q == 0;
 }
 
 // Which FFN kernels run: grouped GEMV (decode) or grouped MFMA GEMM (prefill).
@@ -112,10 +115,11 @@ bool use_gemm(const moe_shape* s) {
 int check_weights(const moe_shape* s, const moe_weights* w) {
     if (!w || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w->w13) || !aligned16(w->w2)) return MOE_ERR_INVALID_ARG;
-    if (s->weight_dtype == MOE_MXFP4 && (!ptr_ok(w->w13_scale) || !ptr_ok(w->w2_scale))) return MOE_ERR_INVALID_ARG;
+    const bool scaled = s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4;
+    if (scaled && (!ptr_ok(w->w13_scale) || !ptr_ok(w->w2_scale))) return MOE_ERR_INVALID_ARG;
     if (s->n_shared) {
         if (!w->s13 || !w->s2 || !aligned16(w->s13) || !aligned16(w->s2)) return MOE_ERR_INVALID_ARG;
-        if (s->weight_dtype == MOE_MXFP4 && (!ptr_ok(w->s13_scale) || !ptr_ok(w->s2_scale))) return MOE_ERR_INVALID_ARG;
+        if (scaled && (!ptr_ok(w->s13_scale) || !ptr_ok(w->s2_scale))) return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
 }
@@ -133,6 +137,15 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 int g_prof_kernel = -1;
 static_assert(MOE_KERNEL_FFN_UP == PROF_FFN_UP && MOE_KERNEL_FFN_DOWN == PROF_FFN_DOWN, "kernel classes");
+
+// NVFP4 tensor scales {routed gate/up, routed down, shared gate/up, shared down}; 1 otherwise.
+void tensor_scales(const moe_shape* s, const moe_weights* w, float g[4]) {
+    const bool nv = s->weight_dtype == MOE_NVFP4;
+    g[0] = nv ? w->w13_gscale : 1.0f;
+    g[1] = nv ? w->w2_gscale : 1.0f;
+    g[2] = nv ? w->s13_gscale : 1.0f;
+    g[3] = nv ? w->s2_gscale : 1.0f;
+}
 
 // Routed + shared FFNs given ws-resident permute results; writes either the fused combine into
 // `out` (decode, T <= 64) or y_sorted / y_shared.
@@ -152,11 +165,13 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
         return MOE_OK;
     }
     float* a = at<float>(ws, L.a);
+    float gs[4];
+    tensor_scales(s, w, gs);
     MOE_TRY(launch_gemv_w13(wt, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13, w->s13_scale, a,
-                            s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, st));
+                            s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, gs[0], gs[2], st));
     MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
                                   w->s2, w->s2_scale, y_sorted, y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
-                                  s->n_experts, s->n_shared, st));
+                                  s->n_experts, s->n_shared, gs[1], gs[3], st));
     return MOE_OK;
 }
 
@@ -166,6 +181,8 @@ int run_decode(const moe_shape* s, const void* x, const void* w_router, const fl
                void* out, int out_dtype, bool accumulate, int32_t* idx_out, bool prenorm, void* ws, const Layout& L,
                const uint8_t* mask, hipStream_t st) {
     void* xn = at<void>(ws, L.xn);
+    float gs[4];
+    tensor_scales(s, w, gs);
     MOE_TRY(launch_dec_logits(s->act_dtype, x, w_router, b, at<float>(ws, L.logits), xn, s->T, s->d_model,
                               s->n_experts, prenorm, st));
     hipError_t e = launch_dec_ffn(
@@ -173,7 +190,7 @@ int run_decode(const moe_shape* s, const void* x, const void* w_router, const fl
         at<float>(ws, L.topk_w), idx_out, at<int32_t>(ws, L.meta), at<int4>(ws, L.slots), at<float>(ws, L.pos_gate),
         (s->flags & MOE_F_NO_RENORM) != 0, w->w13, w->w13_scale, w->s13, w->s13_scale, w->w2, w->w2_scale, w->s2,
         w->s2_scale, at<float>(ws, L.a), out, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
-        s->n_experts, s->n_shared, accumulate, mask, st);
+        s->n_experts, s->n_shared, accumulate, mask, gs, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -209,11 +226,13 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
     if (!gemm && T <= 64 && !mask) {
         float* a = at<float>(ws, L.a);
+        float gs[4];
+        tensor_scales(s, w, gs);
         MOE_TRY(launch_gemv_w13(s->weight_dtype, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13,
-                                w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, st));
+                                w->s13_scale, a, T, d, s->d_ff, fs, k, E, s->n_shared, gs[0], gs[2], st));
         MOE_TRY(launch_gemv_w2_combine(s->weight_dtype, out_dtype == MOE_BF16, a, perm, offsets, act_list, meta, g,
                                        w->w2, w->w2_scale, w->s2, w->s2_scale, out, T, d, s->d_ff, fs, k,
-                                       s->n_shared, accumulate, st));
+                                       s->n_shared, accumulate, gs[1], gs[3], st));
         return MOE_OK;
     }
     void* y = at<void>(ws, L.y);
@@ -409,6 +428,15 @@ int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,
     if (rows == 0 || K == 0) return MOE_OK;
     if (!ptr_ok(codes) || !scales || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
     MOE_TRY(launch_mxfp4_dequant(codes, scales, out, rows, K, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, int64_t rows, int64_t K, float* out,
+                      void* stream) {
+    if (rows < 0 || K < 0 || K % 32) return MOE_ERR_INVALID_ARG;
+    if (rows == 0 || K == 0) return MOE_OK;
+    if (!ptr_ok(codes) || !scales || ((uintptr_t)scales & 1) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_nvfp4_dequant(codes, scales, gscale, out, rows, K, (hipStream_t)stream));
     return MOE_OK;
 }
 

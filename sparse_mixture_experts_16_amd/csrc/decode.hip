@@ -342,7 +342,8 @@ struct DecFfnArgs {
     float* a;               // [P + T, fmax] fp32
     void* out;              // [T, d] (f32 or bf16)
     int T, d, f, fs, fmax, k, accumulate;
-    int slot_bound;          // routed slots can number at most min(T*k, E), plus the shared one
+    int slot_bound;
+    float g13, g2, gs13, gs2;   // NVFP4 tensor scales (1 otherwise): routed / shared gate-up, down          // routed slots can number at most min(T*k, E), plus the shared one
 };
 
 template <int WT> struct DecAct { using T = uint16_t; };
@@ -373,7 +374,7 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
     const int r_items = rs.n_routed * ngr;
     const int n_items = r_items + (rs.n_slots > rs.n_routed ? ngs : 0);
     const int NC = p.d / EC;
-    const int64_t rb = row_bytes(WT, p.d), sb = p.d / 32;
+    const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
     const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
     const int NWB = blockDim.x / MOE_WAVE;
     for (int item = blockIdx.x * NWB + wave_id(); item < n_items; item += gridDim.x * NWB) {
@@ -384,7 +385,8 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
         const int fc = sh ? p.fs : p.f;
         const int j0 = jg * R;
         const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)S.x * 2 * p.f * rb;
-        const uint8_t* sbp = (WT == 2) ? (sh ? p.s13s : p.w13s + (int64_t)S.x * 2 * p.f * sb) : nullptr;
+        const uint8_t* sbp = (WT >= 2) ? (sh ? p.s13s : p.w13s + (int64_t)S.x * 2 * p.f * sb) : nullptr;
+        const float gsc = sh ? p.gs13 : p.g13;
         // the slot's tokens in ascending order, 4 at a time; one K step covers a row in the
         // configured shapes, otherwise rows are re-streamed per group of tokens (cache hits)
         uint32_t mask = (uint32_t)S.w;
@@ -449,7 +451,7 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
                 if (q >= nq) break;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float g = wave_sum(ag[r][q]), u = wave_sum(au[r][q]);
+                    const float g = wave_sum(ag[r][q]) * gsc, u = wave_sum(au[r][q]) * gsc;
                     const int j = j0 + r;
                     if (lane == 0 && j < fc) p.a[(int64_t)(pos + q) * p.fmax + j] = g / (1.0f + expf(-g)) * u;
                 }
@@ -486,9 +488,10 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
         const bool sh = S.x == p.rt.E;
         const int fc = sh ? p.fs : p.f;
         const int NC = fc / EC;
-        const int64_t rb = row_bytes(WT, fc), sbb = fc / 32;
+        const int64_t rb = row_bytes(WT, fc), sbb = scale_row_bytes(WT, fc);
         const uint8_t* base = sh ? p.s2 : p.w2 + (int64_t)S.x * p.d * rb;
-        const uint8_t* sbase = (WT == 2) ? (sh ? p.s2s : p.w2s + (int64_t)S.x * p.d * sbb) : nullptr;
+        const uint8_t* sbase = (WT >= 2) ? (sh ? p.s2s : p.w2s + (int64_t)S.x * p.d * sbb) : nullptr;
+        const float gsc = sh ? p.gs2 : p.g2;
         for (int c0 = 0; c0 < NC; c0 += MOE_WAVE * U) {
             W w[R][U];
 #pragma unroll
@@ -519,7 +522,7 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float y = wave_sum(acc[r]);
+                    const float y = wave_sum(acc[r]) * gsc;
                     if (lane == t) o[r] = fmaf(g, y, o[r]);
                 }
             }
@@ -581,13 +584,13 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
                           int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate,
-                          const uint8_t* mask, hipStream_t st) {
+                          const uint8_t* mask, const float* gsc, hipStream_t st) {
     const int fmax = (n_shared && fs > f) ? fs : f;
     DecRouteIO rt{logits, topk_idx, topk_w, idx_out, meta, slots, pos_gate, T, E, k, n_shared, no_renorm ? 1 : 0, mask};
     const int64_t max_slots = (int64_t)(T * k < E ? T * k : E);
     DecFfnArgs p{x, rt, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, (const uint8_t*)w2, w2s,
                  (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0,
-                 (int)max_slots + n_shared};
+                 (int)max_slots + n_shared, gsc[0], gsc[1], gsc[2], gsc[3]};
     const size_t lds = dec_route_lds_bytes(T, E, k);
 #define MOE_DW13(WTV, RV, UV)                                                                                    \
     do {                                                                                                         \
@@ -597,7 +600,8 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     // about 8 16-byte loads per lane in flight per item (HBM streams best at 4-8 per lane)
     if (wt == 0) MOE_DW13(0, 2, 1);
     else if (wt == 1) MOE_DW13(1, 1, 4);
-    else MOE_DW13(2, 2, 2);
+    else if (wt == 2) MOE_DW13(2, 2, 2);
+    else MOE_DW13(3, 2, 2);
 #undef MOE_DW13
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -609,7 +613,8 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     } while (0)
     if (wt == 0) MOE_DW2(0, 4, 1);
     else if (wt == 1) MOE_DW2(1, 4, 2);
-    else MOE_DW2(2, 16, 1);
+    else if (wt == 2) MOE_DW2(2, 16, 1);
+    else MOE_DW2(3, 16, 1);
 #undef MOE_DW2
     return hipGetLastError();
 }

@@ -33,6 +33,7 @@ struct GemvW13Args {
     const uint8_t* s13s;
     float* a;                   // routed [P, f] then shared [T, fs]
     int T, d, f, fs, k, n_shared;
+    float g_r, g_s;             // NVFP4 tensor scales of the routed / shared gate-up weights (1 otherwise)
 };
 
 template <int WT> struct ActOf { using T = uint16_t; };
@@ -57,7 +58,7 @@ __global__ void __launch_bounds__(256) gemv_w13(GemvW13Args p) {
     const int ngs = p.n_shared ? (p.fs + R - 1) / R : 0;
     const int n_items = n_act * ngr + ngs;
     const int NC = p.d / EC;  // chunks per row
-    const int64_t rb = row_bytes(WT, p.d), sb = p.d / 32;
+    const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
     const int P = p.T * p.k;
     const int wave_global = blockIdx.x * (blockDim.x / MOE_WAVE) + wave_id();
     const int n_waves = gridDim.x * (blockDim.x / MOE_WAVE);
@@ -68,6 +69,7 @@ __global__ void __launch_bounds__(256) gemv_w13(GemvW13Args p) {
         int fcur, j0, pos0, npos;
         float* abase;
         bool routed = item < n_act * ngr;
+        const float gsc = routed ? p.g_r : p.g_s;
         if (routed) {
             const int e = p.act_list[item / ngr];
             j0 = (item % ngr) * R;
@@ -134,8 +136,8 @@ __global__ void __launch_bounds__(256) gemv_w13(GemvW13Args p) {
             for (int q = 0; q < PG; ++q) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float g = wave_sum(ag[r][q]);
-                    const float u = wave_sum(au[r][q]);
+                    const float g = wave_sum(ag[r][q]) * gsc;
+                    const float u = wave_sum(au[r][q]) * gsc;
                     const int j = j0 + r;
                     if (lane == 0 && tok[q] >= 0 && j < fcur) {
                         const int pos = pos0 + q0 + q;
@@ -162,6 +164,7 @@ struct GemvW2Args {
     void* y_shared;             // sorted variant: [T, d] act dtype, or NULL
     int T, d, f, fs, k, n_shared;
     int accumulate;             // combine: out += result
+    float g_r, g_s;             // NVFP4 tensor scales of the routed / shared down weights (1 otherwise)
 };
 
 template <int WT>
@@ -199,7 +202,8 @@ __global__ void __launch_bounds__(256) gemv_w2_combine(GemvW2Args p) {
             const bool routed = sl < n_act;
             const int fcur = routed ? p.f : p.fs;
             const int NC = fcur / EC;
-            const int64_t rb = row_bytes(WT, fcur), sb = fcur / 32;
+            const int64_t rb = row_bytes(WT, fcur), sb = scale_row_bytes(WT, fcur);
+            const float gsc = routed ? p.g_r : p.g_s;
             const uint8_t* base;
             const uint8_t* sbase;
             int pos0, npos;
@@ -248,7 +252,7 @@ __global__ void __launch_bounds__(256) gemv_w2_combine(GemvW2Args p) {
                     const float g = routed ? p.topk_w[pr] : 1.0f;
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float y = wave_sum(acc[r]);
+                        const float y = wave_sum(acc[r]) * gsc;
                         // Multi-step K (f > 64*U*EC) accumulates g*partial; exact order differs
                         // only in fp32 rounding.
                         if (lane == t) o[r] = fmaf(g, y, o[r]);
@@ -296,7 +300,8 @@ __global__ void __launch_bounds__(256) gemv_w2_sorted(GemvW2Args p) {
         const bool routed = sl < n_act;
         const int fcur = routed ? p.f : p.fs;
         const int NC = fcur / EC;
-        const int64_t rb = row_bytes(WT, fcur), sb = fcur / 32;
+        const int64_t rb = row_bytes(WT, fcur), sb = scale_row_bytes(WT, fcur);
+        const float gsc = routed ? p.g_r : p.g_s;
         const uint8_t* base;
         const uint8_t* sbase;
         int pos0, npos;
@@ -341,7 +346,7 @@ __global__ void __launch_bounds__(256) gemv_w2_sorted(GemvW2Args p) {
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float y = wave_sum(acc[r]);
+                const float y = wave_sum(acc[r]) * gsc;
                 const int i = i0 + r;
                 if (lane == 0 && i < p.d && ybase) {
                     const int64_t off = (int64_t)pos * p.d + i;
@@ -366,9 +371,9 @@ static int gemv_grid(int64_t max_items, int waves_per_block) {
 hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int32_t* offsets,
                            const int32_t* act_list, const int32_t* meta, const void* w13, const uint8_t* w13s,
                            const void* s13, const uint8_t* s13s, float* a, int T, int d, int f, int fs, int k,
-                           int E, int n_shared, hipStream_t st) {
+                           int E, int n_shared, float g_r, float g_s, hipStream_t st) {
     GemvW13Args p{x, perm, offsets, act_list, meta, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s,
-                  a, T, d, f, fs, k, n_shared};
+                  a, T, d, f, fs, k, n_shared, g_r, g_s};
     const int64_t max_act = (int64_t)(T * k < E ? T * k : E);
     if (wt == 0) {
         constexpr int R = 1;
@@ -378,10 +383,14 @@ hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int
         constexpr int R = 1;
         int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
         MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<1, R, 4, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
-    } else {
+    } else if (wt == 2) {
         constexpr int R = 2;
         int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
         MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<2, R, 2, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
+    } else {
+        constexpr int R = 2;
+        int64_t items = max_act * ((f + R - 1) / R) + (n_shared ? (fs + R - 1) / R : 0);
+        MOE_LAUNCH(PROF_FFN_UP, (gemv_w13<3, R, 2, 4>), dim3(gemv_grid(items, 4)), dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }
@@ -389,9 +398,10 @@ hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int
 hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* act_list, const int32_t* meta, const float* topk_w, const void* w2,
                                   const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* out, int T, int d,
-                                  int f, int fs, int k, int n_shared, bool accumulate, hipStream_t st) {
+                                  int f, int fs, int k, int n_shared, bool accumulate, float g_r, float g_s,
+                                  hipStream_t st) {
     GemvW2Args p{a, perm, offsets, act_list, meta, topk_w, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s,
-                 out, nullptr, T, d, f, fs, k, n_shared, accumulate ? 1 : 0};
+                 out, nullptr, T, d, f, fs, k, n_shared, accumulate ? 1 : 0, g_r, g_s};
 #define MOE_W2C(WTV, RV, UV)                                                                              \
     do {                                                                                                  \
         int64_t items = (d + RV - 1) / RV;                                                                \
@@ -402,7 +412,8 @@ hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const i
     } while (0)
     if (wt == 0) MOE_W2C(0, 1, 2);
     else if (wt == 1) MOE_W2C(1, 2, 2);
-    else MOE_W2C(2, 4, 1);
+    else if (wt == 2) MOE_W2C(2, 4, 1);
+    else MOE_W2C(3, 4, 1);
 #undef MOE_W2C
     return hipGetLastError();
 }
@@ -410,9 +421,9 @@ hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const i
 hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
                                  const int32_t* act_list, const int32_t* meta, const void* w2, const uint8_t* w2s,
                                  const void* s2, const uint8_t* s2s, void* y, void* y_shared, int T, int d, int f,
-                                 int fs, int k, int E, int n_shared, hipStream_t st) {
+                                 int fs, int k, int E, int n_shared, float g_r, float g_s, hipStream_t st) {
     GemvW2Args p{a, perm, offsets, act_list, meta, nullptr, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s,
-                 y, y_shared, T, d, f, fs, k, n_shared, 0};
+                 y, y_shared, T, d, f, fs, k, n_shared, 0, g_r, g_s};
     const int64_t max_act = (int64_t)(T * k < E ? T * k : E) + (n_shared ? 1 : 0);
 #define MOE_W2S(WTV, RV, UV)                                                                              \
     do {                                                                                                  \
@@ -424,7 +435,8 @@ hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int3
     } while (0)
     if (wt == 0) MOE_W2S(0, 1, 2);
     else if (wt == 1) MOE_W2S(1, 2, 2);
-    else MOE_W2S(2, 4, 1);
+    else if (wt == 2) MOE_W2S(2, 4, 1);
+    else MOE_W2S(3, 4, 1);
 #undef MOE_W2S
     return hipGetLastError();
 }

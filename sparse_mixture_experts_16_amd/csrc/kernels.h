@@ -51,15 +51,16 @@ hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int bm, int
 hipError_t launch_gemv_w13(int wt, const void* x, const int32_t* perm, const int32_t* offsets,
                            const int32_t* act_list, const int32_t* meta, const void* w13, const uint8_t* w13s,
                            const void* s13, const uint8_t* s13s, float* a, int T, int d, int f, int fs, int k,
-                           int E, int n_shared, hipStream_t st);
+                           int E, int n_shared, float g_r, float g_s, hipStream_t st);
 hipError_t launch_gemv_w2_combine(int wt, bool out_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
                                   const int32_t* act_list, const int32_t* meta, const float* topk_w, const void* w2,
                                   const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* out, int T, int d,
-                                  int f, int fs, int k, int n_shared, bool accumulate, hipStream_t st);
+                                  int f, int fs, int k, int n_shared, bool accumulate, float g_r, float g_s,
+                                  hipStream_t st);
 hipError_t launch_gemv_w2_sorted(int wt, bool y_bf16, const float* a, const int32_t* perm, const int32_t* offsets,
                                  const int32_t* act_list, const int32_t* meta, const void* w2, const uint8_t* w2s,
                                  const void* s2, const uint8_t* s2s, void* y, void* y_shared, int T, int d, int f,
-                                 int fs, int k, int E, int n_shared, hipStream_t st);
+                                 int fs, int k, int E, int n_shared, float g_r, float g_s, hipStream_t st);
 
 // Prefill grouped GEMM (MFMA).  a_bf16: routed [P, f] then shared [T, fs].
 // mask (nullable, E + 1 bytes): groups whose byte is 0 get no tiles.
@@ -82,7 +83,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           bool no_renorm, const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s,
                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, float* a, void* out,
                           int T, int d, int f, int fs, int k, int E, int n_shared, bool accumulate,
-                          const uint8_t* mask, hipStream_t st);
+                          const uint8_t* mask, const float* gsc, hipStream_t st);  // gsc: g13, g2, gs13, gs2
 
 // mask (nullable, E + 1 bytes; needs idx): terms of experts whose byte is 0 are left out.
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
@@ -90,6 +91,8 @@ hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32
                           const uint8_t* mask, int E, hipStream_t st);
 hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, float* out, int64_t rows, int64_t K,
                                 hipStream_t st);
+hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, float* out, int64_t rows,
+                                int64_t K, hipStream_t st);
 hipError_t launch_rmsnorm(int x_dtype, const float* h, void* x, int T, int d, float eps, hipStream_t st);
 
 }  // namespace moe

@@ -195,6 +195,41 @@ hipError_t launch_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, flo
     return hipGetLastError();
 }
 
+// NVFP4 -> f32: per 32-element chunk, the unit-scale converts give the exact E2M1 values, each
+// 16-element block's E4M3 scale multiplies them exactly, and the tensor scale rounds once.
+__global__ void __launch_bounds__(256) nvfp4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales, float gscale,
+                                                            float* __restrict__ out, int64_t n_chunks) {
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 v = reinterpret_cast<const uint4*>(codes)[c];
+        const uint32_t s2 = reinterpret_cast<const uint16_t*>(scales)[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float4* o = reinterpret_cast<float4*>(out + c * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float sb = e4m3_to_f32(q < 2 ? (s2 & 0xFFu) : (s2 >> 8));
+            f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 0);
+            f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 1);
+            f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 2);
+            f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 3);
+            o[2 * q] = make_float4((p0.x * sb) * gscale, (p0.y * sb) * gscale, (p1.x * sb) * gscale, (p1.y * sb) * gscale);
+            o[2 * q + 1] = make_float4((p2.x * sb) * gscale, (p2.y * sb) * gscale, (p3.x * sb) * gscale, (p3.y * sb) * gscale);
+        }
+    }
+}
+
+hipError_t launch_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, float* out, int64_t rows,
+                                int64_t K, hipStream_t st) {
+    const int64_t n_chunks = rows * (K / 32);
+    if (n_chunks == 0) return hipSuccess;
+    int64_t blocks = (n_chunks + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, scales, gscale, out,
+                       n_chunks);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------------
 // Residual stack glue: x = h / sqrt(mean(h^2) + eps), rounded to the activation dtype.
 // One workgroup per token.

@@ -138,8 +138,56 @@ template <> struct WChunk<2> {
     }
 };
 
+// ---------------------------------------------------------------- NVFP4 weights
+// OCP FP8 E4M3 (no infinities) -> fp32 from its bit fields: (1 + m/8) * 2^(e-7), subnormal
+// m/8 * 2^-6, NaN for e = 15 and m = 7.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+    return (b & 0x80u) ? -v : v;
+}
+
+// 32 E2M1 codes (16 bytes) and their two E4M3 block scales (one per 16 elements); the codes
+// expand exactly with the unit-scale converts and each block's partial sum takes its scale.
+// The tensor's fp32 scale is applied by the kernels to the finished row sums.
+template <> struct WChunk<3> {
+    static constexpr int EC = 32;
+    uint4 v;
+    uint32_t s;  // two scale bytes: block 0 in bits 0..7, block 1 in bits 8..15
+    __device__ __forceinline__ void load(const uint8_t* row, const uint8_t* srow, int c) {
+        v = reinterpret_cast<const uint4*>(row)[c];
+        s = reinterpret_cast<const uint16_t*>(srow)[c];
+    }
+    __device__ __forceinline__ void zero() {
+        v = make_uint4(0, 0, 0, 0);
+        s = 0x3838u;  // 1.0, 1.0
+    }
+    __device__ __forceinline__ float dot_bf16(const uint16_t* a, float acc) const {
+        const uint4* x = reinterpret_cast<const uint4*>(a);
+        float p0 = 0.0f, p1 = 0.0f;
+        p0 = WChunk<2>::word_bf16(v.x, 1.0f, x[0], p0);
+        p0 = WChunk<2>::word_bf16(v.y, 1.0f, x[1], p0);
+        p1 = WChunk<2>::word_bf16(v.z, 1.0f, x[2], p1);
+        p1 = WChunk<2>::word_bf16(v.w, 1.0f, x[3], p1);
+        return acc + p0 * e4m3_to_f32(s & 0xFFu) + p1 * e4m3_to_f32(s >> 8);
+    }
+    __device__ __forceinline__ float dot_f32(const float* a, float acc) const {
+        float p0 = 0.0f, p1 = 0.0f;
+        p0 = WChunk<2>::word_f32(v.x, 1.0f, a, p0);
+        p0 = WChunk<2>::word_f32(v.y, 1.0f, a + 8, p0);
+        p1 = WChunk<2>::word_f32(v.z, 1.0f, a + 16, p1);
+        p1 = WChunk<2>::word_f32(v.w, 1.0f, a + 24, p1);
+        return acc + p0 * e4m3_to_f32(s & 0xFFu) + p1 * e4m3_to_f32(s >> 8);
+    }
+};
+
 __host__ __device__ __forceinline__ int64_t row_bytes(int wt, int64_t K) {
     return wt == 0 ? K * 4 : (wt == 1 ? K * 2 : K / 2);
+}
+// Scale bytes per weight row: MXFP4 one E8M0 per 32 elements, NVFP4 one E4M3 per 16.
+__host__ __device__ __forceinline__ int64_t scale_row_bytes(int wt, int64_t K) {
+    return wt == 2 ? K / 32 : (wt == 3 ? K / 16 : 0);
 }
 
 }  // namespace moe

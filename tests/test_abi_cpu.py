@@ -52,12 +52,16 @@ def _layer(shape, x=FAKE, wr=FAKE, out=FAKE, w=None, ws=FAKE, ws_bytes=1 << 40):
     (dict(n_shared=1, shared_d_ff=0), moe.MOE_ERR_INVALID_ARG),
     (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_MXFP4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=moe.MOE_F32, weight_dtype=moe.MOE_NVFP4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=moe.MOE_NVFP4), moe.MOE_ERR_INVALID_ARG),
     (dict(act_dtype=moe.MOE_MXFP4), moe.MOE_ERR_INVALID_ARG),
     (dict(weight_dtype=7), moe.MOE_ERR_INVALID_ARG),
     (dict(n_experts=2048, top_k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=128, top_k=65), moe.MOE_ERR_UNSUPPORTED),
     (dict(weight_dtype=moe.MOE_MXFP4, d_model=48), moe.MOE_ERR_INVALID_ARG),
     (dict(weight_dtype=moe.MOE_MXFP4, d_ff=80), moe.MOE_ERR_INVALID_ARG),
+    (dict(weight_dtype=moe.MOE_NVFP4, d_model=48), moe.MOE_ERR_INVALID_ARG),
+    (dict(weight_dtype=moe.MOE_NVFP4, n_shared=1, shared_d_ff=80), moe.MOE_ERR_INVALID_ARG),
     (dict(d_model=100), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=1 << 20), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=moe.F_FORCE_GEMV | moe.F_FORCE_GEMM), moe.MOE_ERR_INVALID_ARG),
@@ -77,6 +81,10 @@ def test_null_and_misaligned_pointers_rejected():
     # MXFP4 needs its scale arrays
     s4 = _shape(weight_dtype=moe.MOE_MXFP4)
     assert _layer(s4, w=moe.Weights(w13=FAKE, w2=FAKE)) == moe.MOE_ERR_INVALID_ARG
+    # and so does NVFP4 (a tensor scale alone is not enough)
+    s5 = _shape(weight_dtype=moe.MOE_NVFP4)
+    assert _layer(s5, w=moe.Weights(w13=FAKE, w2=FAKE, w13_gscale=1.0, w2_gscale=1.0)) == moe.MOE_ERR_INVALID_ARG
+    assert _layer(s5, w=moe.Weights(w13=FAKE, w2=FAKE, w13_scale=FAKE)) == moe.MOE_ERR_INVALID_ARG
     # a shared expert needs its weights
     s1 = _shape(n_shared=1, shared_d_ff=64)
     assert _layer(s1) == moe.MOE_ERR_INVALID_ARG
@@ -109,6 +117,11 @@ def test_other_entry_points_validate():
     assert L.moe_mxfp4_dequant(FAKE, FAKE, 4, 48, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_mxfp4_dequant(FAKE, FAKE, -1, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_mxfp4_dequant(FAKE, FAKE, 0, 64, FAKE, None) == moe.MOE_OK
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 4, 48, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, -1, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(FAKE, FAKE + 1, 1.0, 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(FAKE, None, 1.0, 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 0, 64, FAKE, None) == moe.MOE_OK
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert L.moe_stack_forward(ctypes.byref(s), -1, FAKE, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE + 8, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
