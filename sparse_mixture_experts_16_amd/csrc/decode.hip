@@ -18,6 +18,10 @@
 //               every token; its 8 wavefronts split the slots, each adds g * (W2_e[i] . a) for
 //               its slots, and the 8 partial sums are added in wavefront order through LDS --
 //               a fixed order, so results are deterministic and need no atomics.
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "common.h"
 #include "kernels.h"
 #include "wchunk.h"
@@ -573,9 +577,30 @@ hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const
 
 // One 8-wavefront workgroup per CU at most (the routing prologue runs once per workgroup);
 // the wavefronts loop over the (slot, R columns) items.
-static unsigned dec_grid(int64_t max_items) {
+// Workgroups of `kernel` that are resident on the current device at once: its occupancy per CU
+// (registers, LDS) times the CU count, cached per (kernel, device, LDS bytes).
+static int resident_blocks(const void* kernel, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::tuple<const void*, int, size_t>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_tuple(kernel, dev, lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per_cu = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    return cache[key] = per_cu * cus;
+}
+
+// The gate/up grid fills the device exactly once (every workgroup redoes the routing, so a
+// second round of workgroups would pay it again), capped by the items there can be.
+static unsigned dec_grid(int64_t max_items, int resident) {
     int64_t blocks = (max_items + 7) / 8;
-    if (blocks > 256) blocks = 256;
+    if (blocks > resident) blocks = resident;
     return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
@@ -595,7 +620,8 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
 #define MOE_DW13(WTV, RV, UV)                                                                                    \
     do {                                                                                                         \
         const int64_t items = max_slots * ((f + RV - 1) / RV) + (n_shared ? (fs + RV - 1) / RV : 0);             \
-        MOE_LAUNCH(PROF_FFN_UP, (dec_w13<WTV, RV, UV>), dim3(dec_grid(items)), dim3(512), lds, st, p);         \
+        const int res = resident_blocks((const void*)dec_w13<WTV, RV, UV>, 512, lds);                           \
+        MOE_LAUNCH(PROF_FFN_UP, (dec_w13<WTV, RV, UV>), dim3(dec_grid(items, res)), dim3(512), lds, st, p);    \
     } while (0)
     // about 8 16-byte loads per lane in flight per item (HBM streams best at 4-8 per lane)
     if (wt == 0) MOE_DW13(0, 2, 1);
