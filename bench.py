@@ -214,6 +214,7 @@ def run_layer_workload(hip, name, steps, warmup):
     total, _ = _timed(hip, stream, step, steps, warmup)
     _, k_up = _timed(hip, stream, lambda i: step(i, log=(i - warmup) if i >= warmup else None), steps, warmup,
                      profile=moe.KERNEL_FFN_UP)
+    _, k_down = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_DOWN)
     torch.cuda.synchronize()
     # Routing actually taken (timed pass 2 logged it) -> unique experts per step.
     idx = idx_log[:, :T * s.k].cpu().numpy()
@@ -223,7 +224,8 @@ def run_layer_workload(hip, name, steps, warmup):
     sh_up, sh_down = expert_bytes(s, s.f_shared) if s.n_shared else (0, 0)
     ms = total / steps
     rec = dict(workload=name, desc=desc, T=T, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
-               ffn_up_us=float(np.mean(k_up) * 1e3), experts_hit_per_step=float(uniq.mean()),
+               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3),
+               experts_hit_per_step=float(uniq.mean()),
                experts_never_hit=int((counts == 0).sum()), load_max_over_mean=float(counts.max() / counts.mean()))
     if decode:
         layer_bytes = uniq * (up_b + down_b) + s.n_shared * (sh_up + sh_down)
@@ -292,6 +294,7 @@ def run_stack_workload(hip, steps, warmup):
     total, _ = _timed(hip, stream, step_graph, steps, warmup)
     # the timing hook's events ride on eager launches
     _, k_up = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_UP)
+    _, k_down = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_DOWN)
     ms = total / steps
     up_b, down_b = expert_bytes(s)
     # T = 1, k = 6 distinct experts per layer
@@ -299,7 +302,7 @@ def run_stack_workload(hip, steps, warmup):
     rec = dict(workload="c4_stack", desc=WORKLOADS["c4_stack"][3], T=1, ms_per_step=ms, tokens_per_s=1.0 / (ms * 1e-3),
                bound="hbm", alg_bytes_per_step=float(layer_bytes * s.n_layers),
                step_GBps=layer_bytes * s.n_layers / (ms * 1e-3) / 1e9,
-               ffn_up_us=float(np.mean(k_up) * 1e3))
+               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3))
     rec["step_frac_hbm"] = rec["step_GBps"] / HBM_PEAK_GBS
     # the hook's events bracket the last layer's launch of the step only
     rec["ffn_up_alg_bytes"] = float(s.k * up_b)
@@ -396,7 +399,9 @@ def main():
         "config": {"workload": head["desc"], "name": head["workload"], "T": head["T"],
                    **{key: head[key] for key in ("experts_hit_per_step", "step_GBps", "step_frac_hbm",
                                                  "step_TFLOPs", "step_frac_mfma") if key in head}},
-        "roofline": roof, "cpu_baseline": cpu, "sweep": sweep,
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernels_us": {key: head[key] for key in ("ffn_up_us", "ffn_down_us") if key in head},
+        "sweep": sweep,
     }
     print(json.dumps(line))
 

@@ -247,7 +247,6 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
-    const bool pub = blockIdx.x == 0;
     for (int i = tid; i < T * E; i += blockDim.x) s_logits[i] = io.logits[i];
     for (int e = tid; e < E; e += blockDim.x) {
         s_cnt[e] = 0;
@@ -280,11 +279,6 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
             R.gate[t * k + lane] = g;
             atomicAdd(&s_cnt[my_sel], 1);
             atomicOr(&s_mask[my_sel], 1 << t);
-            if (pub) {
-                io.topk_idx[t * k + lane] = my_sel;
-                io.topk_w[t * k + lane] = g;
-                if (io.idx_out) io.idx_out[t * k + lane] = my_sel;
-            }
         }
     }
     __syncthreads();
@@ -313,24 +307,36 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
         }
     }
     __syncthreads();
-    if (pub) {
-        // gate per sorted position for the down kernel: a slot's positions follow its tokens in order
-        for (int s = wv; s < R.n_slots; s += NW) {
-            const int4 S = R.slot[s];
-            if (lane == 0) io.slots[s] = S;
-            const uint32_t m = (uint32_t)S.w;
-            if (lane < T && ((m >> lane) & 1u)) {
-                const uint32_t below = lane == 0 ? 0u : (m & (0xFFFFFFFFu >> (32 - lane)));
-                const int pos = S.y + __popc(below);
-                float g = 1.0f;
-                if (S.x < E)
-                    for (int j = 0; j < k; ++j)
-                        if (R.sel[lane * k + j] == S.x) g = R.gate[lane * k + j];
-                io.pos_gate[pos] = g;
-            }
-        }
-        if (tid == 0) io.meta[0] = R.n_slots;
+}
+
+// Workgroup 0 hands the routing to the caller and the down kernel: top-k indices and gates,
+// the slot table and its size, and the gate of every sorted position (a slot's positions follow
+// its tokens in ascending order).  Each wavefront does its share once its own items are done,
+// so publishing never delays that workgroup's weight stream.
+__device__ void dec_route_publish(const DecRouteIO& io, const DecRoute& R) {
+    const int lane = lane_id(), wv = wave_id();
+    const int NW = blockDim.x / MOE_WAVE;
+    const int T = io.T, E = io.E, k = io.k;
+    for (int i = wv * MOE_WAVE + lane; i < T * k; i += NW * MOE_WAVE) {
+        io.topk_idx[i] = R.sel[i];
+        io.topk_w[i] = R.gate[i];
+        if (io.idx_out) io.idx_out[i] = R.sel[i];
     }
+    for (int s = wv; s < R.n_slots; s += NW) {
+        const int4 S = R.slot[s];
+        if (lane == 0) io.slots[s] = S;
+        const uint32_t m = (uint32_t)S.w;
+        if (lane < T && ((m >> lane) & 1u)) {
+            const uint32_t below = lane == 0 ? 0u : (m & (0xFFFFFFFFu >> (32 - lane)));
+            const int pos = S.y + __popc(below);
+            float g = 1.0f;
+            if (S.x < E)
+                for (int j = 0; j < k; ++j)
+                    if (R.sel[lane * k + j] == S.x) g = R.gate[lane * k + j];
+            io.pos_gate[pos] = g;
+        }
+    }
+    if (wv == 0 && lane == 0) io.meta[0] = R.n_slots;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -343,12 +349,31 @@ struct DecFfnArgs {
     const uint8_t* s13; const uint8_t* s13s;   // shared gate/up
     const uint8_t* w2; const uint8_t* w2s;     // routed down
     const uint8_t* s2; const uint8_t* s2s;     // shared down
-    float* a;               // [P + T, fmax] fp32
+    float* a;               // [P + T, fmax] fp32, each row chunk-transposed (a_off)
     void* out;              // [T, d] (f32 or bf16)
     int T, d, f, fs, fmax, k, accumulate;
-    int slot_bound;
-    float g13, g2, gs13, gs2;   // NVFP4 tensor scales (1 otherwise): routed / shared gate-up, down          // routed slots can number at most min(T*k, E), plus the shared one
+    int slot_bound;         // routed slots number at most min(T*k, E), plus the shared one
+    float g13, g2, gs13, gs2;   // NVFP4 tensor scales (1 otherwise): routed / shared gate-up, down
 };
+
+// Rows of `a` are stored chunk-transposed for the down kernels: with EC elements per weight
+// chunk and ncp = fmax / EC chunks per row, float4 q of chunk c sits at float (q * ncp + c) * 4,
+// so the 64 lanes of a wavefront, reading chunks c0 .. c0+63, read consecutive 16-byte pieces.
+template <int EC>
+__device__ __forceinline__ int64_t a_off(int j, int ncp) {
+    return ((int64_t)((j % EC) >> 2) * ncp + j / EC) * 4 + (j & 3);
+}
+template <int EC>
+__device__ __forceinline__ void a_chunk(const float* row, int ncp, int c, float (&out)[EC]) {
+#pragma unroll
+    for (int q = 0; q < EC / 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(row)[(int64_t)q * ncp + c];
+        out[4 * q] = v.x;
+        out[4 * q + 1] = v.y;
+        out[4 * q + 2] = v.z;
+        out[4 * q + 3] = v.w;
+    }
+}
 
 template <int WT> struct DecAct { using T = uint16_t; };
 template <> struct DecAct<0> { using T = float; };
@@ -457,12 +482,14 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
                 for (int r = 0; r < R; ++r) {
                     const float g = wave_sum(ag[r][q]) * gsc, u = wave_sum(au[r][q]) * gsc;
                     const int j = j0 + r;
-                    if (lane == 0 && j < fc) p.a[(int64_t)(pos + q) * p.fmax + j] = g / (1.0f + expf(-g)) * u;
+                    if (lane == 0 && j < fc)
+                        p.a[(int64_t)(pos + q) * p.fmax + a_off<EC>(j, p.fmax / EC)] = g / (1.0f + expf(-g)) * u;
                 }
             }
             pos += nq;
         }
     }
+    if (blockIdx.x == 0) dec_route_publish(p.rt, rs);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -520,8 +547,10 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
                 for (int u = 0; u < U; ++u) {
                     const int c = c0 + lane + MOE_WAVE * u;
                     if (c < NC) {
+                        float av[EC];
+                        a_chunk<EC>(ar, p.fmax / EC, c, av);
 #pragma unroll
-                        for (int r = 0; r < R; ++r) acc[r] = w[r][u].dot_f32(ar + (int64_t)c * EC, acc[r]);
+                        for (int r = 0; r < R; ++r) acc[r] = w[r][u].dot_f32(av, acc[r]);
                     }
                 }
 #pragma unroll
@@ -555,6 +584,106 @@ __global__ void __launch_bounds__(512) dec_w2c(DecFfnArgs p) {
                 const float prev = p.accumulate ? out[off] : 0.0f;
                 out[off] = prev + v;
             }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dec_w2c1: the down kernel for a single token.  The workgroup's (slot, row) units, slot-major,
+// are cut into 8 contiguous ranges, one per wavefront, so every wavefront streams about the
+// same number of weight rows whatever the slot count (8 wavefronts over 9 slots would otherwise
+// leave one wavefront with two slots and the others with one).  A wavefront issues the loads of
+// up to MAXU units at once, then adds g * y for each unit into its LDS row partials; the 8
+// partials of a row are added in wavefront order, which keeps the ascending-slot order.
+// ------------------------------------------------------------------------------------------------
+template <int WT, int R, int U, int MAXU, bool OUT_BF16>
+__global__ void __launch_bounds__(512, 2) dec_w2c1(DecFfnArgs p) {
+    using W = WChunk<WT>;
+    constexpr int EC = W::EC;
+    constexpr int NW = 8;
+    __shared__ float s_part[NW][R];
+    __shared__ int4 s_slot[MOE_MAX_K + 1];
+    __shared__ float s_pg[MOE_MAX_K + 1];
+    __shared__ int s_n;
+    const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    // slot count, slot table and the per-position gates in one round trip
+    if (tid == 0) s_n = p.rt.meta[0];
+    for (int s = tid; s < p.slot_bound; s += blockDim.x) s_slot[s] = p.rt.slots[s];
+    for (int i = tid; i <= p.k; i += blockDim.x) s_pg[i] = p.rt.pos_gate[i];
+    if (tid < NW * R) (&s_part[0][0])[tid] = 0.0f;
+    __syncthreads();
+    const int n_slots = s_n, E = p.rt.E, ncp = p.fmax / EC;
+    const int i0 = blockIdx.x * R;
+    const int nu = n_slots * R;
+    const int u_lo = wv * nu / NW, u_hi = (wv + 1) * nu / NW;
+    for (int b0 = u_lo; b0 < u_hi; b0 += MAXU) {
+        const int nb = min(MAXU, u_hi - b0);
+        W w[MAXU][U];
+#pragma unroll
+        for (int j = 0; j < MAXU; ++j) {
+            const int u = b0 + j, s = u / R, i = i0 + u % R;
+            if (j < nb && i < p.d) {
+                const int4 S = s_slot[s];
+                const bool sh = S.x == E;
+                const int fc = sh ? p.fs : p.f, NC = fc / EC;
+                const int64_t rb = row_bytes(WT, fc), sbb = scale_row_bytes(WT, fc);
+                const uint8_t* row = (sh ? p.s2 : p.w2 + (int64_t)S.x * p.d * rb) + (int64_t)i * rb;
+                const uint8_t* srow = (WT >= 2) ? (sh ? p.s2s : p.w2s + (int64_t)S.x * p.d * sbb) + (int64_t)i * sbb : nullptr;
+#pragma unroll
+                for (int v = 0; v < U; ++v) {
+                    const int c = lane + MOE_WAVE * v;
+                    if (c < NC) w[j][v].load(row, srow, c);
+                    else w[j][v].zero();
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < U; ++v) w[j][v].zero();
+            }
+        }
+        int cur = -1, NC = 0;
+        float g = 0.0f, gsc = 1.0f;
+        float av[U][EC];
+#pragma unroll
+        for (int j = 0; j < MAXU; ++j) {
+            if (j < nb) {
+                const int u = b0 + j, s = u / R, r = u % R;
+                if (s != cur) {
+                    const int4 S = s_slot[s];
+                    const bool sh = S.x == E;
+                    NC = (sh ? p.fs : p.f) / EC;
+                    g = s_pg[S.y];
+                    gsc = sh ? p.gs2 : p.g2;
+                    const float* ar = p.a + (int64_t)S.y * p.fmax;
+#pragma unroll
+                    for (int v = 0; v < U; ++v) {
+                        const int c = lane + MOE_WAVE * v;
+                        if (c < NC) a_chunk<EC>(ar, ncp, c, av[v]);
+                    }
+                    cur = s;
+                }
+                float acc = 0.0f;
+#pragma unroll
+                for (int v = 0; v < U; ++v)
+                    if (lane + MOE_WAVE * v < NC) acc = w[j][v].dot_f32(av[v], acc);
+                const float y = wave_sum(acc) * gsc;
+                if (lane == 0) s_part[wv][r] = fmaf(g, y, s_part[wv][r]);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < R && i0 + tid < p.d) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w8 = 0; w8 < NW; ++w8) v += s_part[w8][tid];
+        const int i = i0 + tid;
+        if (OUT_BF16) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+            const float prev = p.accumulate ? bf16_to_f32(out[i]) : 0.0f;
+            out[i] = f32_to_bf16(prev + v);
+        } else {
+            float* out = reinterpret_cast<float*>(p.out);
+            const float prev = p.accumulate ? out[i] : 0.0f;
+            out[i] = prev + v;
         }
     }
 }
@@ -637,10 +766,27 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
         if (out_bf16) MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c<WTV, RV, UV, true>), grid, dim3(512), 0, st, p);         \
         else MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c<WTV, RV, UV, false>), grid, dim3(512), 0, st, p);                 \
     } while (0)
-    if (wt == 0) MOE_DW2(0, 4, 1);
-    else if (wt == 1) MOE_DW2(1, 4, 2);
-    else if (wt == 2) MOE_DW2(2, 16, 1);
-    else MOE_DW2(3, 16, 1);
+#define MOE_DW21(WTV, RV, UV, MU)                                                                               \
+    do {                                                                                                         \
+        const dim3 grid((d + RV - 1) / RV);                                                                      \
+        if (out_bf16) MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c1<WTV, RV, UV, MU, true>), grid, dim3(512), 0, st, p);    \
+        else MOE_LAUNCH(PROF_FFN_DOWN, (dec_w2c1<WTV, RV, UV, MU, false>), grid, dim3(512), 0, st, p);            \
+    } while (0)
+    // one token: (slot, row) units split evenly over the wavefronts, when a row is one step
+    const int ec = wt == 0 ? 4 : (wt == 1 ? 8 : 32);
+    const int u1 = wt == 1 ? 2 : 1;
+    if (T == 1 && fmax / ec <= MOE_WAVE * u1) {
+        if (wt == 0) MOE_DW21(0, 4, 1, 8);
+        else if (wt == 1) MOE_DW21(1, 4, 2, 6);
+        else if (wt == 2) MOE_DW21(2, 8, 1, 6);
+        else MOE_DW21(3, 8, 1, 6);
+    } else {
+        if (wt == 0) MOE_DW2(0, 4, 1);
+        else if (wt == 1) MOE_DW2(1, 4, 2);
+        else if (wt == 2) MOE_DW2(2, 16, 1);
+        else MOE_DW2(3, 16, 1);
+    }
+#undef MOE_DW21
 #undef MOE_DW2
     return hipGetLastError();
 }

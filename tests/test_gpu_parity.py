@@ -232,6 +232,12 @@ DECODE_ODD = [
     mi.LayerSpec("dec_long_k", 2, 4096, 64, 8, 2, 1, 32, "bf16", "bf16", 1.0, 0.02, 0.02, seed=34),
     mi.LayerSpec("dec_long_f", 3, 64, 2048, 8, 2, 0, 0, "bf16", "bf16", 1.0, 0.02, 0.02, seed=35),
     mi.LayerSpec("dec_f32_E1", 4, 64, 32, 1, 1, 0, 0, "f32", "f32", 0.5, 0.1, 0.1, seed=36),
+    # a single token: the down kernel that splits (slot, row) units over the wavefronts
+    mi.LayerSpec("dec1_fs_gt_f", 1, 256, 64, 16, 3, 1, 192, "bf16", "bf16", 1.0, 0.05, 0.05, seed=37),
+    mi.LayerSpec("dec1_fs_lt_f", 1, 256, 192, 16, 9, 1, 64, "bf16", "bf16", 1.0, 0.05, 0.05, seed=38),
+    mi.LayerSpec("dec1_mxfp4_k12", 1, 160, 96, 24, 12, 1, 64, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=39),
+    mi.LayerSpec("dec1_f32", 1, 100, 40, 8, 5, 1, 24, "f32", "f32", 0.5, 0.1, 0.1, seed=40),
+    mi.LayerSpec("dec1_long_f", 1, 64, 2048, 8, 2, 0, 0, "bf16", "bf16", 1.0, 0.02, 0.02, seed=41),
 ]
 
 
