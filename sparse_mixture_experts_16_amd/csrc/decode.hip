@@ -243,6 +243,38 @@ __device__ __forceinline__ int dec_select(const float* l, int E, int k) {
     return wave_topk<KPL>(key, k);
 }
 
+// Slot table from the per-expert pair counts, token masks and on flags (one wavefront): lane l
+// owns experts l*PER .. l*PER+PER-1, read once into registers; exclusive scans of the counts
+// (first sorted position) and of the active experts (slot index).  Returns, at every lane, the
+// number of active experts before its own range plus its own: lane 63 holds the total.
+template <int PER>
+__device__ __forceinline__ int dec_slot_scan(DecRoute& R, const int* s_cnt, const int* s_mask, const int* s_on, int E) {
+    const int lane = lane_id();
+    const int lo = lane * PER;
+    int c[PER], m[PER];
+    bool on[PER];
+    int sc = 0, sa = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool in = lo + j < E;
+        c[j] = in ? s_cnt[lo + j] : 0;
+        m[j] = in ? s_mask[lo + j] : 0;
+        on[j] = in && s_on[lo + j];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        sc += c[j];
+        sa += c[j] > 0 && on[j];
+    }
+    int pc = wave_incl_scan(sc) - sc, pa = wave_incl_scan(sa) - sa;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (c[j] > 0 && on[j]) R.slot[pa++] = make_int4(lo + j, pc, c[j], m[j]);
+        pc += c[j];
+    }
+    return pa;
+}
+
 __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
@@ -285,19 +317,25 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     // slot table: exclusive scan over experts (wavefront 0)
     const int P = T * k;
     if (wv == 0) {
-        const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
-        const int lo = min(lane * per, E), hi = min(lo + per, E);
-        int sc = 0, sa = 0;
-        for (int e = lo; e < hi; ++e) {
-            sc += s_cnt[e];
-            sa += s_cnt[e] > 0 && s_on[e];
-        }
-        const int ic = wave_incl_scan(sc), ia = wave_incl_scan(sa);
-        int pc = ic - sc, pa = ia - sa;
-        for (int e = lo; e < hi; ++e) {
-            const int c = s_cnt[e];
-            if (c > 0 && s_on[e]) R.slot[pa++] = make_int4(e, pc, c, s_mask[e]);
-            pc += c;
+        int pa;
+        if (E <= 64) pa = dec_slot_scan<1>(R, s_cnt, s_mask, s_on, E);
+        else if (E <= 128) pa = dec_slot_scan<2>(R, s_cnt, s_mask, s_on, E);
+        else if (E <= 256) pa = dec_slot_scan<4>(R, s_cnt, s_mask, s_on, E);
+        else {
+            const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
+            const int lo = min(lane * per, E), hi = min(lo + per, E);
+            int sc = 0, sa = 0;
+            for (int e = lo; e < hi; ++e) {
+                sc += s_cnt[e];
+                sa += s_cnt[e] > 0 && s_on[e];
+            }
+            int pc = wave_incl_scan(sc) - sc;
+            pa = wave_incl_scan(sa) - sa;
+            for (int e = lo; e < hi; ++e) {
+                const int c = s_cnt[e];
+                if (c > 0 && s_on[e]) R.slot[pa++] = make_int4(e, pc, c, s_mask[e]);
+                pc += c;
+            }
         }
         if (lane == MOE_WAVE - 1) {
             R.n_routed = pa;

@@ -325,3 +325,24 @@ def test_no_renorm_gates():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(idx), ref_idx)
     np.testing.assert_allclose(host(w), ref_w, rtol=2e-5, atol=1e-8)
+
+
+@pytest.mark.parametrize("E,k,tied,T", [(16, 4, [1, 3, 6, 10, 12], 3), (256, 6, [3, 7, 100, 101, 200, 201, 255], 1),
+                                        (128, 8, [0, 5, 9, 64, 65, 127, 100, 99, 98], 2), (64, 2, [63, 0, 31], 5)])
+def test_decode_routing_exact_ties(E, k, tied, T):
+    """Equal router rows give bit-equal logits; the decode layer keeps the lower expert index among
+    equal logits, also when the tie straddles the k-th place, and lists equal logits by index."""
+    s = mi.LayerSpec("ties", T, 128, 64, E, k, 0, 0, "bf16", "bf16", 1.0, 0.05, 0.05, seed=50)
+    x = mi.host_x(s)
+    wr, _ = mi.host_router(s)
+    wr = wr.copy()
+    wr[tied] = wr[tied[0]]
+    b = np.zeros(E, np.float32)
+    b[tied] = 50.0
+    w = mi.host_experts(s)
+    ref = oracle.layer_forward(s, x, wr, b, w)
+    assert (ref["topk_idx"] == np.array(sorted(tied)[:k])).all()
+    res = moe.layer_forward(s, dev(x), dev(wr), dev(b), {n: dev(v) for n, v in w.items()})
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
+    assert_close(host(res["out"]), ref["out"], what="ties")
