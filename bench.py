@@ -62,11 +62,12 @@ KERNEL_SOURCES = {
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=27742.3, write_kib=27.3),
-    "c3_decode_T1": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=26254.8, write_kib=50.9),
-    "c4_stack": dict(src="decode:dffa2ffc3924dfe9", fetch_kib=26254.1, write_kib=50.6),
-    "c2_prefill": dict(src="gemm:b209a7bae128a13c", fetch_kib=804629.1, write_kib=111068.6),
-    "c3_prefill": dict(src="gemm:b209a7bae128a13c", fetch_kib=1435668.2, write_kib=393546.4),
+    "c1_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=27758.1, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=26278.3, write_kib=97.2),
+    "c3nv_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=27835.9, write_kib=97.0),
+    "c4_stack": dict(src="decode:078267efadcde7e2", fetch_kib=26277.7, write_kib=97.0),
+    "c2_prefill": dict(src="gemm:d456c04b472f1605", fetch_kib=710907.9, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:d456c04b472f1605", fetch_kib=1356208.3, write_kib=393216.0),
 }
 
 
