@@ -794,7 +794,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     if (wt == 0) MOE_DW13(0, 2, 1);
     else if (wt == 1) MOE_DW13(1, 1, 4);
     else if (wt == 2) MOE_DW13(2, 2, 2);
-    else MOE_DW13(3, 2, 2);
+    else MOE_DW13(3, 1, 2);
 #undef MOE_DW13
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
