@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_REF_LIB") or os.path.join(_HERE, "libmoe_ref.so")
 
 F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
-NO_RENORM, ACCUMULATE = 1, 2
+NO_RENORM, ACCUMULATE, MX_GEMM = 1, 2, 4
 _DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "nvfp4": NVFP4}
 
 
@@ -50,6 +50,7 @@ def lib():
         L.moe_ref_mxfp4_dequant.argtypes = [vp, vp, i64, i64, vp]
         L.moe_ref_e4m3_to_f32.argtypes = [vp, i64, vp]
         L.moe_ref_nvfp4_dequant.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
+        L.moe_ref_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp]
         L.moe_ref_router_logits.argtypes = [sp, vp, vp, vp, vp, vp]
         L.moe_ref_topk.argtypes = [sp, vp, vp, vp]
         L.moe_ref_permute.argtypes = [sp, vp, vp, vp, vp, vp]
@@ -113,6 +114,16 @@ def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, gscale: float) -> np.nd
     return out
 
 
+def mxfp8_quantize(v: np.ndarray):
+    """fp32 [rows, K] -> (E4M3 codes uint8 [rows, K], E8M0 scales uint8 [rows, K/32])."""
+    v = np.ascontiguousarray(v, np.float32)
+    rows, K = v.shape
+    codes = np.empty((rows, K), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint8)
+    _rc(lib().moe_ref_mxfp8_quantize(_p(v), rows, K, _p(codes), _p(scales)), "mxfp8_quantize")
+    return codes, scales
+
+
 def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     rows, half_k = codes.shape[0], codes.shape[1]
     K = 2 * half_k
@@ -152,9 +163,9 @@ def permute(spec, topk_idx: np.ndarray, E: Optional[int] = None):
 
 
 def grouped_ffn(spec, x, perm, offsets, w: dict, shared: Optional[dict] = None, k: Optional[int] = None,
-                E: Optional[int] = None):
+                E: Optional[int] = None, flags: int = 0):
     T = x.shape[0]
-    S = shape(spec, T=T, k=k, E=E)
+    S = shape(spec, T=T, k=k, E=E, flags=flags)
     ys = np.empty((T * S.k, spec.d), np.float64)
     ysh = np.empty((T, spec.d), np.float64) if shared is not None else None
     W = weights(w, shared)

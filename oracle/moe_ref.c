@@ -98,6 +98,67 @@ int moe_ref_e4m3_to_f32(const uint8_t* b, int64_t n, float* out) {
     return 0;
 }
 
+/* E4M3 code of a magnitude 0 <= a <= 448, rounded to nearest (ties to even code).  Normal range
+   a >= 2^-6: a = fr * 2^ex (frexp, fr in [0.5, 1)), so the exponent is ex - 1 and the mantissa
+   step 2^(ex - 4); subnormal range: steps of 2^-9, where a count of 8 is the smallest normal. */
+static uint8_t e4m3_code_of(double a) {
+    if (a < ldexp(1.0, -6)) return (uint8_t)nearbyint(ldexp(a, 9));
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                                   /* 2^e <= a < 2^(e+1) */
+    double m = nearbyint(ldexp(a, 3 - e));            /* 8 .. 16 */
+    if (m == 16.0) { m = 8.0; ++e; }
+    return (uint8_t)(((e + 7) << 3) | ((int)m - 8));
+}
+
+int moe_ref_mxfp8_quantize(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales) {
+    if (!v || !codes || !scales || rows < 0 || K < 0 || K % 32 != 0) return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float* blk = v + r * K + b * 32;
+            uint8_t* cb = codes + r * K + b * 32;
+            double amax = 0.0;
+            int bad = 0;
+            for (int i = 0; i < 32; ++i) {
+                if (!isfinite(blk[i])) bad = 1;
+                else if (fabs((double)blk[i]) > amax) amax = fabs((double)blk[i]);
+            }
+            if (bad) {
+                scales[r * (K / 32) + b] = 0xFF;
+                for (int i = 0; i < 32; ++i) cb[i] = 0x7F;
+                continue;
+            }
+            int e = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);
+                e = (ex - 1) - 8;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scales[r * (K / 32) + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) {
+                double q = ldexp((double)blk[i], -e);
+                double a = fabs(q);
+                if (a > 448.0) a = 448.0;
+                cb[i] = (uint8_t)(e4m3_code_of(a) | (q < 0.0 ? 0x80 : 0x00));
+            }
+        }
+    return 0;
+}
+
+/* An fp64 row replaced by its MXFP8 quantisation (the row rounded to fp32 first), as values. */
+static void mx_round_row(double* row, int64_t K) {
+    float blk[32];
+    uint8_t c[32], sc;
+    for (int64_t b = 0; b < K / 32; ++b) {
+        for (int i = 0; i < 32; ++i) blk[i] = (float)row[b * 32 + i];
+        moe_ref_mxfp8_quantize(blk, 1, 32, c, &sc);
+        for (int i = 0; i < 32; ++i)
+            row[b * 32 + i] = sc == 0xFF ? NAN : e4m3_value(c[i]) * ldexp(1.0, (int)sc - 127);
+    }
+}
+
 /* One NVFP4 element: E2M1 value * E4M3 block scale * tensor scale, exact in fp64. */
 static double nvfp4_value(uint8_t code, uint8_t scale, float gscale) {
     double m = (double)kE2M1[code & 7];
@@ -273,9 +334,18 @@ int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* co
 /* SwiGLU expert on n tokens (xs [n][d] fp64): ys [n][d] = W2 (silu(Wg x) * (Wu x)).
    Weight tensors hold several experts; `e` picks one; f is this expert's d_ff. */
 static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g13, const void* w2,
-                       const uint8_t* w2s, float g2, int64_t e, int64_t d, int64_t f, const double* xs, int64_t n,
-                       double* ys) {
+                       const uint8_t* w2s, float g2, int64_t e, int64_t d, int64_t f, const double* xs_in, int64_t n,
+                       int mx, double* ys) {
     double* a = (double*)malloc(sizeof(double) * (size_t)(n * f + 1));
+    /* MXFP8 quantisation of the activation rows before each contraction (MOE_REF_MX_GEMM) */
+    double* xq = NULL;
+    const double* xs = xs_in;
+    if (mx) {
+        xq = (double*)malloc(sizeof(double) * (size_t)(n * d + 1));
+        memcpy(xq, xs_in, sizeof(double) * (size_t)(n * d));
+        for (int64_t t = 0; t < n; ++t) mx_round_row(xq + t * d, d);
+        xs = xq;
+    }
     /* Gate and up projections, then the SwiGLU activation. */
 #pragma omp parallel
     {
@@ -294,6 +364,8 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g
         free(rg);
         free(ru);
     }
+    if (mx)
+        for (int64_t t = 0; t < n; ++t) mx_round_row(a + t * f, f);
     /* Down projection. */
 #pragma omp parallel
     {
@@ -306,6 +378,7 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g
         free(rd);
     }
     free(a);
+    free(xq);
 }
 
 int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
@@ -314,6 +387,8 @@ int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* pe
     const int64_t T = s->T, d = s->d, f = s->f, E = s->E, k = s->k;
     if (s->wt_dtype == MOE_REF_MXFP4 && (d % 32 || f % 32 || !w->w13_scale || !w->w2_scale)) return -1;
     if (s->wt_dtype == MOE_REF_NVFP4 && (d % 16 || f % 16 || !w->w13_scale || !w->w2_scale)) return -1;
+    const int mx = (s->flags & MOE_REF_MX_GEMM) != 0;
+    if (mx && s->wt_dtype != MOE_REF_MXFP4) return -1;
     if (T > 0 && (!x || !perm || !y_sorted || !w->w13 || !w->w2)) return -1;
     double* xs = (double*)malloc(sizeof(double) * (size_t)(T * d + 1));
     for (int64_t e = 0; e < E; ++e) {
@@ -321,7 +396,7 @@ int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* pe
         if (n == 0) continue;
         for (int64_t i = 0; i < n; ++i) act_row(s->act_dtype, x, d, perm[offsets[e] + i] / k, xs + i * d);
         expert_ffn(s->wt_dtype, w->w13, w->w13_scale, w->w13_gscale, w->w2, w->w2_scale, w->w2_gscale, e, d, f, xs,
-                   n, y_sorted + (int64_t)offsets[e] * d);
+                   n, mx, y_sorted + (int64_t)offsets[e] * d);
     }
     if (y_shared) {
         if (s->n_shared != 1 || !w->s13 || !w->s2) { free(xs); return -1; }
@@ -330,7 +405,7 @@ int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* pe
         for (int64_t t = 0; t < T; ++t) act_row(s->act_dtype, x, d, t, xs + t * d);
         if (T > 0)
             expert_ffn(s->wt_dtype, w->s13, w->s13_scale, w->s13_gscale, w->s2, w->s2_scale, w->s2_gscale, 0, d,
-                       s->f_shared, xs, T, y_shared);
+                       s->f_shared, xs, T, mx, y_shared);
     }
     free(xs);
     return 0;

@@ -35,13 +35,16 @@ extern "C" {
 #endif
 
 enum { MOE_REF_F32 = 0, MOE_REF_BF16 = 1, MOE_REF_MXFP4 = 2, MOE_REF_NVFP4 = 3 };
-enum { MOE_REF_NO_RENORM = 1u << 0, MOE_REF_ACCUMULATE = 1u << 1 };
+/* MOE_REF_MX_GEMM (MXFP4 weights only): before each expert contraction the activation row is
+   quantised to MXFP8 (moe_ref_mxfp8_quantize) and the contraction uses the quantised values:
+   x before gate/up, and a = silu(g)*u, rounded to fp32, before the down projection. */
+enum { MOE_REF_NO_RENORM = 1u << 0, MOE_REF_ACCUMULATE = 1u << 1, MOE_REF_MX_GEMM = 1u << 2 };
 
 typedef struct {
     int64_t T, d, f, E, k, n_shared, f_shared;
     int32_t act_dtype;   /* MOE_REF_F32 or MOE_REF_BF16 (bf16 given as raw uint16 bits) */
     int32_t wt_dtype;    /* MOE_REF_F32, MOE_REF_BF16, MOE_REF_MXFP4 or MOE_REF_NVFP4 */
-    uint32_t flags;      /* MOE_REF_NO_RENORM, MOE_REF_ACCUMULATE */
+    uint32_t flags;      /* MOE_REF_NO_RENORM, MOE_REF_ACCUMULATE, MOE_REF_MX_GEMM */
 } moe_ref_shape;
 
 /* Routed weights w13 [E, 2f, d] (rows 0..f-1 gate, f..2f-1 up), w2 [E, d, f];
@@ -64,6 +67,14 @@ int moe_ref_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t r
 /* OCP FP8 E4M3 (the "fn" variant: no infinities) -> fp32, by its bit fields:
    (-1)^s * (e == 0 ? m/8 * 2^-6 : (1 + m/8) * 2^(e-7)), NaN for e = 15, m = 7. */
 int moe_ref_e4m3_to_f32(const uint8_t* b, int64_t n, float* out);
+
+/* fp32 rows -> MXFP8 (OCP Microscaling Formats v1.0: E4M3 elements, one E8M0 shared scale per
+   32 consecutive elements of a row): for each block, e = floor(log2(max |v|)) - 8 (8 = the
+   exponent of E4M3's largest normal, 448), clamped to [-127, 127] (-127 for an all-zero block);
+   scales = e + 127; codes = E4M3(v / 2^e) rounded to nearest even, magnitudes above 448 clamped
+   to 448.  A block holding a NaN or an infinity gets scale 0xFF and NaN codes.
+   v [rows, K], codes [rows, K], scales [rows, K/32]; K % 32 == 0. */
+int moe_ref_mxfp8_quantize(const float* v, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales);
 
 /* NVFP4 -> fp32: out[r*K + j] = E2M1(code) * E4M3(scales[r*(K/16) + j/16]) * gscale,
    the exact product rounded once to fp32; codes [rows, K/2] as for MXFP4; K % 16 == 0. */

@@ -39,6 +39,12 @@ MUTANTS = {
     "nvfp4_block_32": ("scales[r * (K / 16) + j / 16]", "scales[r * (K / 16) + j / 32]"),
     "nvfp4_rows_block_32": ("row[j] = nvfp4_value(code, sc[j / 16], gscale);", "row[j] = nvfp4_value(code, sc[j / 32], gscale);"),
     "nvfp4_tensor_scale_dropped": ("return m * e4m3_value(scale) * (double)gscale;", "return m * e4m3_value(scale);"),
+    "mx_emax_7": ("e = (ex - 1) - 8;", "e = (ex - 1) - 7;"),
+    "mx_no_saturation": ("if (a > 448.0) a = 448.0;", "(void)0;"),
+    "mx_truncating_round": ("double m = nearbyint(ldexp(a, 3 - e));", "double m = floor(ldexp(a, 3 - e));"),
+    "mx_subnormal_step": ("return (uint8_t)nearbyint(ldexp(a, 9));", "return (uint8_t)nearbyint(ldexp(a, 8));"),
+    "mx_a_not_quantised": ("for (int64_t t = 0; t < n; ++t) mx_round_row(a + t * f, f);", "(void)0;"),
+    "mx_x_not_quantised": ("for (int64_t t = 0; t < n; ++t) mx_round_row(xq + t * d, d);", "(void)0;"),
 }
 
 

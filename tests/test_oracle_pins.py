@@ -104,6 +104,138 @@ def test_mxfp4_nibble_order_and_scale_blocks():
 
 
 # ---------------------------------------------------------------------------------------------
+# MXFP8 quantisation (OCP Microscaling Formats v1.0: E4M3 elements, one E8M0 scale per 32)
+# ---------------------------------------------------------------------------------------------
+def _torch_e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Independent element rounding: torch's cast to float8_e4m3fn (round to nearest even;
+    it has no saturation, so callers keep |v| <= 448)."""
+    torch = pytest.importorskip("torch")
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_mxfp8_element_rounding_matches_torch_float8_cast():
+    """Blocks whose largest magnitude is 256 have shared scale 2^0, so each code is the plain
+    E4M3 rounding of the value: every E4M3 value, every midpoint between neighbours (ties go to
+    the even code), subnormal midpoints and random values, with both signs."""
+    pos = _torch_e4m3(np.arange(0, 127, dtype=np.uint8)).astype(np.float64)  # 0 .. 448, increasing
+    mids = (pos[:-1] + pos[1:]) / 2
+    rnd = np.random.default_rng(3).uniform(0, 448, 4000)
+    vals = np.concatenate([pos, mids, rnd, (np.arange(0, 17) + 0.5) * 2.0 ** -9])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 256]  # keep 256 the block maximum
+    n = (len(vals) + 30) // 31
+    blocks = np.zeros((n, 32), np.float32)
+    blocks[:, 0] = 256.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[: len(vals)] = vals
+    blocks[:, 1:] = flat.reshape(n, 31)
+    codes, scales = oracle.mxfp8_quantize(blocks)
+    assert np.all(scales == 127)
+    want = _torch_e4m3_round(blocks)
+    zero = blocks == 0  # -0 and +0 carry the same value
+    assert np.array_equal(codes[~zero], want[~zero])
+    assert np.all(codes[zero] & 0x7F == 0)
+
+
+def test_mxfp8_shared_exponent_and_saturation_landmarks():
+    """The shared scale is floor(log2 amax) - 8 (8 = E4M3's largest exponent), clamped to the
+    E8M0 range; magnitudes above 448 after scaling clamp to 448 (0x7E / 0xFE)."""
+    cases = [  # (amax, scale byte)
+        (1.0, 119), (1.999, 119), (2.0, 120), (448.0, 127), (511.9, 127), (512.0, 128),
+        (2.0 ** -126, 0), (2.0 ** -130, 0), (3.0e38, 127 + 127 - 8), (0.75, 118),
+    ]
+    for amax, want in cases:
+        blk = np.zeros((1, 32), np.float32)
+        blk[0, 5] = np.float32(amax)
+        c, sc = oracle.mxfp8_quantize(blk)
+        assert int(sc[0, 0]) == want, (amax, int(sc[0, 0]), want)
+    blk = np.zeros((1, 32), np.float32)
+    c, sc = oracle.mxfp8_quantize(blk)
+    assert sc[0, 0] == 0 and np.all(c == 0)
+    # saturation: amax in [448, 512) keeps scale 2^0, so 460 and 500 exceed the largest normal
+    blk = np.array([[460.0, -500.0, 448.0, 447.0] + [0.0] * 28], np.float32)
+    c, sc = oracle.mxfp8_quantize(blk)
+    assert sc[0, 0] == 127 and list(c[0, :4]) == [0x7E, 0xFE, 0x7E, 0x7E]
+    # a value just under a power of two still takes the lower exponent
+    blk = np.array([[np.nextafter(np.float32(4.0), np.float32(0.0))] + [0.0] * 31], np.float32)
+    _, sc = oracle.mxfp8_quantize(blk)
+    assert sc[0, 0] == 127 + 1 - 8
+
+
+def test_mxfp8_blocks_and_rows_are_independent():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((3, 96)).astype(np.float32)
+    c0, s0 = oracle.mxfp8_quantize(v)
+    assert c0.shape == (3, 96) and s0.shape == (3, 3)
+    v2 = v.copy()
+    v2[1, 32:64] *= 1000.0
+    c1, s1 = oracle.mxfp8_quantize(v2)
+    keep = np.ones((3, 96), bool)
+    keep[1, 32:64] = False
+    assert np.array_equal(c0[keep], c1[keep])
+    assert s1[1, 1] == s0[1, 1] + 9 or s1[1, 1] == s0[1, 1] + 10
+    assert np.array_equal(np.delete(s0.reshape(-1), 4), np.delete(s1.reshape(-1), 4))
+
+
+def _np_mx(v: np.ndarray) -> np.ndarray:
+    """MXFP8 quantise-dequantise of fp32 rows, written from the specification in numpy with
+    torch's float8 cast for the element rounding."""
+    v = np.ascontiguousarray(v, np.float32)
+    blk = v.reshape(v.shape[0], -1, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=2, keepdims=True)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    e = np.clip(e, -127, 127)
+    q = np.clip(blk / 2.0 ** e, -448.0, 448.0).astype(np.float32)
+    deq = _torch_e4m3(_torch_e4m3_round(q)).astype(np.float64) * 2.0 ** e
+    return deq.reshape(v.shape)
+
+
+def test_mx_gemm_layer_matches_numpy_quantise_then_multiply():
+    """MOE_REF_MX_GEMM: x quantised to MXFP8 before gate/up and the fp32-rounded SwiGLU output
+    before the down projection, weights MXFP4; against numpy over independently decoded weights
+    and independently quantised activations, routing unchanged."""
+    s = mi.LayerSpec("mx_small", 6, 64, 64, 4, 2, 1, 32, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=72)
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w, sh = mi.host_experts(s), mi.host_experts(s, shared=True)
+    ref = oracle.layer_forward(s, x, wr, b, w, sh, flags=oracle.MX_GEMM)
+    plain = oracle.layer_forward(s, x, wr, b, w, sh)
+    np.testing.assert_array_equal(ref["topk_idx"], plain["topk_idx"])
+
+    def deq(codes, sc):
+        return oracle.mxfp4_dequant(codes.reshape(-1, codes.shape[-1]), sc.reshape(-1, sc.shape[-1])).astype(
+            np.float64).reshape(*codes.shape[:-1], -1)
+
+    W13, W2 = deq(w["w13"], w["w13_scale"]), deq(w["w2"], w["w2_scale"])
+    S13, S2 = deq(sh["w13"], sh["w13_scale"])[0], deq(sh["w2"], sh["w2_scale"])[0]
+    xq = _np_mx(bf16_to_f64(x).astype(np.float32))
+
+    def ffn(w13, w2, xr, f):
+        h = w13 @ xr
+        a = h[:f] / (1.0 + np.exp(-h[:f])) * h[f:]
+        return w2 @ _np_mx(a.astype(np.float32)[None, :])[0]
+
+    want = np.zeros((s.T, s.d))
+    for t in range(s.T):
+        for j in range(s.k):
+            e = int(ref["topk_idx"][t, j])
+            want[t] += ref["topk_w"][t, j] * ffn(W13[e], W2[e], xq[t], s.f)
+        want[t] += ffn(S13, S2, xq[t], s.f_shared)
+    np.testing.assert_allclose(ref["out"], want, rtol=1e-9, atol=1e-12 * np.abs(want).max())
+    # the quantisation is visible: the MX layer differs from the exact one by a few percent
+    err = np.sqrt(np.mean((ref["out"] - plain["out"]) ** 2) / np.mean(plain["out"] ** 2))
+    assert 1e-3 < err < 0.2, err
+
+
+def test_mx_gemm_flag_needs_mxfp4_weights():
+    s = mi.spec("c0")
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    with pytest.raises(ValueError):
+        oracle.layer_forward(s, x, wr, b, mi.host_experts(s), flags=oracle.MX_GEMM)
+
+
+# ---------------------------------------------------------------------------------------------
 # NVFP4 dequantisation: E2M1 x FP8 E4M3 block scale (16 elements) x fp32 tensor scale
 # ---------------------------------------------------------------------------------------------
 def _torch_e4m3(b: np.ndarray) -> np.ndarray:
