@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published (the fp8 x fp4 scaled MFMA runs at the fp8 rate)
 
 WORKLOADS = {
     # name: (config, T, weight copies, description)
@@ -45,11 +46,14 @@ WORKLOADS = {
     "c3_decode_T8": ("c3", 8, 4, "decode, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c3_decode_T32": ("c3", 32, 4, "decode, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=32"),
     "c3_prefill": ("c3", 8192, 1, "prefill, MXFP4 weights, E=256 top-6, d=4096, f=2048, T=8192"),
+    "c3_prefill_mx": ("c3", 8192, 1, "prefill, MXFP4 weights on the fp8 x fp4 matrix cores, activations quantised to "
+                                     "MXFP8 (MOE_F_MX_GEMM), E=256 top-6, d=4096, f=2048, T=8192"),
     "c3nv_decode_T1": ("c3nv", 1, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=1"),
     "c3nv_decode_T8": ("c3nv", 8, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c4_stack": ("c4", 1, 1, "43-layer MXFP4 stack of the E=256 top-6 layer, T=1, RMS-norm residual"),
 }
 HEADLINE = "c1_decode_T1"
+MX_WORKLOADS = {"c3_prefill_mx"}  # run with MOE_F_MX_GEMM
 POOL = 256
 
 # HBM traffic of the roofline kernel, from two rocprofv3 --pmc passes (FETCH_SIZE, then
@@ -200,7 +204,8 @@ def run_layer_workload(hip, name, steps, warmup):
         w = mi.device_experts(s, layer=c)
         sh = mi.device_experts(s, layer=c, shared=True) if s.n_shared else None
         layers.append((_to_dev(wr), _to_dev(b), moe.make_weights(w, sh), w, sh))
-    shape = moe.make_shape(s)
+    mx = name in MX_WORKLOADS
+    shape = moe.make_shape(s, flags=moe.F_MX_GEMM if mx else 0)
     ws = moe.workspace(shape)
     out = torch.empty((T, s.d), dtype=torch.bfloat16, device="cuda")
     row = (T * s.k + 3) // 4 * 4  # keep every step's slice 16-byte aligned
@@ -242,13 +247,15 @@ def run_layer_workload(hip, name, steps, warmup):
         rows = T * s.k + s.n_shared * T
         fl_up = 2.0 * rows * 2 * s.f * s.d
         fl_layer = 3.0 / 2.0 * fl_up + 2.0 * T * s.E * s.d
+        peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
         rec["bound"] = "mfma"
+        rec["mfma_dtype"] = "fp8 x fp4 (scaled)" if mx else "bf16"
         rec["alg_flops_per_step"] = fl_layer
         rec["step_TFLOPs"] = fl_layer / (ms * 1e-3) / 1e12
-        rec["step_frac_mfma"] = rec["step_TFLOPs"] / BF16_PEAK_TFLOPS
+        rec["step_frac_mfma"] = rec["step_TFLOPs"] / peak
         rec["ffn_up_alg_flops"] = fl_up
         rec["ffn_up_TFLOPs"] = fl_up / (np.mean(k_up) * 1e-3) / 1e12
-        rec["ffn_up_frac"] = rec["ffn_up_TFLOPs"] / BF16_PEAK_TFLOPS
+        rec["ffn_up_frac"] = rec["ffn_up_TFLOPs"] / peak
     del layers, x_pool, ws, out, idx_log
     moe._ws_cache.clear()
     torch.cuda.empty_cache()
@@ -389,7 +396,8 @@ def main():
                     frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
                     alg_bytes_per_launch=head["ffn_up_alg_bytes"], avg_launch_us=head["ffn_up_us"])
     else:
-        roof = dict(bound="mfma", achieved=head["ffn_up_TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+        roof = dict(bound="mfma", achieved=head["ffn_up_TFLOPs"],
+                    peak=FP8_PEAK_TFLOPS if head["workload"] in MX_WORKLOADS else BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (prefill grouped MFMA GEMM)",
                     alg_flops_per_launch=head["ffn_up_alg_flops"], avg_launch_us=head["ffn_up_us"])
     line = {

@@ -83,7 +83,15 @@ enum {
     MOE_F_NO_RENORM = 1u << 0,   /* gates = full-softmax probabilities at the selected experts */
     MOE_F_ACCUMULATE = 1u << 1,  /* out += layer(x) instead of out = layer(x) */
     MOE_F_FORCE_GEMV = 1u << 3,  /* use the decode (grouped GEMV) kernels at any T */
-    MOE_F_FORCE_GEMM = 1u << 4   /* use the prefill (grouped MFMA GEMM) kernels at any T */
+    MOE_F_FORCE_GEMM = 1u << 4,  /* use the prefill (grouped MFMA GEMM) kernels at any T */
+    /* MXFP4 weights only (else MOE_ERR_UNSUPPORTED): where the grouped MFMA GEMM kernels run
+       (T > 32, or MOE_F_FORCE_GEMM), run them on the fp8 x fp4 scaled matrix cores, with x and
+       the SwiGLU output a quantised to MXFP8 (OCP Microscaling Formats v1.0: E4M3 elements,
+       one E8M0 scale floor(log2 max|v|) - 8 per 32 consecutive elements along K, round to
+       nearest even, magnitudes above 448 clamped to 448) before each contraction.  This is an
+       approximation of the layer (a few percent relative error); the decode kernels (T <= 32)
+       ignore the flag and stay exact. */
+    MOE_F_MX_GEMM = 1u << 5
 };
 
 /* Limits of this implementation (MOE_ERR_UNSUPPORTED beyond them). */
@@ -190,6 +198,29 @@ int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows,
    [rows, K/16]; K % 32 == 0.  MOE_ERR_INVALID_ARG otherwise. */
 int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale, int64_t rows, int64_t K,
                       float* out, void* stream);
+
+/* Rows -> MXFP8, the activation quantisation of MOE_F_MX_GEMM on its own (OCP Microscaling
+   Formats v1.0): for each 32-element block of a row, scale byte = max(biased exponent of the
+   block's largest magnitude - 8, 0) (E8M0: floor(log2 max|v|) - 8), codes = E4M3(v / 2^(s-127))
+   rounded to nearest even with magnitudes above 448 clamped to 448; a block holding an infinity
+   or NaN gets scale 0xFF and NaN codes 0x7F.  x [rows, K] f32 or bf16 (x_dtype MOE_F32 /
+   MOE_BF16), codes [rows, K], scales [rows, K/32]; K % 32 == 0. */
+int moe_mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/* The two contractions of the MOE_F_MX_GEMM path as separate calls (MXFP4 weights, bf16
+   activations, d_model, d_ff and shared_d_ff multiples of 128; else MOE_ERR_UNSUPPORTED).
+   moe_mx_gate_up: x quantised to MXFP8 (as moe_mxfp8_quantize), then for every sorted slot i
+   (perm/offsets as from moe_permute) and the shared expert, a = silu(Wg x) * (Wu x) on the fp8 x
+   fp4 matrix cores, quantised to MXFP8 per 32 consecutive elements: a_codes [T*k*f + T*f_s]
+   bytes (slot rows of f, then the shared rows of f_s), a_scales [(T*k*f + T*f_s)/32].  Uses the
+   workspace.  moe_mx_down: y_sorted [T*k, d] and y_shared [T, d] (bf16) from those codes and
+   scales. */
+int moe_mx_gate_up(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
+                   const moe_weights* weights, uint8_t* a_codes, uint8_t* a_scales, void* ws, size_t ws_bytes,
+                   void* stream);
+int moe_mx_down(const moe_shape* shape, const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* offsets,
+                const moe_weights* weights, void* y_sorted, void* y_shared, void* stream);
 
 /* Timing aid for benchmarks: while set, every launch of the given kernel class carries
    ev_start / ev_stop on its own dispatch (hipExtLaunchKernel), so the events hold that

@@ -55,6 +55,7 @@ def lib():
         L.moe_ref_topk.argtypes = [sp, vp, vp, vp]
         L.moe_ref_permute.argtypes = [sp, vp, vp, vp, vp, vp]
         L.moe_ref_grouped_ffn.argtypes = [sp, vp, vp, vp, wp, vp, vp]
+        L.moe_ref_swiglu_act.argtypes = [sp, vp, vp, vp, wp, vp, vp]
         L.moe_ref_combine.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_ref_layer_forward.argtypes = [sp, vp, vp, vp, wp, vp, vp, vp, vp, vp]
         L.moe_ref_rmsnorm.argtypes = [i64, i64, vp, ctypes.c_double, i32, vp]
@@ -172,6 +173,18 @@ def grouped_ffn(spec, x, perm, offsets, w: dict, shared: Optional[dict] = None, 
     _rc(lib().moe_ref_grouped_ffn(ctypes.byref(S), _p(x), _p(perm), _p(offsets), ctypes.byref(W), _p(ys), _p(ysh)),
         "grouped_ffn")
     return ys, ysh
+
+
+def swiglu_act(spec, x, perm, offsets, w: dict, shared: Optional[dict] = None, flags: int = 0):
+    """The grouped FFN's SwiGLU activations (fp64): a_sorted [T*k, f], a_shared [T, f_shared]."""
+    T = x.shape[0]
+    S = shape(spec, T=T, flags=flags)
+    a = np.empty((T * S.k, spec.f), np.float64)
+    ash = np.empty((T, spec.f_shared), np.float64) if shared is not None else None
+    W = weights(w, shared)
+    _rc(lib().moe_ref_swiglu_act(ctypes.byref(S), _p(x), _p(perm), _p(offsets), ctypes.byref(W), _p(a), _p(ash)),
+        "swiglu_act")
+    return a, ash
 
 
 def combine(spec, y_sorted, inv_perm, topk_idx, topk_w, y_shared=None, residual=None, expert_mask=None):

@@ -335,7 +335,7 @@ int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* co
    Weight tensors hold several experts; `e` picks one; f is this expert's d_ff. */
 static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g13, const void* w2,
                        const uint8_t* w2s, float g2, int64_t e, int64_t d, int64_t f, const double* xs_in, int64_t n,
-                       int mx, double* ys) {
+                       int mx, double* ys, double* a_out) {
     double* a = (double*)malloc(sizeof(double) * (size_t)(n * f + 1));
     /* MXFP8 quantisation of the activation rows before each contraction (MOE_REF_MX_GEMM) */
     double* xq = NULL;
@@ -364,6 +364,12 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g
         free(rg);
         free(ru);
     }
+    if (a_out) memcpy(a_out, a, sizeof(double) * (size_t)(n * f));
+    if (!ys) {  /* activations only */
+        free(a);
+        free(xq);
+        return;
+    }
     if (mx)
         for (int64_t t = 0; t < n; ++t) mx_round_row(a + t * f, f);
     /* Down projection. */
@@ -381,34 +387,48 @@ static void expert_ffn(int32_t wt, const void* w13, const uint8_t* w13s, float g
     free(xq);
 }
 
-int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
-                        const moe_ref_weights* w, double* y_sorted, double* y_shared) {
+static int grouped(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                   const moe_ref_weights* w, double* y_sorted, double* y_shared, double* a_sorted, double* a_shared,
+                   int want_shared) {
     if (!shape_ok(s) || !w || !offsets) return -1;
     const int64_t T = s->T, d = s->d, f = s->f, E = s->E, k = s->k;
     if (s->wt_dtype == MOE_REF_MXFP4 && (d % 32 || f % 32 || !w->w13_scale || !w->w2_scale)) return -1;
     if (s->wt_dtype == MOE_REF_NVFP4 && (d % 16 || f % 16 || !w->w13_scale || !w->w2_scale)) return -1;
     const int mx = (s->flags & MOE_REF_MX_GEMM) != 0;
     if (mx && s->wt_dtype != MOE_REF_MXFP4) return -1;
-    if (T > 0 && (!x || !perm || !y_sorted || !w->w13 || !w->w2)) return -1;
+    if (T > 0 && (!x || !perm || (!y_sorted && !a_sorted) || !w->w13 || !w->w2)) return -1;
     double* xs = (double*)malloc(sizeof(double) * (size_t)(T * d + 1));
     for (int64_t e = 0; e < E; ++e) {
         int64_t n = offsets[e + 1] - offsets[e];
         if (n == 0) continue;
         for (int64_t i = 0; i < n; ++i) act_row(s->act_dtype, x, d, perm[offsets[e] + i] / k, xs + i * d);
         expert_ffn(s->wt_dtype, w->w13, w->w13_scale, w->w13_gscale, w->w2, w->w2_scale, w->w2_gscale, e, d, f, xs,
-                   n, mx, y_sorted + (int64_t)offsets[e] * d);
+                   n, mx, y_sorted ? y_sorted + (int64_t)offsets[e] * d : NULL,
+                   a_sorted ? a_sorted + (int64_t)offsets[e] * f : NULL);
     }
-    if (y_shared) {
+    if (want_shared) {
         if (s->n_shared != 1 || !w->s13 || !w->s2) { free(xs); return -1; }
         if (s->wt_dtype == MOE_REF_MXFP4 && (s->f_shared % 32 || !w->s13_scale || !w->s2_scale)) { free(xs); return -1; }
         if (s->wt_dtype == MOE_REF_NVFP4 && (s->f_shared % 16 || !w->s13_scale || !w->s2_scale)) { free(xs); return -1; }
         for (int64_t t = 0; t < T; ++t) act_row(s->act_dtype, x, d, t, xs + t * d);
         if (T > 0)
             expert_ffn(s->wt_dtype, w->s13, w->s13_scale, w->s13_gscale, w->s2, w->s2_scale, w->s2_gscale, 0, d,
-                       s->f_shared, xs, T, mx, y_shared);
+                       s->f_shared, xs, T, mx, y_shared, a_shared);
     }
     free(xs);
     return 0;
+}
+
+int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                        const moe_ref_weights* w, double* y_sorted, double* y_shared) {
+    if (s && s->T > 0 && !y_sorted) return -1;
+    return grouped(s, x, perm, offsets, w, y_sorted, y_shared, NULL, NULL, y_shared != NULL);
+}
+
+int moe_ref_swiglu_act(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                       const moe_ref_weights* w, double* a_sorted, double* a_shared) {
+    if (s && s->T > 0 && !a_sorted) return -1;
+    return grouped(s, x, perm, offsets, w, NULL, NULL, a_sorted, a_shared, a_shared != NULL);
 }
 
 /* ------------------------------------------------------------------------------------------ */

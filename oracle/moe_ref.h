@@ -104,6 +104,12 @@ int moe_ref_permute(const moe_ref_shape* s, const int32_t* topk_idx, int32_t* co
 int moe_ref_grouped_ffn(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
                         const moe_ref_weights* w, double* y_sorted, double* y_shared);
 
+/* The SwiGLU activations of the same computation, before the down projection (and before its
+   MXFP8 rounding under MOE_REF_MX_GEMM, whose x quantisation it includes): a_sorted [T*k, f]
+   in sorted-slot order, a_shared [T, f_shared] (NULL: not computed). */
+int moe_ref_swiglu_act(const moe_ref_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                       const moe_ref_weights* w, double* a_sorted, double* a_shared);
+
 /* out[t] = sum over the token's selected experts, in ascending expert index, of
    g * y_sorted[inv_perm[t*k+j]], then + y_shared[t] (if given), then + residual[t]
    (if given).  expert_mask (nullable, E + 1 bytes: routed experts then shared)

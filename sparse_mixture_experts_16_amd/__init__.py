@@ -22,13 +22,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_MXFP4, MOE_NVFP4 = 0, 1, 2, 3
-F_NO_RENORM, F_ACCUMULATE, F_FORCE_GEMV, F_FORCE_GEMM = 1 << 0, 1 << 1, 1 << 3, 1 << 4
+F_NO_RENORM, F_ACCUMULATE, F_FORCE_GEMV, F_FORCE_GEMM, F_MX_GEMM = 1 << 0, 1 << 1, 1 << 3, 1 << 4, 1 << 5
 MAX_EXPERTS, MAX_TOPK = 1024, 64
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4, "nvfp4": MOE_NVFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_masked", "moe_stack_forward", "moe_mxfp4_dequant",
-           "moe_nvfp4_dequant", "moe_profile_kernel"]
+           "moe_nvfp4_dequant", "moe_mxfp8_quantize", "moe_mx_gate_up", "moe_mx_down",
+           "moe_profile_kernel"]
 KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
 
 
@@ -62,6 +63,9 @@ _lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
 _lib.moe_nvfp4_dequant.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp]
+_lib.moe_mxfp8_quantize.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _vp]
+_lib.moe_mx_gate_up.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_mx_down.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp]
 _lib.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
 for _n in EXPORTS[2:]:
     getattr(_lib, _n).restype = ctypes.c_int
@@ -201,6 +205,26 @@ def mxfp4_dequant(codes, scales, out, stream=None):
     rows = codes.numel() // half_k
     _check(_lib.moe_mxfp4_dequant(_ptr(codes), _ptr(scales), rows, 2 * half_k, _ptr(out), _stream(stream)),
            "moe_mxfp4_dequant")
+
+
+def mxfp8_quantize(x, codes, scales, stream=None):
+    """x [rows, K] float32 or bfloat16 -> codes uint8 [rows, K], scales uint8 [rows, K/32]."""
+    import torch
+    dt = MOE_F32 if x.dtype == torch.float32 else MOE_BF16
+    K = x.shape[-1]
+    _check(_lib.moe_mxfp8_quantize(_ptr(x), dt, x.numel() // K, K, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_mxfp8_quantize")
+
+
+def mx_gate_up(shape: Shape, x, perm, offsets, weights: Weights, a_codes, a_scales, ws=None, stream=None):
+    ws = workspace(shape, x.device) if ws is None else ws
+    _check(_lib.moe_mx_gate_up(ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(offsets), ctypes.byref(weights),
+                               _ptr(a_codes), _ptr(a_scales), _ptr(ws), ws.numel(), _stream(stream)), "moe_mx_gate_up")
+
+
+def mx_down(shape: Shape, a_codes, a_scales, offsets, weights: Weights, y_sorted, y_shared=None, stream=None):
+    _check(_lib.moe_mx_down(ctypes.byref(shape), _ptr(a_codes), _ptr(a_scales), _ptr(offsets), ctypes.byref(weights),
+                            _ptr(y_sorted), _ptr(y_shared), _stream(stream)), "moe_mx_down")
 
 
 def nvfp4_dequant(codes, scales, gscale, out, stream=None):

@@ -10,7 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "ffn_gemv.hip", "decode.hip", "gemm.hip", "misc.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "ffn_gemv.hip", "decode.hip", "gemm.hip", "mxgemm.hip",
+           "misc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

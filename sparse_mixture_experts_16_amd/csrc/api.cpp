@@ -88,9 +88,11 @@ int check_shape(const moe_shape* s) {
     } else {
         if (s->d_model % vec || s->d_ff % vec || fs % vec) return MOE_ERR_INVALID_ARG;
     }
-    if (s->flags & ~(uint32_t)(MOE_F_NO_RENORM | MOE_F_ACCUMULATE | MOE_F_FORCE_GEMV | MOE_F_FORCE_GEMM))
+    if (s->flags &
+        ~(uint32_t)(MOE_F_NO_RENORM | MOE_F_ACCUMULATE | MOE_F_FORCE_GEMV | MOE_F_FORCE_GEMM | MOE_F_MX_GEMM))
         return MOE_ERR_INVALID_ARG;
     if ((s->flags & MOE_F_FORCE_GEMV) && (s->flags & MOE_F_FORCE_GEMM)) return MOE_ERR_INVALID_ARG;
+    if ((s->flags & MOE_F_MX_GEMM) && s->weight_dtype != MOE_MXFP4) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -154,6 +156,22 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
             void* y_sorted, void* y_shared, const uint8_t* mask, hipStream_t st) {
     const int wt = s->weight_dtype;
     const int fs = s->n_shared ? s->shared_d_ff : 0;
+    if (use_gemm(s) && (s->flags & MOE_F_MX_GEMM)) {
+        // x codes and scales in the y region (consumed by gate/up before the down projection
+        // writes y), a codes and scales in the a region
+        const int64_t T = s->T, d = s->d_model, P = T * s->top_k;
+        uint8_t* xq = at<uint8_t>(ws, L.y);
+        uint8_t* xs = xq + T * d;
+        uint8_t* aq = at<uint8_t>(ws, L.a);
+        uint8_t* aqs = aq + P * s->d_ff + T * fs;
+        MOE_TRY(launch_mx_quant_rows(MOE_BF16, x, xq, xs, T, d, st));
+        MOE_TRY(launch_mxgemm_w13(xq, xs, perm, offsets, w->w13, w->w13_scale, w->s13, w->s13_scale, aq, aqs, s->T,
+                                  s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, mask, st));
+        MOE_TRY(launch_mxgemm_w2(aq, aqs, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, (uint16_t*)y_sorted,
+                                 (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
+                                 s->n_shared, mask, st));
+        return MOE_OK;
+    }
     if (use_gemm(s)) {
         uint16_t* a = at<uint16_t>(ws, L.a);
         MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
@@ -339,6 +357,47 @@ int moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* perm, cons
     return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, nullptr, st);
 }
 
+// The two contractions of the MX prefill path as separate calls (MXFP4 weights, bf16 act, the
+// MFMA GEMM's shape constraints).
+static int mx_stage_check(const moe_shape* s, const moe_weights* w) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->weight_dtype != MOE_MXFP4 || !gemm_shape_ok(s)) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    return check_weights(s, w);
+}
+
+int moe_mx_gate_up(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets,
+                   const moe_weights* w, uint8_t* a_codes, uint8_t* a_scales, void* ws, size_t ws_bytes,
+                   void* stream) {
+    int rc = mx_stage_check(s, w);
+    if (rc != MOE_OK || s->T == 0) return rc;
+    if (!ptr_ok(x) || !ptr_ok(perm) || !ptr_ok(offsets) || !ptr_ok(a_codes) || !ptr_ok(a_scales))
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = layout(s);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t T = s->T, d = s->d_model;
+    uint8_t* xq = at<uint8_t>(ws, L.y);
+    MOE_TRY(launch_mx_quant_rows(MOE_BF16, x, xq, xq + T * d, T, d, st));
+    MOE_TRY(launch_mxgemm_w13(xq, xq + T * d, perm, offsets, w->w13, w->w13_scale, w->s13, w->s13_scale, a_codes,
+                              a_scales, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
+                              s->n_experts, s->n_shared, nullptr, st));
+    return MOE_OK;
+}
+
+int moe_mx_down(const moe_shape* s, const uint8_t* a_codes, const uint8_t* a_scales, const int32_t* offsets,
+                const moe_weights* w, void* y_sorted, void* y_shared, void* stream) {
+    int rc = mx_stage_check(s, w);
+    if (rc != MOE_OK || s->T == 0) return rc;
+    if (!ptr_ok(a_codes) || !ptr_ok(a_scales) || !ptr_ok(offsets) || !ptr_ok(y_sorted)) return MOE_ERR_INVALID_ARG;
+    if (s->n_shared ? !ptr_ok(y_shared) : y_shared != nullptr) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_mxgemm_w2(a_codes, a_scales, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, (uint16_t*)y_sorted,
+                             (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0,
+                             s->top_k, s->n_experts, s->n_shared, nullptr, (hipStream_t)stream));
+    return MOE_OK;
+}
+
 int moe_combine(const moe_shape* s, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
                 const void* y_shared, void* out, void* stream) {
     int rc = check_shape(s);
@@ -437,6 +496,15 @@ int moe_nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, float gscale,
     if (rows == 0 || K == 0) return MOE_OK;
     if (!ptr_ok(codes) || !scales || ((uintptr_t)scales & 1) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
     MOE_TRY(launch_nvfp4_dequant(codes, scales, gscale, out, rows, K, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_mxfp8_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+    if (rows < 0 || K < 0 || K % 32 || (x_dtype != MOE_F32 && x_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+    if (rows == 0 || K == 0) return MOE_OK;
+    if (!ptr_ok(x) || !ptr_ok(codes) || !scales) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_mx_quant_rows(x_dtype, x, codes, scales, rows, K, (hipStream_t)stream));
     return MOE_OK;
 }
 

@@ -9,15 +9,10 @@
 //   MODE_W2      y[pos, n] = a[pos] . W2_e[n]                          A rows contiguous
 //   MODE_ROUTER  l[t, e]   = x_t . W_r[e] + b[e]                       one group, fp32 out
 //
-// Tiles are 128 (token rows) x 128 (weight rows) x 64 or 32 (K); four wavefronts each own a 64x64
-// quarter computed with v_mfma_f32_16x16x32_bf16 (operand lane layout: lane l holds row l%16,
-// k = 8*(l/16)..+7 of A and column l%16 of B; the accumulator holds column l%16, rows
-// 4*(l/16)..+3).  Tiles stream through double-buffered LDS rows padded to 72 bf16 so that the
-// 16-byte fragment reads of 8 consecutive rows fall on distinct banks.  MXFP4 weights are
-// expanded to bf16 (exactly: E2M1 x 2^k fits bf16) with the scaled converts on the way into
-// LDS.  For MODE_W13 the LDS B tile interleaves 32 gate rows and the matching 32 up rows per
-// wavefront column, so the SwiGLU pairs meet in the same lane and the activation is fused
-// into the epilogue.
+// The tile shape, operand layouts and K pipeline are described above the kernel template below.
+// For MODE_W13 the LDS B tile interleaves gate rows and the matching up rows per wavefront
+// column, so the SwiGLU pairs meet in the same lane and the activation is fused into the
+// epilogue.
 //
 // Tile order: a flat list over (group, m-tile, n-tile), n fastest, built per workgroup from
 // the expert offsets; workgroup b takes list entry (b % 8) * (grid / 8) + b / 8 so that each
@@ -25,12 +20,10 @@
 // shared in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 #include "wchunk.h"
 
 namespace moe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int TBM = 128;
 enum { MODE_W13 = 0, MODE_W2 = 1, MODE_ROUTER = 2 };
@@ -96,14 +89,6 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// s_waitcnt immediate: vmcnt(n) (n < 16), expcnt untouched, lgkmcnt(0).
-#define VM_WAIT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4))
-
-__device__ __forceinline__ void dma16(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0); }
-__device__ __forceinline__ void dma4(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0); }
-__device__ __forceinline__ int chunk_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 template <int MODE, int WT, int BN, bool SPLIT, int NWN>
 __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 waves per SIMD: <= 256 registers

@@ -73,6 +73,21 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            const uint8_t* s2s, uint16_t* y, uint16_t* y_shared, int T, int d, int f, int fs, int k,
                            int E, int n_shared, const uint8_t* mask, hipStream_t st);
 
+// MX prefill (MXFP4 weights on the scaled fp8 x fp4 matrix cores, activations quantised to MXFP8):
+// x -> codes [rows, d] + E8M0 scales [rows, d/32]; gate/up (+ SwiGLU, a quantised in the
+// epilogue into codes [P*f + T*fs] and scales [(P*f + T*fs)/32]); down projection to bf16.
+// x_dtype 0: f32 rows, 1: bf16 rows; K % 32 == 0
+hipError_t launch_mx_quant_rows(int x_dtype, const void* x, uint8_t* q, uint8_t* sc, int64_t rows, int64_t K,
+                                hipStream_t st);
+hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t* perm, const int32_t* offsets,
+                             const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s, uint8_t* aq,
+                             uint8_t* aqs, int T, int d, int f, int fs, int k, int E, int n_shared,
+                             const uint8_t* mask, hipStream_t st);
+hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t* offsets, const void* w2,
+                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y, uint16_t* y_shared,
+                            int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
+                            hipStream_t st);
+
 // Decode path (T <= 32, T*E <= 8192): router logits, then the FFN kernels (the gate/up kernel
 // redoes the routing per workgroup in LDS; workgroup 0 publishes it).
 bool dec_supported(int T, int E, int k);

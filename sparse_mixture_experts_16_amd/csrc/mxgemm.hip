@@ -1,0 +1,428 @@
+// Prefill grouped GEMM on the gfx950 scaled matrix cores (MOE_F_MX_GEMM): MXFP4 expert weights
+// enter v_mfma_scale_f32_32x32x64_f8f6f4 as they are stored, and the activations are quantised
+// on the fly to MXFP8 (E4M3 elements, one E8M0 scale per 32 along K; OCP Microscaling Formats
+// v1.0): x by mx_quant_rows before gate/up, the SwiGLU output a inside the gate/up epilogue.
+// The pages run their DeepSeek-V4-Flash build on MXFP4 experts (dothoosh.com FreeToken article,
+// "Benchmarks and real performance"); at prefill every expert's weights meet thousands of
+// tokens, and the fp8 x fp4 matrix cores do twice the work per cycle of the bf16 ones with no
+// per-fragment expansion of the codes.
+//
+// Operand layout of the scaled MFMA (measured on gfx950): A (E4M3, 32 bytes per lane): lane l
+// holds row l%32; its bytes 0..15 are K = 16*(l/32) + 0..15 and bytes 16..31 are
+// K = 32 + 16*(l/32) + 0..15.  B (E2M1, 16 bytes per lane): lane l holds column l%32,
+// K = 32*(l/32) + 0..31, element 2i in the low nibble of byte i.  Scales: byte 0 of lane l's
+// scale operand is the E8M0 scale of row (column) l%32 for the K block l/32.  Accumulator j of
+// lane l: row 8*(j/4) + 4*(l/32) + j%4, column l%32.
+//
+// Tile: 128 token rows x BN weight rows, K in stages of 64 (one MFMA per 32x32 sub-tile), 4
+// wavefronts as 2 x 2, each owning 64 x BN/2.  Stages stream through a three-deep LDS ring by
+// global_load_lds (A rows 64 bytes with the chunk swizzle of the bf16 kernel, B rows 32 bytes);
+// the scales of two stages (four blocks) travel as one dword per row into a double-buffered row
+// list.  Tiles come from the flat (expert, m-tile, n-tile) list of the bf16 kernel.
+#include "common.h"
+#include "kernels.h"
+#include "lds_dma.h"
+
+namespace moe {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+enum { MX_W13 = 0, MX_W2 = 1 };
+
+// ---------------------------------------------------------------------------------------------
+// MXFP8 quantisation of one 32-element block
+// ---------------------------------------------------------------------------------------------
+// E4M3 code of q (finite, |q| < 512), rounded to nearest even on the fp32 bits; magnitudes
+// above 448 (E4M3's largest normal) clamp to it.
+__device__ __forceinline__ uint32_t e4m3_rne(float q) {
+    const uint32_t sgn = (__float_as_uint(q) >> 24) & 0x80u;
+    const float a = fminf(fabsf(q), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (a count of 8 is 2^-6)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        uint32_t u = __float_as_uint(a);
+        u += 0x7FFFFu + ((u >> 20) & 1u);  // keep 3 mantissa bits, ties to even
+        code = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
+    }
+    return code | sgn;
+}
+
+// Shared scale of a block from the bit pattern of its largest magnitude: E8M0 byte
+// floor(log2 amax) - 8 + 127 = (biased fp32 exponent) - 8, at least 0; 0xFF (NaN) when the
+// block holds an infinity or a NaN.  Codes are packed 4 to a word, element i in byte i % 4.
+__device__ __forceinline__ uint32_t mx_block(const float (&v)[32], uint32_t (&code)[8]) {
+    uint32_t am = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    const uint32_t ex = am >> 23;
+    if (ex == 0xFFu) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) code[w] = 0x7F7F7F7Fu;
+        return 0xFFu;
+    }
+    const uint32_t sb = ex > 8u ? ex - 8u : 0u;
+    const float mul = __uint_as_float((254u - sb) << 23);  // 2^(127 - sb): exact scaling
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+        code[w] = e4m3_rne(v[4 * w] * mul) | (e4m3_rne(v[4 * w + 1] * mul) << 8) |
+                  (e4m3_rne(v[4 * w + 2] * mul) << 16) | (e4m3_rne(v[4 * w + 3] * mul) << 24);
+    return sb;
+}
+
+// rows [rows, d] (bf16 or f32) -> codes [rows, d], scales [rows, d/32]; one thread per block.
+template <typename X>
+__global__ void __launch_bounds__(256) mx_quant_rows(const X* __restrict__ x, uint8_t* __restrict__ q,
+                                                     uint8_t* __restrict__ sc, int64_t nblk) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+        float v[32];
+        if constexpr (sizeof(X) == 2) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4 u = src[c];
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[8 * c + 2 * h] = bf16_lo(w[h]);
+                    v[8 * c + 2 * h + 1] = bf16_hi(w[h]);
+                }
+            }
+        } else {
+            const float4* src = reinterpret_cast<const float4*>(x + b * 32);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float4 u = src[c];
+                v[4 * c] = u.x;
+                v[4 * c + 1] = u.y;
+                v[4 * c + 2] = u.z;
+                v[4 * c + 3] = u.w;
+            }
+        }
+        uint32_t code[8];
+        sc[b] = (uint8_t)mx_block(v, code);
+        uint4* dst = reinterpret_cast<uint4*>(q + b * 32);
+        dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+        dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+    }
+}
+
+hipError_t launch_mx_quant_rows(int x_dtype, const void* x, uint8_t* q, uint8_t* sc, int64_t rows, int64_t K,
+                                hipStream_t st) {
+    const int64_t nblk = rows * (K / 32);
+    if (nblk == 0) return hipSuccess;
+    int64_t blocks = (nblk + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (x_dtype == 0)
+        hipLaunchKernelGGL(mx_quant_rows<float>, dim3((unsigned)blocks), dim3(256), 0, st, (const float*)x, q, sc, nblk);
+    else
+        hipLaunchKernelGGL(mx_quant_rows<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)x, q, sc,
+                           nblk);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// The grouped GEMM
+// ---------------------------------------------------------------------------------------------
+struct MxGemmArgs {
+    const uint8_t* A;        // W13: x codes [T, d]; W2: a codes (routed [P, f], shared at +P*f as [T, fs])
+    const uint8_t* As;       // A scales: W13 [T, d/32]; W2 routed [P, f/32], shared at +P*f/32 as [T, fs/32]
+    const int32_t* perm;     // W13: sorted slot -> pair
+    const int32_t* offsets;  // [E+1]
+    const uint8_t* w;        // routed MXFP4 codes [E, N, K/2]
+    const uint8_t* wsc;      // routed E8M0 scales [E, N, K/32]
+    const uint8_t* sw;       // shared expert
+    const uint8_t* swsc;
+    uint8_t* aq;             // W13 out: a codes, laid out as the W2 A operand
+    uint8_t* aqs;            // W13 out: a scales
+    uint16_t* y;             // W2 out: y_sorted [P, d] bf16
+    uint16_t* y_sh;          // W2 out: y_shared [T, d] bf16
+    int T, d, f, fs, k, E, n_shared;
+    const uint8_t* mask;     // nullable [E + 1]: groups whose byte is 0 get no tiles
+};
+
+template <int MODE, int BN>
+__global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
+    constexpr int BM = 128, BK = 64, NS = 3, NWN = 2, THREADS = 256;
+    constexpr int WN = BN / NWN, NT32 = WN / 32;
+    constexpr int NA = BM * 4 / THREADS;  // 16-byte A chunks per thread per stage (rows of 64 bytes)
+    constexpr int NB = BN * 2 / THREADS;  // 16-byte B chunks per thread per stage (rows of 32 bytes)
+    constexpr int OPS = NA + NB;          // loads one stage adds per thread (the scale dwords not counted)
+    static_assert(NA >= 1 && NB >= 1 && OPS < 16, "tile / thread count");
+    constexpr int SZ_A = NS * BM * 64, SZ_B = NS * BN * 32, SZ_SA = 2 * BM * 4, SZ_SB = 2 * BN * 4;
+    constexpr int APITCH = 132;  // fp32 a-values per staged row (W13 epilogue, 64 rows at a time)
+    constexpr int OP = BN + 8;   // bf16 per staged output row (W2 epilogue)
+    constexpr int SZ_EP = (MODE == MX_W13) ? 64 * APITCH * 4 : BM * OP * 2;
+    constexpr int SZ_RING = SZ_A + SZ_B + SZ_SA + SZ_SB;
+    constexpr int SZ = SZ_RING > SZ_EP ? SZ_RING : SZ_EP;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ + (MOE_MAX_E + 2) * 4];
+    uint8_t* sA = smem;
+    uint8_t* sB = smem + SZ_A;
+    uint32_t* sSA = reinterpret_cast<uint32_t*>(smem + SZ_A + SZ_B);
+    uint32_t* sSB = reinterpret_cast<uint32_t*>(smem + SZ_A + SZ_B + SZ_SA);
+    int* s_pref = reinterpret_cast<int*>(smem + SZ);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv / NWN, wn = wv % NWN;
+    const int G = p.E + p.n_shared;
+    const int P = p.T * p.k;
+
+    // ---- flat tile list: tiles of group g = ceil(rows_g / BM) * ntiles_g
+    auto tiles_of = [&](int g) -> int {
+        const bool sh = g == p.E;
+        const int rows = (p.mask && !p.mask[g]) ? 0 : (sh ? p.T : p.offsets[g + 1] - p.offsets[g]);
+        const int nt = (MODE == MX_W13) ? (sh ? p.fs : p.f) / (BN / 2) : p.d / BN;
+        return ((rows + BM - 1) / BM) * nt;
+    };
+    if (wv == 0) {
+        const int per = (G + 63) / 64;
+        const int lo = min(lane * per, G), hi = min(lo + per, G);
+        int sum = 0;
+        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
+        const int incl = wave_incl_scan(sum);
+        int run = incl - sum;
+        for (int g = lo; g < hi; ++g) {
+            s_pref[g] = run;
+            run += tiles_of(g);
+        }
+        if (lane == 63) s_pref[G] = incl;
+    }
+    __syncthreads();
+    const int nb = gridDim.x;  // a multiple of 8: XCD x walks entries x*nb/8 ..
+    const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+    if (L >= s_pref[G]) return;
+    int g = 0;
+    {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= L) lo = mid;
+            else hi = mid;
+        }
+        g = lo;
+    }
+    const bool shared = g == p.E;
+    const int fg = shared ? p.fs : p.f;
+    const int rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
+    const int base = shared ? 0 : p.offsets[g];
+    const int K = (MODE == MX_W13) ? p.d : fg, N = (MODE == MX_W13) ? 2 * fg : p.d;
+    const int ntiles = (MODE == MX_W13) ? fg / (BN / 2) : p.d / BN;
+    const int64_t wrb = K / 2, wsb = K / 32;
+    const uint8_t* W = shared ? p.sw : p.w + (int64_t)g * N * wrb;
+    const uint8_t* WS = shared ? p.swsc : p.wsc + (int64_t)g * N * wsb;
+    const int local = L - s_pref[g];
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int m0 = mt * BM;
+    const int mrows = min(BM, rows_g - m0);
+
+    // ---- A sources: chunk slot s = i*256 + tid holds row s/4 at physical chunk s%4; rows past
+    // the group's end re-read the tile's first row (their results are never stored).
+    auto a_row = [&](int r) -> int64_t {  // byte offset of row r's codes; scales at /32
+        if (r >= mrows) r = 0;
+        if (MODE == MX_W13) return (int64_t)(shared ? m0 + r : p.perm[base + m0 + r] / p.k) * p.d;
+        return shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
+    };
+    const int pc = tid & 3;
+    const uint8_t* asrc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int r = i * (THREADS / 4) + (tid >> 2);
+        asrc[i] = p.A + a_row(r) + (pc ^ chunk_swz(r)) * 16;
+    }
+    const uint8_t* assrc = p.As + a_row(tid < BM ? tid : 0) / 32;
+    // ---- B sources.  Gate/up: each wavefront column holds BN/4 gate rows and the matching
+    // BN/4 up rows, so SwiGLU pairs meet in the same lane.
+    auto wrow_of = [&](int n) -> int {
+        if (MODE == MX_W13) {
+            constexpr int H = BN / (2 * NWN);
+            const int h = n / (2 * H), w = n % (2 * H);
+            const int j = nt * (BN / 2) + h * H + (w < H ? w : w - H);
+            return w < H ? j : fg + j;
+        }
+        return nt * BN + n;
+    };
+    const uint8_t* bsrc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int n = i * (THREADS / 2) + (tid >> 1);
+        bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (tid & 1) * 16;
+    }
+    const uint8_t* bssrc = WS + (int64_t)wrow_of(tid < BN ? tid : 0) * wsb;
+
+    auto issue = [&](int kt) {
+        const int st = kt % NS;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) dma16(asrc[i] + kt * 64, sA + st * BM * 64 + (i * THREADS + wv * 64) * 16);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) dma16(bsrc[i] + kt * 32, sB + st * BN * 32 + (i * THREADS + wv * 64) * 16);
+        if ((kt & 1) == 0) {  // scales of stages kt and kt+1: blocks 2kt .. 2kt+3, one dword per row
+            const int sbuf = (kt >> 1) & 1;
+            if (tid < BM) dma4(assrc + (kt >> 1) * 4, sSA + sbuf * BM + wv * 64);
+            if (tid < BN) dma4(bssrc + (kt >> 1) * 4, sSB + sbuf * BN + wv * 64);
+        }
+    };
+
+    f32x16_t acc[2][NT32];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < NT32; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.0f;
+
+    const int l32 = lane & 31, hk = lane >> 5;
+    const int fc0 = (hk ^ chunk_swz(l32)) * 16, fc1 = ((2 + hk) ^ chunk_swz(l32)) * 16;
+    const int nk = K / BK;
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt % NS;
+        asm volatile("" ::: "memory");
+        if (kt + 1 < nk) VM_WAIT(OPS);
+        else VM_WAIT(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + 2 < nk) issue(kt + 2);
+
+        const int sbuf = (kt >> 1) & 1, sh8 = 8 * ((kt & 1) * 2 + hk);
+        v8i_t af[2];
+        int sa[2];
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            const int r = wm * 64 + ms * 32 + l32;
+            const uint4 lo = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc0);
+            const uint4 hi = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc1);
+            af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sa[ms] = (int)((sSA[sbuf * BM + r] >> sh8) & 0xFFu);
+        }
+#pragma unroll
+        for (int ns = 0; ns < NT32; ++ns) {
+            const int n = wn * WN + ns * 32 + l32;
+            const uint4 b = *reinterpret_cast<const uint4*>(sB + st * BN * 32 + n * 32 + hk * 16);
+            const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+            const int sb = (int)((sSB[sbuf * BN + n] >> sh8) & 0xFFu);
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, sa[ms],
+                                                                              0, sb);
+        }
+    }
+
+    // ---- epilogue: accumulator j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32
+    if constexpr (MODE == MX_W13) {
+        // SwiGLU in place of the gate accumulators, then MXFP8 quantisation of a: the tile's
+        // 128 a-columns of 64 rows at a time are staged in LDS as fp32, and each thread
+        // quantises one (row, 32-column block).
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < NT32 / 2; ++ns)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
+                    acc[ms][ns][j] = gt / (1.0f + expf(-gt)) * up;
+                }
+        float* o_st = reinterpret_cast<float*>(smem);
+        const int col0 = nt * (BN / 2);
+        const int64_t rowbytes = shared ? p.fs : p.f;
+        uint8_t* qbase = p.aq + (shared ? (int64_t)P * p.f : 0);
+        uint8_t* sbase = p.aqs + (shared ? (int64_t)P * (p.f / 32) : 0);
+        const int qrow0 = shared ? m0 : base + m0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads();
+            if (wm == half) {
+#pragma unroll
+                for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int r = ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
+#pragma unroll
+                        for (int ns = 0; ns < NT32 / 2; ++ns) o_st[r * APITCH + wn * (WN / 2) + ns * 32 + l32] = acc[ms][ns][j];
+                    }
+            }
+            __syncthreads();
+            const int rr = tid >> 2, cb = tid & 3;
+            const int row = half * 64 + rr;
+            if (row < mrows) {
+                float v[32];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float4 t = *reinterpret_cast<const float4*>(&o_st[rr * APITCH + cb * 32 + q * 4]);
+                    v[4 * q] = t.x;
+                    v[4 * q + 1] = t.y;
+                    v[4 * q + 2] = t.z;
+                    v[4 * q + 3] = t.w;
+                }
+                uint32_t code[8];
+                const uint32_t sb = mx_block(v, code);
+                const int64_t qr = (int64_t)(qrow0 + row);
+                uint4* dst = reinterpret_cast<uint4*>(qbase + qr * rowbytes + col0 + cb * 32);
+                dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+                dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+                sbase[qr * (rowbytes / 32) + col0 / 32 + cb] = (uint8_t)sb;
+            }
+        }
+    } else {
+        // bf16 outputs staged in LDS, then whole 16-byte row chunks stored
+        uint16_t* o_st = reinterpret_cast<uint16_t*>(smem);
+        __syncthreads();
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns) o_st[r * OP + wn * WN + ns * 32 + l32] = f32_to_bf16(acc[ms][ns][j]);
+            }
+        __syncthreads();
+        constexpr int CH = BN / 8;
+        const int col0 = nt * BN;
+        for (int i = tid; i < BM * CH; i += THREADS) {
+            const int r = i / CH, ch = i % CH;
+            if (r >= mrows) continue;
+            const int row = m0 + r;
+            const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
+            uint16_t* o = (shared ? p.y_sh + (int64_t)row * p.d : p.y + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+            *reinterpret_cast<uint4*>(o) = v;
+        }
+    }
+}
+
+static unsigned mx_grid8(int64_t tiles) {
+    int64_t g = (tiles + 7) / 8 * 8;
+    return (unsigned)(g < 8 ? 8 : g);
+}
+
+static int64_t mx_max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t routed_mt = (P + 127) / 128 + (P < E ? P : E);
+    const int64_t shared_mt = n_shared ? (T + 127) / 128 : 0;
+    return routed_mt * rows_nt + shared_mt * shared_nt;
+}
+
+hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t* perm, const int32_t* offsets,
+                             const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s, uint8_t* aq,
+                             uint8_t* aqs, int T, int d, int f, int fs, int k, int E, int n_shared,
+                             const uint8_t* mask, hipStream_t st) {
+    constexpr int BN = 256;
+    MxGemmArgs p{xq, xs, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, aq, aqs,
+                 nullptr, nullptr, T, d, f, fs, k, E, n_shared, mask};
+    const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
+    MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t* offsets, const void* w2,
+                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y, uint16_t* y_shared,
+                            int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
+                            hipStream_t st) {
+    constexpr int BN = 128;
+    MxGemmArgs p{aq, aqs, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, nullptr,
+                 y, y_shared, T, d, f, fs, k, E, n_shared, mask};
+    const int nt = d / BN;
+    const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
+    MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN>), dim3(grid), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

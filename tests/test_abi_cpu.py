@@ -64,6 +64,8 @@ def _layer(shape, x=FAKE, wr=FAKE, out=FAKE, w=None, ws=FAKE, ws_bytes=1 << 40):
     (dict(weight_dtype=moe.MOE_NVFP4, n_shared=1, shared_d_ff=80), moe.MOE_ERR_INVALID_ARG),
     (dict(d_model=100), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=1 << 20), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=moe.F_MX_GEMM), moe.MOE_ERR_UNSUPPORTED),                    # MX GEMM needs MXFP4 weights
+    (dict(weight_dtype=moe.MOE_NVFP4, flags=moe.F_MX_GEMM), moe.MOE_ERR_UNSUPPORTED),
     (dict(flags=moe.F_FORCE_GEMV | moe.F_FORCE_GEMM), moe.MOE_ERR_INVALID_ARG),
 ])
 def test_invalid_shapes_rejected(kw, status):
@@ -122,6 +124,24 @@ def test_other_entry_points_validate():
     assert L.moe_nvfp4_dequant(FAKE, FAKE + 1, 1.0, 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_nvfp4_dequant(FAKE, None, 1.0, 4, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 0, 64, FAKE, None) == moe.MOE_OK
+    assert L.moe_mxfp8_quantize(FAKE, moe.MOE_BF16, 4, 48, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(FAKE, moe.MOE_MXFP4, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(FAKE + 4, moe.MOE_F32, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp8_quantize(FAKE, moe.MOE_F32, 0, 64, FAKE, FAKE, None) == moe.MOE_OK
+    # the MX stages: MXFP4 weights and 128-multiple sizes only; argument checks before any launch
+    mx = _shape(weight_dtype=moe.MOE_MXFP4, d_model=256, d_ff=128)
+    W4 = moe.Weights(w13=FAKE, w2=FAKE, w13_scale=FAKE, w2_scale=FAKE)
+    assert L.moe_mx_gate_up(ctypes.byref(_shape()), FAKE, FAKE, FAKE, ctypes.byref(W4), FAKE, FAKE, FAKE, 1 << 40,
+                            None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_gate_up(ctypes.byref(_shape(weight_dtype=moe.MOE_MXFP4, d_model=96 * 2, d_ff=128)), FAKE, FAKE,
+                            FAKE, ctypes.byref(W4), FAKE, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_mx_gate_up(ctypes.byref(mx), FAKE, FAKE, FAKE, ctypes.byref(W4), None, FAKE, FAKE, 1 << 40,
+                            None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_gate_up(ctypes.byref(mx), FAKE, FAKE, FAKE, ctypes.byref(W4), FAKE, FAKE, FAKE, 1,
+                            None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_mx_down(ctypes.byref(mx), FAKE, FAKE, FAKE, ctypes.byref(W4), None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mx_down(ctypes.byref(_shape(weight_dtype=moe.MOE_MXFP4, d_model=256, d_ff=128, T=0)), None, None,
+                         None, ctypes.byref(W4), None, None, None) == moe.MOE_OK
     arr = (ctypes.c_void_p * 1)(FAKE)
     assert L.moe_stack_forward(ctypes.byref(s), -1, FAKE, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE + 8, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG

@@ -227,6 +227,41 @@ def test_mx_gemm_layer_matches_numpy_quantise_then_multiply():
     assert 1e-3 < err < 0.2, err
 
 
+def test_swiglu_act_is_the_grouped_ffn_intermediate():
+    """moe_ref_swiglu_act: numpy silu(Wg x) * (Wu x) per sorted slot (plain), and under the MX
+    flag the down projection of its MXFP8-rounded rows gives the grouped FFN's output."""
+    s = mi.LayerSpec("act_small", 5, 64, 64, 4, 2, 1, 32, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=73)
+    x = mi.host_x(s)
+    wr, b = mi.host_router(s)
+    w, sh = mi.host_experts(s), mi.host_experts(s, shared=True)
+    l32, _ = oracle.router_logits(s, x, wr, b)
+    idx, _ = oracle.topk(s, l32)
+    _, off, perm, _ = oracle.permute(s, idx)
+
+    def deq(codes, sc):
+        return oracle.mxfp4_dequant(codes.reshape(-1, codes.shape[-1]), sc.reshape(-1, sc.shape[-1])).astype(
+            np.float64).reshape(*codes.shape[:-1], -1)
+
+    W13, W2 = deq(w["w13"], w["w13_scale"]), deq(w["w2"], w["w2_scale"])
+    S13 = deq(sh["w13"], sh["w13_scale"])[0]
+    xf = bf16_to_f64(x)
+    a, ash = oracle.swiglu_act(s, x, perm, off, w, sh)
+    for i in range(s.T * s.k):
+        e = int(np.searchsorted(off, i, side="right") - 1)
+        h = W13[e] @ xf[perm[i] // s.k]
+        np.testing.assert_allclose(a[i], h[:s.f] / (1.0 + np.exp(-h[:s.f])) * h[s.f:], rtol=1e-12, atol=1e-15)
+    for t in range(s.T):
+        h = S13 @ xf[t]
+        fs = s.f_shared
+        np.testing.assert_allclose(ash[t], h[:fs] / (1.0 + np.exp(-h[:fs])) * h[fs:], rtol=1e-12, atol=1e-15)
+    am, _ = oracle.swiglu_act(s, x, perm, off, w, sh, flags=oracle.MX_GEMM)
+    ys, _ = oracle.grouped_ffn(s, x, perm, off, w, sh, flags=oracle.MX_GEMM)
+    for i in range(s.T * s.k):
+        e = int(np.searchsorted(off, i, side="right") - 1)
+        np.testing.assert_allclose(ys[i], W2[e] @ _np_mx(am[i].astype(np.float32)[None, :])[0], rtol=1e-12,
+                                   atol=1e-15)
+
+
 def test_mx_gemm_flag_needs_mxfp4_weights():
     s = mi.spec("c0")
     x = mi.host_x(s)
