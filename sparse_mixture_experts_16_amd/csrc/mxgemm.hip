@@ -141,15 +141,22 @@ struct MxGemmArgs {
     const uint8_t* mask;     // nullable [E + 1]: groups whose byte is 0 get no tiles
 };
 
-template <int MODE, int BN>
+// SCB: scale bytes fetched per row at a time (4 = two stages, 16 = eight stages; 16 needs the
+// row's block count K/32 to be a multiple of 16).
+template <int MODE, int BN, int NS, int SCB>
 __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
-    constexpr int BM = 128, BK = 64, NS = 3, NWN = 2, THREADS = 256;
+    constexpr int BM = 128, BK = 64, NWN = 2, THREADS = 256;
+    static_assert(NS == 3 || NS == 4, "ring depth");
+    static_assert(SCB == 4 || SCB == 16, "scale fetch");
+    constexpr int SST = SCB / 2;                              // stages covered by one scale fetch
+    constexpr int SB = (SCB == 16) ? 2 : (NS + 2) / 2;        // scale groups in flight at once
+    constexpr int SW = SCB / 4;                               // scale dwords per row per group
     constexpr int WN = BN / NWN, NT32 = WN / 32;
     constexpr int NA = BM * 4 / THREADS;  // 16-byte A chunks per thread per stage (rows of 64 bytes)
     constexpr int NB = BN * 2 / THREADS;  // 16-byte B chunks per thread per stage (rows of 32 bytes)
     constexpr int OPS = NA + NB;          // loads one stage adds per thread (the scale dwords not counted)
-    static_assert(NA >= 1 && NB >= 1 && OPS < 16, "tile / thread count");
-    constexpr int SZ_A = NS * BM * 64, SZ_B = NS * BN * 32, SZ_SA = 2 * BM * 4, SZ_SB = 2 * BN * 4;
+    static_assert(NA >= 1 && NB >= 1 && (NS - 2) * OPS < 16, "tile / thread count");
+    constexpr int SZ_A = NS * BM * 64, SZ_B = NS * BN * 32, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
     constexpr int APITCH = 132;  // fp32 a-values per staged row (W13 epilogue, 64 rows at a time)
     constexpr int OP = BN + 8;   // bf16 per staged output row (W2 epilogue)
     constexpr int SZ_EP = (MODE == MX_W13) ? 64 * APITCH * 4 : BM * OP * 2;
@@ -254,10 +261,15 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         for (int i = 0; i < NA; ++i) dma16(asrc[i] + kt * 64, sA + st * BM * 64 + (i * THREADS + wv * 64) * 16);
 #pragma unroll
         for (int i = 0; i < NB; ++i) dma16(bsrc[i] + kt * 32, sB + st * BN * 32 + (i * THREADS + wv * 64) * 16);
-        if ((kt & 1) == 0) {  // scales of stages kt and kt+1: blocks 2kt .. 2kt+3, one dword per row
-            const int sbuf = (kt >> 1) & 1;
-            if (tid < BM) dma4(assrc + (kt >> 1) * 4, sSA + sbuf * BM + wv * 64);
-            if (tid < BN) dma4(bssrc + (kt >> 1) * 4, sSB + sbuf * BN + wv * 64);
+        if (kt % SST == 0) {  // scales of stages kt .. kt+SST-1: blocks 2kt .. 2kt+SCB-1 of each row
+            const int grp = kt / SST, sbuf = grp % SB;
+            if constexpr (SCB == 16) {
+                if (tid < BM) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
+                if (tid < BN) dma16(bssrc + grp * 16, sSB + (sbuf * BN + wv * 64) * SW);
+            } else {
+                if (tid < BM) dma4(assrc + grp * 4, sSA + sbuf * BM + wv * 64);
+                if (tid < BN) dma4(bssrc + grp * 4, sSB + sbuf * BN + wv * 64);
+            }
         }
     };
 
@@ -272,18 +284,24 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     const int l32 = lane & 31, hk = lane >> 5;
     const int fc0 = (hk ^ chunk_swz(l32)) * 16, fc1 = ((2 + hk) ^ chunk_swz(l32)) * 16;
     const int nk = K / BK;
-    issue(0);
-    if (nk > 1) issue(1);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nk) issue(i);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt % NS;
+        // wait for stage kt; the stages issued after it (up to NS - 2) stay in flight
         asm volatile("" ::: "memory");
-        if (kt + 1 < nk) VM_WAIT(OPS);
+        const int newer = min(NS - 2, nk - 1 - kt);
+        if (newer >= 2) VM_WAIT(2 * OPS);
+        else if (newer == 1) VM_WAIT(OPS);
         else VM_WAIT(0);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + 2 < nk) issue(kt + 2);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
 
-        const int sbuf = (kt >> 1) & 1, sh8 = 8 * ((kt & 1) * 2 + hk);
+        // this lane's block, 2kt + hk, inside its row's scale group
+        const int sbuf = (kt / SST) % SB, sblk = 2 * (kt % SST) + hk;
+        const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
         v8i_t af[2];
         int sa[2];
 #pragma unroll
@@ -292,14 +310,14 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
             const uint4 lo = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc0);
             const uint4 hi = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc1);
             af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sa[ms] = (int)((sSA[sbuf * BM + r] >> sh8) & 0xFFu);
+            sa[ms] = (int)((sSA[(sbuf * BM + r) * SW + sw] >> sh8) & 0xFFu);
         }
 #pragma unroll
         for (int ns = 0; ns < NT32; ++ns) {
             const int n = wn * WN + ns * 32 + l32;
             const uint4 b = *reinterpret_cast<const uint4*>(sB + st * BN * 32 + n * 32 + hk * 16);
             const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-            const int sb = (int)((sSB[sbuf * BN + n] >> sh8) & 0xFFu);
+            const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
                 acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, sa[ms],
@@ -408,7 +426,8 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
     MxGemmArgs p{xq, xs, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, aq, aqs,
                  nullptr, nullptr, T, d, f, fs, k, E, n_shared, mask};
     const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
-    MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN>), dim3(grid), dim3(256), 0, st, p);
+    if (d % 512 == 0) MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, 3, 16>), dim3(grid), dim3(256), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, 3, 4>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -421,7 +440,9 @@ hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t
                  y, y_shared, T, d, f, fs, k, E, n_shared, mask};
     const int nt = d / BN;
     const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
-    MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN>), dim3(grid), dim3(256), 0, st, p);
+    if (f % 512 == 0 && (!n_shared || fs % 512 == 0))
+        MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN, 3, 16>), dim3(grid), dim3(256), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN, 3, 4>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -5,12 +5,15 @@ cores, activations quantised to MXFP8 (OCP Microscaling Formats v1.0) before eac
   at many block scales, fp32 subnormals, zero blocks, saturation, NaN / infinity blocks, bf16 rows.
 - The two contractions separately, each from exact inputs.  Gate/up: the quantised SwiGLU output
   codes against the oracle's, which quantise the oracle's fp64 activations rounded to fp32.  The
-  GPU's activations are fp32 MFMA sums, so where an activation lies within the rounding error of
-  an fp32 sum (bounded by (d + 2) * 2^-24 * sum |terms|, carried through silu) of an E4M3
-  rounding midpoint, or a block maximum that close to a power of two, both codes are correct:
-  there the GPU may differ, by one grid step (or the block's scale), and nowhere else.  Down
-  projection: fed the oracle's own codes, against the oracle's down projection of them, to the
-  layer tolerance.
+  GPU's activations come from the scaled fp8 x fp4 MFMA, which does not sum its products at full
+  fp32 precision: measured on gfx950, products far below the largest of their group are dropped
+  (448 + 63 * 2^-9 returns 448.109 instead of 448.123; 1 + 63 * 2^-9 is exact).  We bound that
+  sum's error by 2^-7 * sum |products| (at most 7 dropped terms per group of 8, each under 2^-10
+  of the group's largest), carried through silu.  Where an activation lies that close to an E4M3
+  rounding midpoint, or a block maximum that close to a power of two, both codes are correct and
+  the GPU may differ, by at most that error plus one grid step; everywhere else the codes must be
+  equal, and at most 2% of them may differ at all.  Down projection: fed the oracle's own codes,
+  against the oracle's down projection of them, to the layer tolerance.
 - The whole layer and the grouped FFN: routing bit for bit, the rms error against the quantising
   oracle below 1% and a tenth of the MX layer's own error against the exact layer (reported).
 """
@@ -96,6 +99,8 @@ SMALL = [
     mi.LayerSpec("mx_ragged", 257, 256, 128, 12, 2, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=23),
     mi.LayerSpec("mx_shared", 64, 256, 128, 8, 8, 1, 128, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=24),
     mi.LayerSpec("mx_shared_wide", 300, 384, 256, 16, 4, 1, 384, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=25),
+    # K multiples of 512: the kernels fetch each row's scales 16 bytes at a time
+    mi.LayerSpec("mx_k512", 160, 512, 512, 8, 2, 1, 1024, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=26),
 ]
 
 
@@ -114,7 +119,7 @@ def _undecided(a_f64, xq_rows, w13, f):
     legitimately flip: within the bound of the fp32 sums of a rounding midpoint (or, for a whole
     block, of a power-of-two maximum).  xq_rows [R, d] are the quantised inputs, w13 [R, 2f, d] (or
     [2f, d]) the gate/up weights of each row."""
-    gam = (xq_rows.shape[1] + 2) * 2.0 ** -24
+    gam = 2.0 ** -7 + (xq_rows.shape[1] + 2) * 2.0 ** -24
     if w13.ndim == 2:
         w13 = np.broadcast_to(w13, (xq_rows.shape[0],) + w13.shape)
     h = np.einsum("rnd,rd->rn", w13, xq_rows)
@@ -139,7 +144,7 @@ def _undecided(a_f64, xq_rows, w13, f):
     p2 = 2.0 ** lg
     bnear = (np.abs(amax - p2) <= damax) | (np.abs(2 * p2 - amax) <= damax)
     return (near.reshape(R, f), np.broadcast_to(bnear, blk.shape).reshape(R, f), bnear[..., 0],
-            (step * X).reshape(R, f))
+            (step * X).reshape(R, f), da)
 
 
 def _dev_weights(w, sh):
@@ -186,7 +191,7 @@ def test_mx_gate_up_codes_match_oracle(s):
     total_diff = 0
     for act, f, gc, gs, xr, w13 in parts:
         rc, rs = oracle.mxfp8_quantize(act.astype(np.float32))
-        near, bnear_el, bnear, step = _undecided(act, xr, w13, f)
+        near, bnear_el, bnear, step, da = _undecided(act, xr, w13, f)
         # scales: equal except where the block maximum is undecided
         assert np.all((gs == rs) | bnear), f"{int(((gs != rs) & ~bnear).sum())} decided block scales differ"
         same_scale = np.repeat(gs == rs, 32, axis=1)
@@ -196,11 +201,15 @@ def test_mx_gate_up_codes_match_oracle(s):
         bad = diff & same_scale & ~near & ~bnear_el
         assert not bad.any(), f"{int(bad.sum())} decided codes differ (of {int(diff.sum())} differing)"
         moved = np.abs(gv - rv)
-        assert np.all(moved[diff & same_scale] <= 1.0001 * step[diff & same_scale]), \
-            "an undecided code moved by more than one grid step"
+        far = diff & same_scale & (moved > 1.0001 * (step + da))
+        if far.any():
+            r, c = np.argwhere(far)[0]
+            raise AssertionError(f"{int(far.sum())} undecided codes moved by more than one grid step, e.g. row {r} "
+                                 f"col {c}: a {act[r, c]:.9g}, gpu {gv[r, c]:.9g}, oracle {rv[r, c]:.9g}, "
+                                 f"step {step[r, c]:.6g}, block scale byte {int(gs[r, c // 32])}")
         total_diff += int(diff.sum())
     print(f"{s.name}: {total_diff} of {n_codes} activation codes differ, all at undecided roundings")
-    assert total_diff <= max(8, n_codes // 200)
+    assert total_diff <= max(8, n_codes // 50)
 
 
 @pytest.mark.parametrize("s", SMALL, ids=lambda s: s.name)
