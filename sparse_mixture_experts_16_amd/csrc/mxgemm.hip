@@ -141,33 +141,54 @@ struct MxGemmArgs {
     const uint8_t* mask;     // nullable [E + 1]: groups whose byte is 0 get no tiles
 };
 
-// SCB: scale bytes fetched per row at a time (4 = two stages, 16 = eight stages; 16 needs the
-// row's block count K/32 to be a multiple of 16).
-template <int MODE, int BN, int NS, int SCB>
+// Chunk swizzles of the LDS tiles: 16-byte chunk c of row r sits at physical chunk c ^ swz(r), so
+// that a wavefront's fragment reads (consecutive rows, one chunk each) fall on distinct banks.
+template <int CH>  // chunks per row
+__device__ __forceinline__ int tile_swz(int r) {
+    if constexpr (CH == 8) return (r >> 1) & 7;   // 128-byte rows
+    else if constexpr (CH == 4) return chunk_swz(r);
+    else return 0;                                // 32-byte rows: two chunks, no conflict to remove
+}
+template <int CH>  // B rows (weights) of CH chunks
+__device__ __forceinline__ int btile_swz(int r) {
+    if constexpr (CH == 4) return (r >> 2) & 3;   // 64-byte rows
+    else return 0;
+}
+
+// BK: K elements per stage (64: A rows of 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring
+// depth.  SCB: scale bytes fetched per row at a time (4 or 16; 16 needs K % 512 == 0).
+template <int MODE, int BN, int NS, int SCB, int BK>
 __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
-    constexpr int BM = 128, BK = 64, NWN = 2, THREADS = 256;
-    static_assert(NS == 3 || NS == 4, "ring depth");
+    constexpr int BM = 128, NWN = 2, THREADS = 256;
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
     static_assert(SCB == 4 || SCB == 16, "scale fetch");
-    constexpr int SST = SCB / 2;                              // stages covered by one scale fetch
-    constexpr int SB = (SCB == 16) ? 2 : (NS + 2) / 2;        // scale groups in flight at once
+    static_assert(BK == 64 || BK == 128, "stage depth");
+    constexpr int KS = BK / 64;                               // MFMA K steps per stage
+    constexpr int ACH = BK / 16, BCH = BK / 32;               // 16-byte chunks per A row / B row
+    constexpr int SBK = BK / 32;                              // scale blocks per row per stage
+    static_assert(SCB % SBK == 0, "scale groups hold whole stages");
+    constexpr int SST = SCB / SBK;                            // stages covered by one scale fetch
+    constexpr int SB = (SST >= NS - 1) ? 2 : NS;              // scale groups in flight at once
     constexpr int SW = SCB / 4;                               // scale dwords per row per group
     constexpr int WN = BN / NWN, NT32 = WN / 32;
-    constexpr int NA = BM * 4 / THREADS;  // 16-byte A chunks per thread per stage (rows of 64 bytes)
-    constexpr int NB = BN * 2 / THREADS;  // 16-byte B chunks per thread per stage (rows of 32 bytes)
-    constexpr int OPS = NA + NB;          // loads one stage adds per thread (the scale dwords not counted)
+    constexpr int NA = BM * ACH / THREADS;                    // A chunks per thread per stage
+    constexpr int NB = BN * BCH / THREADS;                    // B chunks per thread per stage
+    constexpr int OPS = NA + NB;                              // loads one stage adds (scale fetches not counted)
     static_assert(NA >= 1 && NB >= 1 && (NS - 2) * OPS < 16, "tile / thread count");
-    constexpr int SZ_A = NS * BM * 64, SZ_B = NS * BN * 32, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
+    constexpr int SZ_A = NS * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
     constexpr int APITCH = 132;  // fp32 a-values per staged row (W13 epilogue, 64 rows at a time)
     constexpr int OP = BN + 8;   // bf16 per staged output row (W2 epilogue)
     constexpr int SZ_EP = (MODE == MX_W13) ? 64 * APITCH * 4 : BM * OP * 2;
     constexpr int SZ_RING = SZ_A + SZ_B + SZ_SA + SZ_SB;
-    constexpr int SZ = SZ_RING > SZ_EP ? SZ_RING : SZ_EP;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ + (MOE_MAX_E + 2) * 4];
+    constexpr int SZ_LIST = (MOE_MAX_E + 2) * 4;  // the tile list prefix, read before the ring fills
+    constexpr int SZ0 = SZ_RING > SZ_EP ? SZ_RING : SZ_EP;
+    constexpr int SZ = SZ0 > SZ_LIST ? SZ0 : SZ_LIST;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ];
     uint8_t* sA = smem;
     uint8_t* sB = smem + SZ_A;
     uint32_t* sSA = reinterpret_cast<uint32_t*>(smem + SZ_A + SZ_B);
     uint32_t* sSB = reinterpret_cast<uint32_t*>(smem + SZ_A + SZ_B + SZ_SA);
-    int* s_pref = reinterpret_cast<int*>(smem + SZ);
+    int* s_pref = reinterpret_cast<int*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv / NWN, wn = wv % NWN;
     const int G = p.E + p.n_shared;
@@ -207,6 +228,8 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         }
         g = lo;
     }
+    const int local = L - s_pref[g];
+    __syncthreads();  // the list shares its LDS with the ring filled below
     const bool shared = g == p.E;
     const int fg = shared ? p.fs : p.f;
     const int rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
@@ -216,24 +239,22 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     const int64_t wrb = K / 2, wsb = K / 32;
     const uint8_t* W = shared ? p.sw : p.w + (int64_t)g * N * wrb;
     const uint8_t* WS = shared ? p.swsc : p.wsc + (int64_t)g * N * wsb;
-    const int local = L - s_pref[g];
     const int mt = local / ntiles, nt = local % ntiles;
     const int m0 = mt * BM;
     const int mrows = min(BM, rows_g - m0);
 
-    // ---- A sources: chunk slot s = i*256 + tid holds row s/4 at physical chunk s%4; rows past
-    // the group's end re-read the tile's first row (their results are never stored).
+    // ---- A sources: chunk slot s = i*256 + tid holds row s/ACH at physical chunk s%ACH; rows
+    // past the group's end re-read the tile's first row (their results are never stored).
     auto a_row = [&](int r) -> int64_t {  // byte offset of row r's codes; scales at /32
         if (r >= mrows) r = 0;
         if (MODE == MX_W13) return (int64_t)(shared ? m0 + r : p.perm[base + m0 + r] / p.k) * p.d;
         return shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
     };
-    const int pc = tid & 3;
     const uint8_t* asrc[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const int r = i * (THREADS / 4) + (tid >> 2);
-        asrc[i] = p.A + a_row(r) + (pc ^ chunk_swz(r)) * 16;
+        const int slot = i * THREADS + tid, r = slot / ACH;
+        asrc[i] = p.A + a_row(r) + ((slot % ACH) ^ tile_swz<ACH>(r)) * 16;
     }
     const uint8_t* assrc = p.As + a_row(tid < BM ? tid : 0) / 32;
     // ---- B sources.  Gate/up: each wavefront column holds BN/4 gate rows and the matching
@@ -250,18 +271,19 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     const uint8_t* bsrc[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const int n = i * (THREADS / 2) + (tid >> 1);
-        bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (tid & 1) * 16;
+        const int slot = i * THREADS + tid, n = slot / BCH;
+        bsrc[i] = W + (int64_t)wrow_of(n) * wrb + ((slot % BCH) ^ btile_swz<BCH>(n)) * 16;
     }
     const uint8_t* bssrc = WS + (int64_t)wrow_of(tid < BN ? tid : 0) * wsb;
 
     auto issue = [&](int kt) {
         const int st = kt % NS;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) dma16(asrc[i] + kt * 64, sA + st * BM * 64 + (i * THREADS + wv * 64) * 16);
+        for (int i = 0; i < NA; ++i) dma16(asrc[i] + kt * BK, sA + st * BM * BK + (i * THREADS + wv * 64) * 16);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) dma16(bsrc[i] + kt * 32, sB + st * BN * 32 + (i * THREADS + wv * 64) * 16);
-        if (kt % SST == 0) {  // scales of stages kt .. kt+SST-1: blocks 2kt .. 2kt+SCB-1 of each row
+        for (int i = 0; i < NB; ++i)
+            dma16(bsrc[i] + kt * (BK / 2), sB + st * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
+        if (kt % SST == 0) {  // scales of stages kt .. kt+SST-1: SCB blocks of each row
             const int grp = kt / SST, sbuf = grp % SB;
             if constexpr (SCB == 16) {
                 if (tid < BM) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
@@ -282,8 +304,10 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
             for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.0f;
 
     const int l32 = lane & 31, hk = lane >> 5;
-    const int fc0 = (hk ^ chunk_swz(l32)) * 16, fc1 = ((2 + hk) ^ chunk_swz(l32)) * 16;
     const int nk = K / BK;
+    // a wavefront whose 64 rows all lie past the group's end only loads and synchronises; its
+    // matrix-core time goes to the other workgroup on the CU
+    const bool live = wm * 64 < mrows;
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i)
         if (i < nk) issue(i);
@@ -299,29 +323,36 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         asm volatile("" ::: "memory");
         if (kt + NS - 1 < nk) issue(kt + NS - 1);
 
-        // this lane's block, 2kt + hk, inside its row's scale group
-        const int sbuf = (kt / SST) % SB, sblk = 2 * (kt % SST) + hk;
-        const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
-        v8i_t af[2];
-        int sa[2];
+        if (!live) continue;
+        const int sbuf = (kt / SST) % SB;
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-            const int r = wm * 64 + ms * 32 + l32;
-            const uint4 lo = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc0);
-            const uint4 hi = *reinterpret_cast<const uint4*>(sA + st * BM * 64 + r * 64 + fc1);
-            af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sa[ms] = (int)((sSA[(sbuf * BM + r) * SW + sw] >> sh8) & 0xFFu);
-        }
+        for (int u = 0; u < KS; ++u) {
+            // this lane's block inside its row's scale group: (kt % SST) * SBK + 2u + hk
+            const int sblk = (kt % SST) * SBK + 2 * u + hk;
+            const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
+            v8i_t af[2];
+            int sa[2];
 #pragma unroll
-        for (int ns = 0; ns < NT32; ++ns) {
-            const int n = wn * WN + ns * 32 + l32;
-            const uint4 b = *reinterpret_cast<const uint4*>(sB + st * BN * 32 + n * 32 + hk * 16);
-            const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-            const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
+            for (int ms = 0; ms < 2; ++ms) {
+                const int r = wm * 64 + ms * 32 + l32;
+                const uint8_t* row = sA + st * BM * BK + r * BK;
+                const uint4 lo = *reinterpret_cast<const uint4*>(row + ((4 * u + hk) ^ tile_swz<ACH>(r)) * 16);
+                const uint4 hi = *reinterpret_cast<const uint4*>(row + ((4 * u + 2 + hk) ^ tile_swz<ACH>(r)) * 16);
+                af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sa[ms] = (int)((sSA[(sbuf * BM + r) * SW + sw] >> sh8) & 0xFFu);
+            }
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, sa[ms],
-                                                                              0, sb);
+            for (int ns = 0; ns < NT32; ++ns) {
+                const int n = wn * WN + ns * 32 + l32;
+                const uint4 b = *reinterpret_cast<const uint4*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
+                                                                ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
+                const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+                const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
+#pragma unroll
+                for (int ms = 0; ms < 2; ++ms)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0,
+                                                                                  sa[ms], 0, sb);
+            }
         }
     }
 
@@ -347,6 +378,7 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         const int qrow0 = shared ? m0 : base + m0;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            if (half * 64 >= mrows) break;  // uniform over the workgroup
             __syncthreads();
             if (wm == half) {
 #pragma unroll
@@ -406,6 +438,12 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     }
 }
 
+// Stage shapes.  Both stages read 128-byte activation rows and 64-byte weight rows per stage into a
+// double-buffered ring with 256-column tiles (76 KB of LDS, two workgroups per CU).  A down
+// projection with d not a multiple of 256 takes 128-column tiles with 64-element stages three deep,
+// the faster of the shapes measured at that tile width.
+constexpr int MX_BK = 128, MX_NS = 2;
+
 static unsigned mx_grid8(int64_t tiles) {
     int64_t g = (tiles + 7) / 8 * 8;
     return (unsigned)(g < 8 ? 8 : g);
@@ -426,8 +464,8 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
     MxGemmArgs p{xq, xs, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, aq, aqs,
                  nullptr, nullptr, T, d, f, fs, k, E, n_shared, mask};
     const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
-    if (d % 512 == 0) MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, 3, 16>), dim3(grid), dim3(256), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, 3, 4>), dim3(grid), dim3(256), 0, st, p);
+    if (d % 512 == 0) MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, MX_NS, 16, MX_BK>), dim3(grid), dim3(256), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, MX_NS, 4, MX_BK>), dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -435,14 +473,20 @@ hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t
                             const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y, uint16_t* y_shared,
                             int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
                             hipStream_t st) {
-    constexpr int BN = 128;
     MxGemmArgs p{aq, aqs, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, nullptr,
                  y, y_shared, T, d, f, fs, k, E, n_shared, mask};
-    const int nt = d / BN;
-    const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
-    if (f % 512 == 0 && (!n_shared || fs % 512 == 0))
-        MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN, 3, 16>), dim3(grid), dim3(256), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BN, 3, 4>), dim3(grid), dim3(256), 0, st, p);
+    const bool scb16 = f % 512 == 0 && (!n_shared || fs % 512 == 0);
+    if (d % 256 == 0) {
+        const int nt = d / 256;
+        const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
+        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(256), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(256), 0, st, p);
+    } else {
+        const int nt = d / 128;
+        const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
+        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 3, 16, 64>), dim3(grid), dim3(256), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 3, 4, 64>), dim3(grid), dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
