@@ -15,9 +15,9 @@
 // epilogue.
 //
 // Tile order: a flat list over (group, m-tile, n-tile), n fastest, built per workgroup from
-// the expert offsets; workgroup b takes list entry (b % 8) * (grid / 8) + b / 8 so that each
-// of the 8 XCDs walks a contiguous stretch of the list and an expert's weight tiles are
-// shared in that XCD's L2.
+// the expert offsets; workgroup b (on XCD b % 8) takes entry b / 8 of the (b % 8)-th eighth of
+// the list, so that each of the 8 XCDs walks an equal contiguous stretch and an expert's weight
+// tiles are shared in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -156,9 +156,13 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
     }
     __syncthreads();
 
-    const int nb = gridDim.x;  // a multiple of 8
-    const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-    if (L >= s_pref[G]) return;
+    // workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of the actual list (the grid is
+    // only a bound on its length), so all eight share the work and each walks a contiguous stretch
+    const int total = s_pref[G];
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;  // gridDim.x / 8 >= ceil(total / 8)
+    const int t_lo = (int)(((int64_t)total * xcd) >> 3), t_hi = (int)(((int64_t)total * (xcd + 1)) >> 3);
+    if (t_lo + j >= t_hi) return;
+    const int L = t_lo + j;
     int g = 0;
     {
         int lo = 0, hi = G;

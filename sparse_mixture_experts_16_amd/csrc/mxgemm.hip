@@ -155,11 +155,14 @@ __device__ __forceinline__ int btile_swz(int r) {
     else return 0;
 }
 
-// BK: K elements per stage (64: A rows of 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring
-// depth.  SCB: scale bytes fetched per row at a time (4 or 16; 16 needs K % 512 == 0).
-template <int MODE, int BN, int NS, int SCB, int BK>
-__global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
-    constexpr int BM = 128, NWN = 2, THREADS = 256;
+// BM x BN output tile: BM / 64 rows of two wavefronts, each 64 x BN/2 (BM = 128: 256 threads, two
+// workgroups per CU; BM = 256: 512 threads, one per CU).  BK: K elements per stage (64: A rows of
+// 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring depth.  SCB: scale bytes fetched per row at a
+// time (4 or 16; 16 needs K % 512 == 0).
+template <int MODE, int BM, int BN, int NS, int SCB, int BK>
+__global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
+    constexpr int NWN = 2, THREADS = BM * 2;
+    static_assert(BM == 128 || BM == 256, "tile rows");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
     static_assert(SCB == 4 || SCB == 16, "scale fetch");
     static_assert(BK == 64 || BK == 128, "stage depth");
@@ -176,9 +179,13 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     constexpr int OPS = NA + NB;                              // loads one stage adds (scale fetches not counted)
     static_assert(NA >= 1 && NB >= 1 && (NS - 2) * OPS < 16, "tile / thread count");
     constexpr int SZ_A = NS * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
-    constexpr int APITCH = 132;  // fp32 a-values per staged row (W13 epilogue, 64 rows at a time)
-    constexpr int OP = BN + 8;   // bf16 per staged output row (W2 epilogue)
-    constexpr int SZ_EP = (MODE == MX_W13) ? 64 * APITCH * 4 : BM * OP * 2;
+    // epilogue: the output tile passes through LDS EPR rows at a time (gate/up: one thread per
+    // (row, 32-column block) of the 128 a-columns)
+    constexpr int EPR = (MODE == MX_W13) ? THREADS / 4 : 128;
+    static_assert(MODE != MX_W13 || BN == 256, "gate/up tiles give 128 a-columns");
+    constexpr int APITCH = 132;  // fp32 a-values per staged row (gate/up)
+    constexpr int OP = BN + 8;   // bf16 per staged output row (down)
+    constexpr int SZ_EP = (MODE == MX_W13) ? EPR * APITCH * 4 : EPR * OP * 2;
     constexpr int SZ_RING = SZ_A + SZ_B + SZ_SA + SZ_SB;
     constexpr int SZ_LIST = (MOE_MAX_E + 2) * 4;  // the tile list prefix, read before the ring fills
     constexpr int SZ0 = SZ_RING > SZ_EP ? SZ_RING : SZ_EP;
@@ -215,9 +222,13 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         if (lane == 63) s_pref[G] = incl;
     }
     __syncthreads();
-    const int nb = gridDim.x;  // a multiple of 8: XCD x walks entries x*nb/8 ..
-    const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-    if (L >= s_pref[G]) return;
+    // workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of the actual list (the grid is
+    // only a bound on its length), so all eight share the work and each walks a contiguous stretch
+    const int total = s_pref[G];
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;  // gridDim.x / 8 >= ceil(total / 8)
+    const int t_lo = (int)(((int64_t)total * xcd) >> 3), t_hi = (int)(((int64_t)total * (xcd + 1)) >> 3);
+    if (t_lo + j >= t_hi) return;
+    const int L = t_lo + j;
     int g = 0;
     {
         int lo = 0, hi = G;
@@ -243,18 +254,21 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     const int m0 = mt * BM;
     const int mrows = min(BM, rows_g - m0);
 
-    // ---- A sources: chunk slot s = i*256 + tid holds row s/ACH at physical chunk s%ACH; rows
-    // past the group's end re-read the tile's first row (their results are never stored).
+    // ---- A sources: chunk slot s = i*THREADS + tid holds row s/ACH at physical chunk s%ACH; rows
+    // past the group's end re-read the tile's first row (their results are never stored), or, with
+    // a two-stage ring (every wait drains all loads), are not loaded at all.
     auto a_row = [&](int r) -> int64_t {  // byte offset of row r's codes; scales at /32
         if (r >= mrows) r = 0;
         if (MODE == MX_W13) return (int64_t)(shared ? m0 + r : p.perm[base + m0 + r] / p.k) * p.d;
         return shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
     };
     const uint8_t* asrc[NA];
+    bool alive[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int slot = i * THREADS + tid, r = slot / ACH;
         asrc[i] = p.A + a_row(r) + ((slot % ACH) ^ tile_swz<ACH>(r)) * 16;
+        alive[i] = NS != 2 || r < mrows;
     }
     const uint8_t* assrc = p.As + a_row(tid < BM ? tid : 0) / 32;
     // ---- B sources.  Gate/up: each wavefront column holds BN/4 gate rows and the matching
@@ -279,7 +293,8 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     auto issue = [&](int kt) {
         const int st = kt % NS;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) dma16(asrc[i] + kt * BK, sA + st * BM * BK + (i * THREADS + wv * 64) * 16);
+        for (int i = 0; i < NA; ++i)
+            if (alive[i]) dma16(asrc[i] + kt * BK, sA + st * BM * BK + (i * THREADS + wv * 64) * 16);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             dma16(bsrc[i] + kt * (BK / 2), sB + st * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
@@ -377,22 +392,22 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
         uint8_t* sbase = p.aqs + (shared ? (int64_t)P * (p.f / 32) : 0);
         const int qrow0 = shared ? m0 : base + m0;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            if (half * 64 >= mrows) break;  // uniform over the workgroup
+        for (int pass = 0; pass < BM / EPR; ++pass) {
+            if (pass * EPR >= mrows) break;  // uniform over the workgroup
             __syncthreads();
-            if (wm == half) {
+            if (wm * 64 / EPR == pass) {
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int r = ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
+                        const int r = (wm * 64) % EPR + ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
 #pragma unroll
                         for (int ns = 0; ns < NT32 / 2; ++ns) o_st[r * APITCH + wn * (WN / 2) + ns * 32 + l32] = acc[ms][ns][j];
                     }
             }
             __syncthreads();
             const int rr = tid >> 2, cb = tid & 3;
-            const int row = half * 64 + rr;
+            const int row = pass * EPR + rr;
             if (row < mrows) {
                 float v[32];
 #pragma unroll
@@ -415,44 +430,55 @@ __global__ void __launch_bounds__(256, 2) mxgemm(MxGemmArgs p) {
     } else {
         // bf16 outputs staged in LDS, then whole 16-byte row chunks stored
         uint16_t* o_st = reinterpret_cast<uint16_t*>(smem);
-        __syncthreads();
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
-#pragma unroll
-                for (int ns = 0; ns < NT32; ++ns) o_st[r * OP + wn * WN + ns * 32 + l32] = f32_to_bf16(acc[ms][ns][j]);
-            }
-        __syncthreads();
         constexpr int CH = BN / 8;
         const int col0 = nt * BN;
-        for (int i = tid; i < BM * CH; i += THREADS) {
-            const int r = i / CH, ch = i % CH;
-            if (r >= mrows) continue;
-            const int row = m0 + r;
-            const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
-            uint16_t* o = (shared ? p.y_sh + (int64_t)row * p.d : p.y + (int64_t)(base + row) * p.d) + col0 + ch * 8;
-            *reinterpret_cast<uint4*>(o) = v;
+#pragma unroll
+        for (int pass = 0; pass < BM / EPR; ++pass) {
+            if (pass * EPR >= mrows) break;  // uniform over the workgroup
+            __syncthreads();
+            if (wm * 64 / EPR == pass) {
+#pragma unroll
+                for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int r = (wm * 64) % EPR + ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
+#pragma unroll
+                        for (int ns = 0; ns < NT32; ++ns)
+                            o_st[r * OP + wn * WN + ns * 32 + l32] = f32_to_bf16(acc[ms][ns][j]);
+                    }
+            }
+            __syncthreads();
+            for (int i = tid; i < EPR * CH; i += THREADS) {
+                const int r = pass * EPR + i / CH, ch = i % CH;
+                if (r >= mrows) continue;
+                const int row = m0 + r;
+                const uint4 v = *reinterpret_cast<const uint4*>(&o_st[(i / CH) * OP + ch * 8]);
+                uint16_t* o =
+                    (shared ? p.y_sh + (int64_t)row * p.d : p.y + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+                *reinterpret_cast<uint4*>(o) = v;
+            }
         }
     }
 }
 
 // Stage shapes.  Both stages read 128-byte activation rows and 64-byte weight rows per stage into a
-// double-buffered ring with 256-column tiles (76 KB of LDS, two workgroups per CU).  A down
-// projection with d not a multiple of 256 takes 128-column tiles with 64-element stages three deep,
-// the faster of the shapes measured at that tile width.
-constexpr int MX_BK = 128, MX_NS = 2;
+// double-buffered ring with 256-column tiles.  A down projection with d not a multiple of 256 takes
+// 128 x 128 tiles with 64-element stages three deep, the faster of the shapes measured at that
+// tile width.
+// 256-row tiles (one 8-wavefront workgroup per CU) measured slower at every ring depth: the two
+// independent workgroups of 128 rows hide each other's load waits.
+constexpr int MX_BM = 128, MX_BK = 128, MX_NS = 2;
 
 static unsigned mx_grid8(int64_t tiles) {
     int64_t g = (tiles + 7) / 8 * 8;
     return (unsigned)(g < 8 ? 8 : g);
 }
 
-static int64_t mx_max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
+// tiles of BM rows over all groups: at most ceil(P / BM) + one ragged tile per group
+static int64_t mx_max_tiles(int BM, int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
     const int64_t P = (int64_t)T * k;
-    const int64_t routed_mt = (P + 127) / 128 + (P < E ? P : E);
-    const int64_t shared_mt = n_shared ? (T + 127) / 128 : 0;
+    const int64_t routed_mt = (P + BM - 1) / BM + (P < E ? P : E);
+    const int64_t shared_mt = n_shared ? (T + BM - 1) / BM : 0;
     return routed_mt * rows_nt + shared_mt * shared_nt;
 }
 
@@ -460,12 +486,14 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
                              const void* w13, const uint8_t* w13s, const void* s13, const uint8_t* s13s, uint8_t* aq,
                              uint8_t* aqs, int T, int d, int f, int fs, int k, int E, int n_shared,
                              const uint8_t* mask, hipStream_t st) {
-    constexpr int BN = 256;
+    constexpr int BM = MX_BM, BN = 256;
     MxGemmArgs p{xq, xs, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, aq, aqs,
                  nullptr, nullptr, T, d, f, fs, k, E, n_shared, mask};
-    const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
-    if (d % 512 == 0) MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, MX_NS, 16, MX_BK>), dim3(grid), dim3(256), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BN, MX_NS, 4, MX_BK>), dim3(grid), dim3(256), 0, st, p);
+    const unsigned grid =
+        mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
+    if (d % 512 == 0)
+        MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
     return hipGetLastError();
 }
 
@@ -477,15 +505,17 @@ hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t
                  y, y_shared, T, d, f, fs, k, E, n_shared, mask};
     const bool scb16 = f % 512 == 0 && (!n_shared || fs % 512 == 0);
     if (d % 256 == 0) {
+        constexpr int BM = MX_BM;
         const int nt = d / 256;
-        const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
-        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(256), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(256), 0, st, p);
+        const unsigned grid = mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, nt, nt));
+        if (scb16)
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
     } else {
         const int nt = d / 128;
-        const unsigned grid = mx_grid8(mx_max_tiles(T, k, E, n_shared, nt, nt));
-        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 3, 16, 64>), dim3(grid), dim3(256), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 3, 4, 64>), dim3(grid), dim3(256), 0, st, p);
+        const unsigned grid = mx_grid8(mx_max_tiles(128, T, k, E, n_shared, nt, nt));
+        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 128, 3, 16, 64>), dim3(grid), dim3(256), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 128, 3, 4, 64>), dim3(grid), dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }
