@@ -283,6 +283,9 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
     const int fc0 = ((0 + hk) ^ chunk_swz(l32)) * 8, fc1 = ((2 + hk) ^ chunk_swz(l32)) * 8;
 
     const int nk = K / BK;
+    // a wavefront whose 64 rows all lie past the group's end only loads and synchronises; its
+    // matrix-core time goes to the other workgroup on the CU
+    const bool live = wm * 64 < mrows;
     issue(0);
     if (nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
@@ -293,6 +296,7 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (kt + 2 < nk) issue(kt + 2);
+        if (!live) continue;
 
         uint32_t sc_w[NT32];
         if (WT == 2) {
