@@ -26,6 +26,11 @@
 namespace moe {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
+// Fragment reads from LDS are loads of this vector type, not of a struct: a load that carries no
+// type-based alias information makes the compiler's wait insertion drain every global -> LDS
+// load in flight before it, which would serialise the ring (the explicit vmcnt waits and
+// barriers below already order each stage's loads before its reads).
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 
 enum { MX_W13 = 0, MX_W2 = 1 };
 
@@ -159,7 +164,14 @@ __device__ __forceinline__ int btile_swz(int r) {
 // workgroups per CU; BM = 256: 512 threads, one per CU).  BK: K elements per stage (64: A rows of
 // 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring depth.  SCB: scale bytes fetched per row at a
 // time (4 or 16; 16 needs K % 512 == 0).
-template <int MODE, int BM, int BN, int NS, int SCB, int BK>
+// SPLIT: the weights (B, streamed from HBM) keep the NS-deep ring, issued NS - 1 stages ahead,
+// while the activations (A, re-read from L2 by every column tile) have one LDS buffer: each stage
+// first copies its A fragments to registers, then, after a second barrier, the next stage's A is
+// loaded over them.  A is issued before B, so the in-order load counter lets a wavefront wait for
+// A(kt + 1) while B(kt + NS - 1) stays in flight.
+// ILV (two-stage ring): the next stage's loads are issued one between each pair of MFMAs instead
+// of all before them, so a wavefront held up issuing a load still has MFMAs in the pipe.
+template <int MODE, int BM, int BN, int NS, int SCB, int BK, bool SPLIT = false, bool ILV = false>
 __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     constexpr int NWN = 2, THREADS = BM * 2;
     static_assert(BM == 128 || BM == 256, "tile rows");
@@ -171,14 +183,18 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     constexpr int SBK = BK / 32;                              // scale blocks per row per stage
     static_assert(SCB % SBK == 0, "scale groups hold whole stages");
     constexpr int SST = SCB / SBK;                            // stages covered by one scale fetch
-    constexpr int SB = (SST >= NS - 1) ? 2 : NS;              // scale groups in flight at once
+    // scale groups in flight at once: a group's buffer is refilled NS - 1 stages ahead of its first
+    // use, so it must not be the buffer of a group still being read
+    constexpr int SBB = 1 + (NS - 2 + SST) / SST;             // B: 1 + ceil((NS - 1) / SST)
+    constexpr int SBA = SPLIT ? 1 : SBB;                      // A (split: read before its refill)
     constexpr int SW = SCB / 4;                               // scale dwords per row per group
     constexpr int WN = BN / NWN, NT32 = WN / 32;
     constexpr int NA = BM * ACH / THREADS;                    // A chunks per thread per stage
     constexpr int NB = BN * BCH / THREADS;                    // B chunks per thread per stage
     constexpr int OPS = NA + NB;                              // loads one stage adds (scale fetches not counted)
     static_assert(NA >= 1 && NB >= 1 && (NS - 2) * OPS < 16, "tile / thread count");
-    constexpr int SZ_A = NS * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
+    constexpr int NSA = SPLIT ? 1 : NS;                       // A buffers
+    constexpr int SZ_A = NSA * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SBA * BM * SCB, SZ_SB = SBB * BN * SCB;
     // epilogue: the output tile passes through LDS EPR rows at a time (gate/up: one thread per
     // (row, 32-column block) of the 128 a-columns)
     constexpr int EPR = (MODE == MX_W13) ? THREADS / 4 : 128;
@@ -255,8 +271,9 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     const int mrows = min(BM, rows_g - m0);
 
     // ---- A sources: chunk slot s = i*THREADS + tid holds row s/ACH at physical chunk s%ACH; rows
-    // past the group's end re-read the tile's first row (their results are never stored), or, with
-    // a two-stage ring (every wait drains all loads), are not loaded at all.
+    // past the group's end re-read the tile's first row (their results are never stored), or are
+    // not loaded at all where no wait counts A's loads (a two-stage ring drains every load; the
+    // split pipeline counts only the B loads issued after A).
     auto a_row = [&](int r) -> int64_t {  // byte offset of row r's codes; scales at /32
         if (r >= mrows) r = 0;
         if (MODE == MX_W13) return (int64_t)(shared ? m0 + r : p.perm[base + m0 + r] / p.k) * p.d;
@@ -268,7 +285,7 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     for (int i = 0; i < NA; ++i) {
         const int slot = i * THREADS + tid, r = slot / ACH;
         asrc[i] = p.A + a_row(r) + ((slot % ACH) ^ tile_swz<ACH>(r)) * 16;
-        alive[i] = NS != 2 || r < mrows;
+        alive[i] = (NS != 2 && !SPLIT) || r < mrows;
     }
     const uint8_t* assrc = p.As + a_row(tid < BM ? tid : 0) / 32;
     // ---- B sources.  Gate/up: each wavefront column holds BN/4 gate rows and the matching
@@ -290,25 +307,54 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     }
     const uint8_t* bssrc = WS + (int64_t)wrow_of(tid < BN ? tid : 0) * wsb;
 
-    auto issue = [&](int kt) {
-        const int st = kt % NS;
+    // stage kt's A codes (and, at a scale group's first stage, the group's A scales: SCB blocks
+    // of each row for stages kt .. kt+SST-1)
+    auto issue_a = [&](int kt) {
+        const int st = kt % NSA;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
             if (alive[i]) dma16(asrc[i] + kt * BK, sA + st * BM * BK + (i * THREADS + wv * 64) * 16);
+        if (kt % SST == 0 && tid < BM) {
+            const int grp = kt / SST, sbuf = grp % SBA;
+            if constexpr (SCB == 16) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
+            else dma4(assrc + grp * 4, sSA + sbuf * BM + wv * 64);
+        }
+    };
+    // stage kt's B codes (and scales, as for A); a wavefront issues NB loads, plus one scale load
+    // at a group's first stage if its rows hold B rows
+    constexpr bool WAVE_B_SCALES_ALL = BN % 64 == 0 && BN >= THREADS;
+    auto issue_b = [&](int kt) {
+        const int st = kt % NS;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             dma16(bsrc[i] + kt * (BK / 2), sB + st * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
-        if (kt % SST == 0) {  // scales of stages kt .. kt+SST-1: SCB blocks of each row
-            const int grp = kt / SST, sbuf = grp % SB;
-            if constexpr (SCB == 16) {
-                if (tid < BM) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
-                if (tid < BN) dma16(bssrc + grp * 16, sSB + (sbuf * BN + wv * 64) * SW);
-            } else {
-                if (tid < BM) dma4(assrc + grp * 4, sSA + sbuf * BM + wv * 64);
-                if (tid < BN) dma4(bssrc + grp * 4, sSB + sbuf * BN + wv * 64);
-            }
+        if (kt % SST == 0 && tid < BN) {
+            const int grp = kt / SST, sbuf = grp % SBB;
+            if constexpr (SCB == 16) dma16(bssrc + grp * 16, sSB + (sbuf * BN + wv * 64) * SW);
+            else dma4(bssrc + grp * 4, sSB + sbuf * BN + wv * 64);
         }
     };
+    static_assert(!SPLIT || WAVE_B_SCALES_ALL, "split waits count one B-scale load in every wavefront");
+    // load j of stage kt (j < OPS: A chunk j, then B chunk j - NA; the scale groups with j == 0)
+    auto issue_one = [&](int kt, int j) {
+        if (j == 0 && kt % SST == 0) {
+            const int grp = kt / SST;
+            if constexpr (SCB == 16) {
+                if (tid < BM) dma16(assrc + grp * 16, sSA + ((grp % SBA) * BM + wv * 64) * SW);
+                if (tid < BN) dma16(bssrc + grp * 16, sSB + ((grp % SBB) * BN + wv * 64) * SW);
+            } else {
+                if (tid < BM) dma4(assrc + grp * 4, sSA + (grp % SBA) * BM + wv * 64);
+                if (tid < BN) dma4(bssrc + grp * 4, sSB + (grp % SBB) * BN + wv * 64);
+            }
+        }
+        if (j < NA) {
+            if (alive[j]) dma16(asrc[j] + kt * BK, sA + (kt % NSA) * BM * BK + (j * THREADS + wv * 64) * 16);
+        } else {
+            const int i = j - NA;
+            dma16(bsrc[i] + kt * (BK / 2), sB + (kt % NS) * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
+        }
+    };
+    static_assert(!ILV || (NS == 2 && !SPLIT && OPS == KS * (BN / 2 / 32)), "one load per MFMA pair");
 
     f32x16_t acc[2][NT32];
 #pragma unroll
@@ -323,50 +369,127 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     // a wavefront whose 64 rows all lie past the group's end only loads and synchronises; its
     // matrix-core time goes to the other workgroup on the CU
     const bool live = wm * 64 < mrows;
+    // the MFMAs of one K step: A fragments and scales given, B read from ring slot st
+    auto mma = [&](int st, int sbb, int u, const v8i_t (&af)[2], const int (&sa)[2], int sw, int sh8) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-        if (i < nk) issue(i);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt % NS;
-        // wait for stage kt; the stages issued after it (up to NS - 2) stay in flight
-        asm volatile("" ::: "memory");
-        const int newer = min(NS - 2, nk - 1 - kt);
-        if (newer >= 2) VM_WAIT(2 * OPS);
-        else if (newer == 1) VM_WAIT(OPS);
-        else VM_WAIT(0);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (kt + NS - 1 < nk) issue(kt + NS - 1);
+        for (int ns = 0; ns < NT32; ++ns) {
+            const int n = wn * WN + ns * 32 + l32;
+            const v4u_t b = *reinterpret_cast<const v4u_t*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
+                                                            ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
+            const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+            const int sb = (int)((sSB[(sbb * BN + n) * SW + sw] >> sh8) & 0xFFu);
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, sa[ms],
+                                                                              0, sb);
+        }
+    };
+    // A fragments of K step u of stage kt from buffer st, scales from group buffer sba
+    auto read_a = [&](int st, int sba, int kt, int u, v8i_t (&af)[2], int (&sa)[2]) {
+        // this lane's block inside its row's scale group: (kt % SST) * SBK + 2u + hk
+        const int sblk = (kt % SST) * SBK + 2 * u + hk;
+        const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            const int r = wm * 64 + ms * 32 + l32;
+            const uint8_t* row = sA + st * BM * BK + r * BK;
+            const v4u_t lo = *reinterpret_cast<const v4u_t*>(row + ((4 * u + hk) ^ tile_swz<ACH>(r)) * 16);
+            const v4u_t hi = *reinterpret_cast<const v4u_t*>(row + ((4 * u + 2 + hk) ^ tile_swz<ACH>(r)) * 16);
+            af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            sa[ms] = (int)((sSA[(sba * BM + r) * SW + sw] >> sh8) & 0xFFu);
+        }
+    };
 
-        if (!live) continue;
-        const int sbuf = (kt / SST) % SB;
+    if constexpr (!SPLIT) {
 #pragma unroll
-        for (int u = 0; u < KS; ++u) {
-            // this lane's block inside its row's scale group: (kt % SST) * SBK + 2u + hk
-            const int sblk = (kt % SST) * SBK + 2 * u + hk;
-            const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
-            v8i_t af[2];
-            int sa[2];
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-                const int r = wm * 64 + ms * 32 + l32;
-                const uint8_t* row = sA + st * BM * BK + r * BK;
-                const uint4 lo = *reinterpret_cast<const uint4*>(row + ((4 * u + hk) ^ tile_swz<ACH>(r)) * 16);
-                const uint4 hi = *reinterpret_cast<const uint4*>(row + ((4 * u + 2 + hk) ^ tile_swz<ACH>(r)) * 16);
-                af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sa[ms] = (int)((sSA[(sbuf * BM + r) * SW + sw] >> sh8) & 0xFFu);
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < nk) {
+                issue_a(i);
+                issue_b(i);
             }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int st = kt % NS;
+            // wait for stage kt; the stages issued after it (up to NS - 2) stay in flight.  A stage
+            // adds OPS loads plus any scale loads, so waiting down to OPS (2 * OPS) outstanding
+            // leaves only loads of the newer stages.
+            asm volatile("" ::: "memory");
+            const int newer = min(NS - 2, nk - 1 - kt);
+            if (newer >= 2) VM_WAIT(2 * OPS);
+            else if (newer == 1) VM_WAIT(OPS);
+            else VM_WAIT(0);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const bool more = kt + NS - 1 < nk;
+            if (more && (!ILV || !live)) {
+                issue_a(kt + NS - 1);
+                issue_b(kt + NS - 1);
+            }
+
+            if (!live) continue;
+            const int sbuf = (kt / SST) % SBB;
 #pragma unroll
-            for (int ns = 0; ns < NT32; ++ns) {
-                const int n = wn * WN + ns * 32 + l32;
-                const uint4 b = *reinterpret_cast<const uint4*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
-                                                                ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
-                const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-                const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
+            for (int u = 0; u < KS; ++u) {
+                v8i_t af[2];
+                int sa[2];
+                read_a(st, sbuf, kt, u, af, sa);
+                const int sblk = (kt % SST) * SBK + 2 * u + hk;
+                if constexpr (ILV) {
+                    const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0,
-                                                                                  sa[ms], 0, sb);
+                    for (int ns = 0; ns < NT32; ++ns) {
+                        const int n = wn * WN + ns * 32 + l32;
+                        const v4u_t b = *reinterpret_cast<const v4u_t*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
+                                                                        ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
+                        const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+                        const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
+#pragma unroll
+                        for (int ms = 0; ms < 2; ++ms)
+                            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4,
+                                                                                          0, sa[ms], 0, sb);
+                        if (more) issue_one(kt + 1, u * NT32 + ns);
+                    }
+                } else {
+                    mma(st, sbuf, u, af, sa, sblk >> 2, 8 * (sblk & 3));
+                }
+            }
+        }
+    } else {
+        // three-deep B ring: issue order B(0), A(0), B(1); then stage kt issues A(kt+1), B(kt+2)
+        static_assert(NS == 3, "the split pipeline's waits assume one B stage issued after each A");
+        if (nk > 0) {
+            issue_b(0);
+            issue_a(0);
+        }
+        if (nk > 1) issue_b(1);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int st = kt % NS;
+            // wait for A(kt) and B(kt): the only loads issued after A(kt) are B(kt+1)'s, NB codes
+            // plus one scale load at a scale group's first stage (uniform over the wavefront)
+            asm volatile("" ::: "memory");
+            if (kt + 1 >= nk) VM_WAIT(0);
+            else if ((kt + 1) % SST == 0) VM_WAIT(NB + 1);
+            else VM_WAIT(NB);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            // stage kt's A fragments and scales to registers, then free the A buffer
+            v8i_t af[KS][2];
+            int sa[KS][2];
+            if (live) {
+#pragma unroll
+                for (int u = 0; u < KS; ++u) read_a(0, 0, kt, u, af[u], sa[u]);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (kt + 1 < nk) issue_a(kt + 1);
+            if (kt + NS - 1 < nk) issue_b(kt + NS - 1);
+
+            if (!live) continue;
+            const int sbb = (kt / SST) % SBB;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) {
+                const int sblk = (kt % SST) * SBK + 2 * u + hk;
+                mma(st, sbb, u, af[u], sa[u], sblk >> 2, 8 * (sblk & 3));
             }
         }
     }
@@ -468,6 +591,7 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
 // 256-row tiles (one 8-wavefront workgroup per CU) measured slower at every ring depth: the two
 // independent workgroups of 128 rows hide each other's load waits.
 constexpr int MX_BM = 128, MX_BK = 128, MX_NS = 2;
+constexpr bool MX_SPLIT = false, MX_ILV = false;
 
 static unsigned mx_grid8(int64_t tiles) {
     int64_t g = (tiles + 7) / 8 * 8;
@@ -492,8 +616,8 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
     const unsigned grid =
         mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
     if (d % 512 == 0)
-        MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+        MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 16, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 4, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
     return hipGetLastError();
 }
 
@@ -509,8 +633,8 @@ hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t
         const int nt = d / 256;
         const unsigned grid = mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, nt, nt));
         if (scb16)
-            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
     } else {
         const int nt = d / 128;
         const unsigned grid = mx_grid8(mx_max_tiles(128, T, k, E, n_shared, nt, nt));
