@@ -105,9 +105,9 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
     // vector-memory ops one stage adds per thread, counted for the wave that issues the fewest
     constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BN >= THREADS ? 1 : 0));
     static_assert(OPS < 16, "vmcnt immediate");
-    // One LDS object carved by offsets: with a single object the compiler's wait insertion
-    // leaves LDS-DMA completion to the explicit vmcnt waits below instead of draining the
-    // whole ring before every fragment read.
+    // One LDS object carved by offsets.  Fragment reads are loads of plain (vector) types: the
+    // compiler's wait insertion drains every LDS-DMA load in flight before an LDS read that carries
+    // no type-based alias information; LDS-DMA completion is left to the explicit vmcnt waits below.
     constexpr int SZ_A = NS * NPL * BM * ROWE * 2, SZ_B = NS * BN * BROW * 2, SZ_S = (WT == 2 ? 2 * BN * 4 : 0);
     // output staging after the K loop (reuses the ring): bf16 rows of NCOL columns, pitch OP
     constexpr int NCOL = (MODE == MODE_W13) ? BN / 2 : BN, OP = NCOL + 8;
