@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
-                        acc[ms][ns][j] = gt / (1.0f + expf(-gt)) * up;
+                        acc[ms][ns][j] = silu_hw(gt) * up;
                     }
         }
         constexpr int CH = NCOL / 8;  // 16-byte chunks per staged row

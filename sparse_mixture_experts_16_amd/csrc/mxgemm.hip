@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float gt = acc[ms][ns][j], up = acc[ms][ns + NT32 / 2][j];
-                    acc[ms][ns][j] = gt / (1.0f + expf(-gt)) * up;
+                    acc[ms][ns][j] = silu_hw(gt) * up;
                 }
         float* o_st = reinterpret_cast<float*>(smem);
         const int col0 = nt * (BN / 2);
