@@ -62,16 +62,18 @@ POOL = 256
 # the digest of the kernel sources it was taken on; a different digest reports null.
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "common.h", "wchunk.h"],
-    "gemm": ["gemm.hip", "common.h", "wchunk.h"],
+    "gemm": ["gemm.hip", "common.h", "wchunk.h", "lds_dma.h"],
+    "mx": ["mxgemm.hip", "common.h", "lds_dma.h"],
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=27758.1, write_kib=54.3),
-    "c3_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=26278.3, write_kib=97.2),
-    "c3nv_decode_T1": dict(src="decode:078267efadcde7e2", fetch_kib=27835.9, write_kib=97.0),
-    "c4_stack": dict(src="decode:078267efadcde7e2", fetch_kib=26277.7, write_kib=97.0),
-    "c2_prefill": dict(src="gemm:d456c04b472f1605", fetch_kib=710907.9, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:d456c04b472f1605", fetch_kib=1356208.3, write_kib=393216.0),
+    "c1_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=27761.8, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=26278.2, write_kib=97.2),
+    "c3nv_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=27810.9, write_kib=96.2),
+    "c4_stack": dict(src="decode:95054e48d51c9b0a", fetch_kib=26277.9, write_kib=97.0),
+    "c2_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=745945.2, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=2139238.7, write_kib=393216.0),
+    "c3_prefill_mx": dict(src="mx:5301135347d3331a", fetch_kib=1331879.6, write_kib=101700.6),
 }
 
 
