@@ -14,11 +14,13 @@
 // scale operand is the E8M0 scale of row (column) l%32 for the K block l/32.  Accumulator j of
 // lane l: row 8*(j/4) + 4*(l/32) + j%4, column l%32.
 //
-// Tile: 128 token rows x BN weight rows, K in stages of 64 (one MFMA per 32x32 sub-tile), 4
-// wavefronts as 2 x 2, each owning 64 x BN/2.  Stages stream through a three-deep LDS ring by
-// global_load_lds (A rows 64 bytes with the chunk swizzle of the bf16 kernel, B rows 32 bytes);
-// the scales of two stages (four blocks) travel as one dword per row into a double-buffered row
-// list.  Tiles come from the flat (expert, m-tile, n-tile) list of the bf16 kernel.
+// Tile: 128 token rows x 256 weight rows, K in stages of 128 (two MFMAs per 32x32 sub-tile), 4
+// wavefronts as 2 x 2, each owning 64 x 128.  Stages stream through a double-buffered LDS ring by
+// global_load_lds (A rows 128 bytes, B rows 64 bytes, both chunk-swizzled so fragment reads are
+// conflict-free); the E8M0 scales of four stages (16 blocks) travel as 16 bytes per row into a
+// double-buffered row list.  Tiles come from the flat (expert, m-tile, n-tile) list of the bf16
+// kernel.  A down projection with d not a multiple of 256 uses 128-column tiles with 64-element
+// stages three deep.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -164,14 +166,7 @@ __device__ __forceinline__ int btile_swz(int r) {
 // workgroups per CU; BM = 256: 512 threads, one per CU).  BK: K elements per stage (64: A rows of
 // 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring depth.  SCB: scale bytes fetched per row at a
 // time (4 or 16; 16 needs K % 512 == 0).
-// SPLIT: the weights (B, streamed from HBM) keep the NS-deep ring, issued NS - 1 stages ahead,
-// while the activations (A, re-read from L2 by every column tile) have one LDS buffer: each stage
-// first copies its A fragments to registers, then, after a second barrier, the next stage's A is
-// loaded over them.  A is issued before B, so the in-order load counter lets a wavefront wait for
-// A(kt + 1) while B(kt + NS - 1) stays in flight.
-// ILV (two-stage ring): the next stage's loads are issued one between each pair of MFMAs instead
-// of all before them, so a wavefront held up issuing a load still has MFMAs in the pipe.
-template <int MODE, int BM, int BN, int NS, int SCB, int BK, bool SPLIT = false, bool ILV = false>
+template <int MODE, int BM, int BN, int NS, int SCB, int BK>
 __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     constexpr int NWN = 2, THREADS = BM * 2;
     static_assert(BM == 128 || BM == 256, "tile rows");
@@ -185,16 +180,14 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     constexpr int SST = SCB / SBK;                            // stages covered by one scale fetch
     // scale groups in flight at once: a group's buffer is refilled NS - 1 stages ahead of its first
     // use, so it must not be the buffer of a group still being read
-    constexpr int SBB = 1 + (NS - 2 + SST) / SST;             // B: 1 + ceil((NS - 1) / SST)
-    constexpr int SBA = SPLIT ? 1 : SBB;                      // A (split: read before its refill)
+    constexpr int SB = 1 + (NS - 2 + SST) / SST;              // 1 + ceil((NS - 1) / SST)
     constexpr int SW = SCB / 4;                               // scale dwords per row per group
     constexpr int WN = BN / NWN, NT32 = WN / 32;
     constexpr int NA = BM * ACH / THREADS;                    // A chunks per thread per stage
     constexpr int NB = BN * BCH / THREADS;                    // B chunks per thread per stage
     constexpr int OPS = NA + NB;                              // loads one stage adds (scale fetches not counted)
     static_assert(NA >= 1 && NB >= 1 && (NS - 2) * OPS < 16, "tile / thread count");
-    constexpr int NSA = SPLIT ? 1 : NS;                       // A buffers
-    constexpr int SZ_A = NSA * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SBA * BM * SCB, SZ_SB = SBB * BN * SCB;
+    constexpr int SZ_A = NS * BM * BK, SZ_B = NS * BN * BK / 2, SZ_SA = SB * BM * SCB, SZ_SB = SB * BN * SCB;
     // epilogue: the output tile passes through LDS EPR rows at a time (gate/up: one thread per
     // (row, 32-column block) of the 128 a-columns)
     constexpr int EPR = (MODE == MX_W13) ? THREADS / 4 : 128;
@@ -271,9 +264,8 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     const int mrows = min(BM, rows_g - m0);
 
     // ---- A sources: chunk slot s = i*THREADS + tid holds row s/ACH at physical chunk s%ACH; rows
-    // past the group's end re-read the tile's first row (their results are never stored), or are
-    // not loaded at all where no wait counts A's loads (a two-stage ring drains every load; the
-    // split pipeline counts only the B loads issued after A).
+    // past the group's end re-read the tile's first row (their results are never stored), or, with
+    // a two-stage ring (whose every wait drains all loads), are not loaded at all.
     auto a_row = [&](int r) -> int64_t {  // byte offset of row r's codes; scales at /32
         if (r >= mrows) r = 0;
         if (MODE == MX_W13) return (int64_t)(shared ? m0 + r : p.perm[base + m0 + r] / p.k) * p.d;
@@ -285,7 +277,7 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     for (int i = 0; i < NA; ++i) {
         const int slot = i * THREADS + tid, r = slot / ACH;
         asrc[i] = p.A + a_row(r) + ((slot % ACH) ^ tile_swz<ACH>(r)) * 16;
-        alive[i] = (NS != 2 && !SPLIT) || r < mrows;
+        alive[i] = NS != 2 || r < mrows;
     }
     const uint8_t* assrc = p.As + a_row(tid < BM ? tid : 0) / 32;
     // ---- B sources.  Gate/up: each wavefront column holds BN/4 gate rows and the matching
@@ -307,54 +299,27 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     }
     const uint8_t* bssrc = WS + (int64_t)wrow_of(tid < BN ? tid : 0) * wsb;
 
-    // stage kt's A codes (and, at a scale group's first stage, the group's A scales: SCB blocks
+    // stage kt's A and B codes, and at a scale group's first stage the group's scales (SCB blocks
     // of each row for stages kt .. kt+SST-1)
-    auto issue_a = [&](int kt) {
-        const int st = kt % NSA;
+    auto issue = [&](int kt) {
+        const int st = kt % NS;
 #pragma unroll
         for (int i = 0; i < NA; ++i)
             if (alive[i]) dma16(asrc[i] + kt * BK, sA + st * BM * BK + (i * THREADS + wv * 64) * 16);
-        if (kt % SST == 0 && tid < BM) {
-            const int grp = kt / SST, sbuf = grp % SBA;
-            if constexpr (SCB == 16) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
-            else dma4(assrc + grp * 4, sSA + sbuf * BM + wv * 64);
-        }
-    };
-    // stage kt's B codes (and scales, as for A); a wavefront issues NB loads, plus one scale load
-    // at a group's first stage if its rows hold B rows
-    constexpr bool WAVE_B_SCALES_ALL = BN % 64 == 0 && BN >= THREADS;
-    auto issue_b = [&](int kt) {
-        const int st = kt % NS;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             dma16(bsrc[i] + kt * (BK / 2), sB + st * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
-        if (kt % SST == 0 && tid < BN) {
-            const int grp = kt / SST, sbuf = grp % SBB;
-            if constexpr (SCB == 16) dma16(bssrc + grp * 16, sSB + (sbuf * BN + wv * 64) * SW);
-            else dma4(bssrc + grp * 4, sSB + sbuf * BN + wv * 64);
-        }
-    };
-    static_assert(!SPLIT || WAVE_B_SCALES_ALL, "split waits count one B-scale load in every wavefront");
-    // load j of stage kt (j < OPS: A chunk j, then B chunk j - NA; the scale groups with j == 0)
-    auto issue_one = [&](int kt, int j) {
-        if (j == 0 && kt % SST == 0) {
-            const int grp = kt / SST;
+        if (kt % SST == 0) {
+            const int grp = kt / SST, sbuf = grp % SB;
             if constexpr (SCB == 16) {
-                if (tid < BM) dma16(assrc + grp * 16, sSA + ((grp % SBA) * BM + wv * 64) * SW);
-                if (tid < BN) dma16(bssrc + grp * 16, sSB + ((grp % SBB) * BN + wv * 64) * SW);
+                if (tid < BM) dma16(assrc + grp * 16, sSA + (sbuf * BM + wv * 64) * SW);
+                if (tid < BN) dma16(bssrc + grp * 16, sSB + (sbuf * BN + wv * 64) * SW);
             } else {
-                if (tid < BM) dma4(assrc + grp * 4, sSA + (grp % SBA) * BM + wv * 64);
-                if (tid < BN) dma4(bssrc + grp * 4, sSB + (grp % SBB) * BN + wv * 64);
+                if (tid < BM) dma4(assrc + grp * 4, sSA + sbuf * BM + wv * 64);
+                if (tid < BN) dma4(bssrc + grp * 4, sSB + sbuf * BN + wv * 64);
             }
         }
-        if (j < NA) {
-            if (alive[j]) dma16(asrc[j] + kt * BK, sA + (kt % NSA) * BM * BK + (j * THREADS + wv * 64) * 16);
-        } else {
-            const int i = j - NA;
-            dma16(bsrc[i] + kt * (BK / 2), sB + (kt % NS) * BN * (BK / 2) + (i * THREADS + wv * 64) * 16);
-        }
     };
-    static_assert(!ILV || (NS == 2 && !SPLIT && OPS == KS * (BN / 2 / 32)), "one load per MFMA pair");
 
     f32x16_t acc[2][NT32];
 #pragma unroll
@@ -369,127 +334,52 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     // a wavefront whose 64 rows all lie past the group's end only loads and synchronises; its
     // matrix-core time goes to the other workgroup on the CU
     const bool live = wm * 64 < mrows;
-    // the MFMAs of one K step: A fragments and scales given, B read from ring slot st
-    auto mma = [&](int st, int sbb, int u, const v8i_t (&af)[2], const int (&sa)[2], int sw, int sh8) {
 #pragma unroll
-        for (int ns = 0; ns < NT32; ++ns) {
-            const int n = wn * WN + ns * 32 + l32;
-            const v4u_t b = *reinterpret_cast<const v4u_t*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
-                                                            ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
-            const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-            const int sb = (int)((sSB[(sbb * BN + n) * SW + sw] >> sh8) & 0xFFu);
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0, sa[ms],
-                                                                              0, sb);
-        }
-    };
-    // A fragments of K step u of stage kt from buffer st, scales from group buffer sba
-    auto read_a = [&](int st, int sba, int kt, int u, v8i_t (&af)[2], int (&sa)[2]) {
-        // this lane's block inside its row's scale group: (kt % SST) * SBK + 2u + hk
-        const int sblk = (kt % SST) * SBK + 2 * u + hk;
-        const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-            const int r = wm * 64 + ms * 32 + l32;
-            const uint8_t* row = sA + st * BM * BK + r * BK;
-            const v4u_t lo = *reinterpret_cast<const v4u_t*>(row + ((4 * u + hk) ^ tile_swz<ACH>(r)) * 16);
-            const v4u_t hi = *reinterpret_cast<const v4u_t*>(row + ((4 * u + 2 + hk) ^ tile_swz<ACH>(r)) * 16);
-            af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sa[ms] = (int)((sSA[(sba * BM + r) * SW + sw] >> sh8) & 0xFFu);
-        }
-    };
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nk) issue(i);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt % NS;
+        // wait for stage kt; the stages issued after it (up to NS - 2) stay in flight.  A stage adds
+        // OPS loads plus any scale loads, so waiting down to OPS (2 * OPS) outstanding leaves only
+        // loads of the newer stages.
+        asm volatile("" ::: "memory");
+        const int newer = min(NS - 2, nk - 1 - kt);
+        if (newer >= 2) VM_WAIT(2 * OPS);
+        else if (newer == 1) VM_WAIT(OPS);
+        else VM_WAIT(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
 
-    if constexpr (!SPLIT) {
+        if (!live) continue;
+        const int sbuf = (kt / SST) % SB;
 #pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-            if (i < nk) {
-                issue_a(i);
-                issue_b(i);
+        for (int u = 0; u < KS; ++u) {
+            // this lane's block inside its row's scale group: (kt % SST) * SBK + 2u + hk
+            const int sblk = (kt % SST) * SBK + 2 * u + hk;
+            const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
+            v8i_t af[2];
+            int sa[2];
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                const int r = wm * 64 + ms * 32 + l32;
+                const uint8_t* row = sA + st * BM * BK + r * BK;
+                const v4u_t lo = *reinterpret_cast<const v4u_t*>(row + ((4 * u + hk) ^ tile_swz<ACH>(r)) * 16);
+                const v4u_t hi = *reinterpret_cast<const v4u_t*>(row + ((4 * u + 2 + hk) ^ tile_swz<ACH>(r)) * 16);
+                af[ms] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sa[ms] = (int)((sSA[(sbuf * BM + r) * SW + sw] >> sh8) & 0xFFu);
             }
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt % NS;
-            // wait for stage kt; the stages issued after it (up to NS - 2) stay in flight.  A stage
-            // adds OPS loads plus any scale loads, so waiting down to OPS (2 * OPS) outstanding
-            // leaves only loads of the newer stages.
-            asm volatile("" ::: "memory");
-            const int newer = min(NS - 2, nk - 1 - kt);
-            if (newer >= 2) VM_WAIT(2 * OPS);
-            else if (newer == 1) VM_WAIT(OPS);
-            else VM_WAIT(0);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            const bool more = kt + NS - 1 < nk;
-            if (more && (!ILV || !live)) {
-                issue_a(kt + NS - 1);
-                issue_b(kt + NS - 1);
-            }
-
-            if (!live) continue;
-            const int sbuf = (kt / SST) % SBB;
 #pragma unroll
-            for (int u = 0; u < KS; ++u) {
-                v8i_t af[2];
-                int sa[2];
-                read_a(st, sbuf, kt, u, af, sa);
-                const int sblk = (kt % SST) * SBK + 2 * u + hk;
-                if constexpr (ILV) {
-                    const int sw = sblk >> 2, sh8 = 8 * (sblk & 3);
+            for (int ns = 0; ns < NT32; ++ns) {
+                const int n = wn * WN + ns * 32 + l32;
+                const v4u_t b = *reinterpret_cast<const v4u_t*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
+                                                                ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
+                const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+                const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
 #pragma unroll
-                    for (int ns = 0; ns < NT32; ++ns) {
-                        const int n = wn * WN + ns * 32 + l32;
-                        const v4u_t b = *reinterpret_cast<const v4u_t*>(sB + st * BN * (BK / 2) + n * (BK / 2) +
-                                                                        ((2 * u + hk) ^ btile_swz<BCH>(n)) * 16);
-                        const v8i_t bf = v8i_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-                        const int sb = (int)((sSB[(sbuf * BN + n) * SW + sw] >> sh8) & 0xFFu);
-#pragma unroll
-                        for (int ms = 0; ms < 2; ++ms)
-                            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4,
-                                                                                          0, sa[ms], 0, sb);
-                        if (more) issue_one(kt + 1, u * NT32 + ns);
-                    }
-                } else {
-                    mma(st, sbuf, u, af, sa, sblk >> 2, 8 * (sblk & 3));
-                }
-            }
-        }
-    } else {
-        // three-deep B ring: issue order B(0), A(0), B(1); then stage kt issues A(kt+1), B(kt+2)
-        static_assert(NS == 3, "the split pipeline's waits assume one B stage issued after each A");
-        if (nk > 0) {
-            issue_b(0);
-            issue_a(0);
-        }
-        if (nk > 1) issue_b(1);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt % NS;
-            // wait for A(kt) and B(kt): the only loads issued after A(kt) are B(kt+1)'s, NB codes
-            // plus one scale load at a scale group's first stage (uniform over the wavefront)
-            asm volatile("" ::: "memory");
-            if (kt + 1 >= nk) VM_WAIT(0);
-            else if ((kt + 1) % SST == 0) VM_WAIT(NB + 1);
-            else VM_WAIT(NB);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            // stage kt's A fragments and scales to registers, then free the A buffer
-            v8i_t af[KS][2];
-            int sa[KS][2];
-            if (live) {
-#pragma unroll
-                for (int u = 0; u < KS; ++u) read_a(0, 0, kt, u, af[u], sa[u]);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (kt + 1 < nk) issue_a(kt + 1);
-            if (kt + NS - 1 < nk) issue_b(kt + NS - 1);
-
-            if (!live) continue;
-            const int sbb = (kt / SST) % SBB;
-#pragma unroll
-            for (int u = 0; u < KS; ++u) {
-                const int sblk = (kt % SST) * SBK + 2 * u + hk;
-                mma(st, sbb, u, af[u], sa[u], sblk >> 2, 8 * (sblk & 3));
+                for (int ms = 0; ms < 2; ++ms)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[ms], bf, acc[ms][ns], 0, 4, 0,
+                                                                                  sa[ms], 0, sb);
             }
         }
     }
@@ -591,7 +481,6 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
 // 256-row tiles (one 8-wavefront workgroup per CU) measured slower at every ring depth: the two
 // independent workgroups of 128 rows hide each other's load waits.
 constexpr int MX_BM = 128, MX_BK = 128, MX_NS = 2;
-constexpr bool MX_SPLIT = false, MX_ILV = false;
 
 static unsigned mx_grid8(int64_t tiles) {
     int64_t g = (tiles + 7) / 8 * 8;
@@ -616,8 +505,8 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
     const unsigned grid =
         mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
     if (d % 512 == 0)
-        MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 16, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 4, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
+        MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+    else MOE_LAUNCH(PROF_FFN_UP, (mxgemm<MX_W13, BM, BN, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
     return hipGetLastError();
 }
 
@@ -633,8 +522,8 @@ hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t
         const int nt = d / 256;
         const unsigned grid = mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, nt, nt));
         if (scb16)
-            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK, MX_SPLIT, MX_ILV>), dim3(grid), dim3(2 * BM), 0, st, p);
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
     } else {
         const int nt = d / 128;
         const unsigned grid = mx_grid8(mx_max_tiles(128, T, k, E, n_shared, nt, nt));
