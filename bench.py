@@ -73,7 +73,7 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c4_stack": dict(src="decode:95054e48d51c9b0a", fetch_kib=26277.9, write_kib=97.0),
     "c2_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=745945.2, write_kib=110592.0),
     "c3_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=2139238.7, write_kib=393216.0),
-    "c3_prefill_mx": dict(src="mx:5301135347d3331a", fetch_kib=1331879.6, write_kib=101700.6),
+    "c3_prefill_mx": dict(src="mx:7167d4a1ab5db82d", fetch_kib=1366076.8, write_kib=102114.5),
 }
 
 
