@@ -39,20 +39,19 @@ enum { MX_W13 = 0, MX_W2 = 1 };
 // ---------------------------------------------------------------------------------------------
 // MXFP8 quantisation of one 32-element block
 // ---------------------------------------------------------------------------------------------
-// E4M3 code of q (finite, |q| < 512), rounded to nearest even on the fp32 bits; magnitudes
-// above 448 (E4M3's largest normal) clamp to it.
-__device__ __forceinline__ uint32_t e4m3_rne(float q) {
-    const uint32_t sgn = (__float_as_uint(q) >> 24) & 0x80u;
-    const float a = fminf(fabsf(q), 448.0f);
-    uint32_t code;
-    if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (a count of 8 is 2^-6)
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        uint32_t u = __float_as_uint(a);
-        u += 0x7FFFFu + ((u >> 20) & 1u);  // keep 3 mantissa bits, ties to even
-        code = ((((u >> 23) & 0xFFu) - 120u) << 3) | ((u >> 20) & 7u);
-    }
-    return code | sgn;
+typedef short v2i16_t __attribute__((ext_vector_type(2)));
+
+// E4M3 codes of four finite values, rounded to nearest even, magnitudes above 448 (E4M3's
+// largest normal) clamped to it; code k in byte k.  v_cvt_scalef32_pk_fp8_f32 (scale 1) rounds to
+// nearest even but does not saturate, so its inputs are clamped first: checked on the GPU against
+// the rounding done on the fp32 bits, identical for every finite fp32 input (subnormal steps of
+// 2^-9 and signed zeros included).
+__device__ __forceinline__ float clamp448(float q) { return fminf(fmaxf(q, -448.0f), 448.0f); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    v2i16_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp448(a), clamp448(b), 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp448(c), clamp448(d), 1.0f, true);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Shared scale of a block from the bit pattern of its largest magnitude: E8M0 byte
@@ -71,9 +70,7 @@ __device__ __forceinline__ uint32_t mx_block(const float (&v)[32], uint32_t (&co
     const uint32_t sb = ex > 8u ? ex - 8u : 0u;
     const float mul = __uint_as_float((254u - sb) << 23);  // 2^(127 - sb): exact scaling
 #pragma unroll
-    for (int w = 0; w < 8; ++w)
-        code[w] = e4m3_rne(v[4 * w] * mul) | (e4m3_rne(v[4 * w + 1] * mul) << 8) |
-                  (e4m3_rne(v[4 * w + 2] * mul) << 16) | (e4m3_rne(v[4 * w + 3] * mul) << 24);
+    for (int w = 0; w < 8; ++w) code[w] = e4m3x4(v[4 * w] * mul, v[4 * w + 1] * mul, v[4 * w + 2] * mul, v[4 * w + 3] * mul);
     return sb;
 }
 
