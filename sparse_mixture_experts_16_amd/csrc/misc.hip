@@ -43,27 +43,35 @@ __global__ void __launch_bounds__(256) combine_gather(const Y* __restrict__ y, c
                                                       O* __restrict__ out, int d, int k, int accumulate,
                                                       const int32_t* __restrict__ idx, const uint8_t* __restrict__ mask,
                                                       int E) {
+    __shared__ int s_raw[MOE_MAX_K];
     __shared__ int s_pos[MOE_MAX_K];
     __shared__ float s_g[MOE_MAX_K];
     const int t = blockIdx.x;
-    if (threadIdx.x == 0) {
-        // insertion sort of the token's pairs by sorted position
-        for (int j = 0; j < k; ++j) {
-            int pos = inv[(int64_t)t * k + j];
-            const float g = topk_w[(int64_t)t * k + j];
-            if (mask) {
-                const int e = idx[(int64_t)t * k + j];
-                if (e < 0 || e >= E || !mask[e]) pos = -1;  // expert outside this partial layer
-            }
-            int q = j;
-            while (q > 0 && s_pos[q - 1] > pos) {
-                s_pos[q] = s_pos[q - 1];
-                s_g[q] = s_g[q - 1];
-                --q;
-            }
-            s_pos[q] = pos;
-            s_g[q] = g;
+    // the token's pairs in ascending sorted position (= ascending expert): thread j < k loads pair j
+    // and places it at its rank (positions are distinct; pairs outside a partial layer get -1 and
+    // rank first, in pair order)
+    int pos = -1;
+    float g = 0.0f;
+    if (threadIdx.x < k) {
+        const int j = threadIdx.x;
+        pos = inv[(int64_t)t * k + j];
+        g = topk_w[(int64_t)t * k + j];
+        if (mask) {
+            const int e = idx[(int64_t)t * k + j];
+            if (e < 0 || e >= E || !mask[e]) pos = -1;  // expert outside this partial layer
         }
+        s_raw[j] = pos;
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        const int j = threadIdx.x;
+        int r = 0;
+        for (int i = 0; i < k; ++i) {
+            const int pi = s_raw[i];
+            r += pi < pos || (pi == pos && i < j);
+        }
+        s_pos[r] = pos;
+        s_g[r] = g;
     }
     __syncthreads();
     for (int i0 = threadIdx.x * 8; i0 < d; i0 += blockDim.x * 8) {
