@@ -131,7 +131,7 @@ size_t moe_workspace_size(const moe_shape* shape);
 /* Static description of a status code. */
 const char* moe_status_string(int status);
 
-/* Router: logits -> top-k selection -> gates (steps a1, a2).
+/* Router: logits -> top-k selection -> gates.
    logits_in: NULL -> logits are computed from x, w_router, b_router; else a [T,E] f32
    array used as the logits (x, w_router, b_router ignored).  logits_out (nullable)
    receives the logits used.  topk_idx, topk_w as described above. */
@@ -139,14 +139,14 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router, const
               const float* logits_in, int32_t* topk_idx, float* topk_w, float* logits_out,
               void* ws, size_t ws_bytes, void* stream);
 
-/* Grouping of tokens by expert (step a3): stable counting sort of the flat pairs
+/* Grouping of tokens by expert: stable counting sort of the flat pairs
    p = t*k + j by expert id.  counts[e], offsets = exclusive prefix sum [E+1],
    perm = pairs in ascending (expert, p) order, inv_perm[perm[i]] = i.
    Every topk_idx entry must lie in [0, E). */
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                 int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Expert SwiGLU FFNs on the grouped pairs (steps a4, a5, a6, a7):
+/* Expert SwiGLU FFNs on the grouped pairs (gate/up, down, shared expert, 4-bit weights):
    y_sorted[i] = y_e(x[perm[i] / k]) for the expert e whose segment
    [offsets[e], offsets[e+1]) holds slot i; y_shared[t] = shared(x[t]) (NULL if
    n_shared = 0).  perm/offsets as produced by moe_permute. */
@@ -154,13 +154,13 @@ int moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* perm, 
                     const moe_weights* weights, void* y_sorted, void* y_shared,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* Gate-weighted combine (step a8): out[t] = sum over j in ascending expert order
+/* Gate-weighted combine: out[t] = sum over j in ascending expert order
    (= ascending inv_perm[t*k+j]) of topk_w[t,j] * y_sorted[inv_perm[t*k+j]],
    + y_shared[t] (nullable), accumulated in fp32; with MOE_F_ACCUMULATE added to out. */
 int moe_combine(const moe_shape* shape, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
                 const void* y_shared, void* out, void* stream);
 
-/* Whole layer (steps a1..a8), fusing where it pays (at decode the combine is
+/* Whole layer (router to combine), fusing where it pays (at decode the combine is
    fused into the down projection).  topk_idx_out (nullable) receives [T,k]. */
 int moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
                       const moe_weights* weights, void* out, int32_t* topk_idx_out,
@@ -178,7 +178,7 @@ int moe_layer_forward_masked(const moe_shape* shape, const void* x, const void* 
                              const moe_weights* weights, const uint8_t* expert_mask, void* out,
                              int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Residual stack of n_layers MoE layers (step a9) on the fp32 residual stream
+/* Residual stack of n_layers MoE layers on the fp32 residual stream
    h [T, d_model]: for each layer l, x = act(h / sqrt(mean(h^2) + 1e-6)) rounded to
    the act dtype, then h += layer_l(x) in fp32.  w_router, b_router and weights are
    HOST arrays of n_layers entries (each holding device pointers); b_router may be
@@ -187,7 +187,7 @@ int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const 
                       const float* const* b_router, const moe_weights* weights,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* MXFP4 -> f32 dequantisation (step a7 on its own): out[r*K + j] =
+/* MXFP4 -> f32 dequantisation on its own: out[r*K + j] =
    (-1)^b3 * M[code & 7] * 2^(s - 127) with M = {0, .5, 1, 1.5, 2, 3, 4, 6},
    NaN for s = 0xFF; codes [rows, K/2], scales [rows, K/32]; K % 32 == 0. */
 int moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K, float* out,

@@ -18,6 +18,8 @@
 //               every token; its 8 wavefronts split the slots, each adds g * (W2_e[i] . a) for
 //               its slots, and the 8 partial sums are added in wavefront order through LDS --
 //               a fixed order, so results are deterministic and need no atomics.
+//   dec_w2c1    the same for a single token: the workgroup's (slot, row) units are cut into 8
+//               contiguous ranges, one per wavefront, so no wavefront makes two round trips.
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -742,8 +744,6 @@ hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const
     return hipGetLastError();
 }
 
-// One 8-wavefront workgroup per CU at most (the routing prologue runs once per workgroup);
-// the wavefronts loop over the (slot, R columns) items.
 // Workgroups of `kernel` that are resident on the current device at once: its occupancy per CU
 // (registers, LDS) times the CU count, cached per (kernel, device, LDS bytes).
 static int resident_blocks(const void* kernel, int threads, size_t lds) {

@@ -1,4 +1,4 @@
-// Decode path of the expert FFNs (steps a4..a8 at small T): grouped GEMV that streams only the
+// Decode path of the expert FFNs at small T (gate/up, down, combine): grouped GEMV that streams only the
 // active experts' weight rows from HBM.
 //
 // At decode a token needs only its k experts (plus the shared one); the pages' whole point is

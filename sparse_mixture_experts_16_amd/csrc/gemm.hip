@@ -1,4 +1,4 @@
-// Prefill path (steps a1, a4..a7 at large T): grouped GEMM on the gfx950 matrix cores.
+// Prefill path (router logits and the expert FFNs at large T): grouped GEMM on the gfx950 matrix cores.
 //
 // At prefill thousands of tokens reach nearly every expert (dothoosh.com FreeToken article,
 // "FreeToken architecture and the sparsity puzzle", first failure mode), so each expert's

@@ -1,5 +1,5 @@
-// Gather combine (step a8, prefill path), standalone MXFP4 dequantisation (step a7) and the
-// residual-stack RMS normalisation (step a9).
+// Gather combine (prefill path), standalone MXFP4 / NVFP4 dequantisation and the
+// residual-stack RMS normalisation.
 #include "common.h"
 #include "kernels.h"
 #include "wchunk.h"

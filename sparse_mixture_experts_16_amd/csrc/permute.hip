@@ -1,4 +1,4 @@
-// Grouping tokens by expert (step a3): a stable counting sort of the flat (token, slot) pairs
+// Grouping tokens by expert: a stable counting sort of the flat (token, slot) pairs
 // p = t*k + j by expert id, with an LDS histogram, a prefix scan and a stable scatter.
 //
 // At prefill thousands of tokens reach nearly every expert (dothoosh.com FreeToken article,

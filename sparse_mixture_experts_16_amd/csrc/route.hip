@@ -1,4 +1,4 @@
-// Router (steps a1, a2): logits l = x W_r^T + b, then a wavefront per token selects the
+// Router: logits l = x W_r^T + b, then a wavefront per token selects the
 // k largest logits (ties -> lowest expert index) and forms the softmax gates.
 //
 // The pages say only that each token is routed to k experts per layer and that the
