@@ -427,10 +427,17 @@ __global__ void __launch_bounds__(256) router_reduce(const float* __restrict__ p
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
                                     int E, float* part, size_t part_bytes, hipStream_t st) {
     // T/128 x E/128 tiles alone leave most CUs idle: split K (>= 4 steps of 32 each) over up to 8
-    // workgroups when the partials fit the scratch given.
+    // workgroups when the partials fit the scratch given, but not beyond one round of the device's
+    // workgroup slots (two per CU): a second round and its larger partials cost more than they
+    // save (c3 prefill router 53 + 15 us at 8 ways against 41 + 10 us at 4).
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int64_t slots = 2 * (int64_t)cus;
     const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + 127) / 128);
     int ks = 1;
-    while (ks < 8 && tiles * ks * 2 <= 2048 && d % (32 * ks * 2) == 0 && d / (ks * 2) >= 128 &&
+    while (ks < 8 && tiles * ks * 2 <= slots && d % (32 * ks * 2) == 0 && d / (ks * 2) >= 128 &&
            (size_t)ks * 2 * T * E * 4 <= part_bytes)
         ks *= 2;
     GemmArgs p{};
