@@ -11,7 +11,9 @@
 //   dec_w13     every workgroup first redoes the routing from the logits in LDS -- top-k and
 //               gates per token, grouping by expert into a slot table (expert, first sorted
 //               position, pairs, token mask) -- then computes its share of
-//               a[pos, j] = silu(Wg_e[j] . x_t) * (Wu_e[j] . x_t) in fp32.  Workgroup 0 also
+//               a[pos, j] = silu(Wg_e[j] . x_t) * (Wu_e[j] . x_t) in fp32.  The shared
+//               expert's items come first and their rows are pulled into L2 during the
+//               routing, which does not decide them.  Workgroup 0 also
 //               publishes the routing (top-k, slot table, per-position gate) for the down
 //               kernel and the caller.
 //   dec_w2c     down projection fused with the combine: a workgroup owns R output rows of
@@ -277,7 +279,11 @@ __device__ __forceinline__ int dec_slot_scan(DecRoute& R, const int* s_cnt, cons
     return pa;
 }
 
-__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on) {
+// `mid` runs once the logits are in LDS, before the top-k (the rest of the routing issues no
+// global loads, so loads that `mid` leaves in flight never delay it).
+template <typename Mid>
+__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on,
+                              Mid&& mid) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
@@ -288,6 +294,7 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     }
     for (int e = tid; e <= E; e += blockDim.x) s_on[e] = io.emask ? io.emask[e] : 1;
     __syncthreads();
+    mid();
     // top-k + gates, a wavefront per token
     for (int t = wv; t < T; t += NW) {
         const float* l = s_logits + t * E;
@@ -425,6 +432,36 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
     constexpr int EC = W::EC;
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     __shared__ DecRoute rs;
+    const int lane = lane_id();
+    const int ngr = (p.f + R - 1) / R, ngs = (p.fs + R - 1) / R;
+    const int NC = p.d / EC;
+    const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
+    const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
+    const int NWB = blockDim.x / MOE_WAVE;
+    // The shared expert does not depend on the routing, so its items come first: a wavefront
+    // whose first item is one touches the 64-byte pieces of that item's rows (one dword each,
+    // the first NP * 4 KB of a row) while its workgroup routes -- after the logits are in LDS,
+    // so the routing's own loads never wait behind these -- and its loads after the routing
+    // then hit L2.  The dwords are only held until the routing ends.
+    constexpr int NP = WT <= 1 ? 2 : 1;
+    const bool shared_on = p.rt.n_shared && (!p.rt.emask || p.rt.emask[p.rt.E]);
+    const int s_items = shared_on ? ngs : 0;
+    const int item0 = blockIdx.x * NWB + wave_id();
+    uint32_t warm[2][R][NP];
+    auto warm_l2 = [&]() {
+        const int j0 = item0 * R;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < NP; ++i) {
+                    const int64_t o = (int64_t)(lane + i * MOE_WAVE) * 64;
+                    warm[h][r][i] = 0;
+                    if (item0 < s_items && j0 + r < p.fs && o < rb)
+                        warm[h][r][i] = *reinterpret_cast<const uint32_t*>(p.s13 + (int64_t)(h * p.fs + j0 + r) * rb + o);
+                }
+    };
     {
         const int T = p.rt.T, E = p.rt.E, k = p.rt.k;
         unsigned char* q = dyn_lds;
@@ -435,22 +472,21 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
         int* s_cnt = reinterpret_cast<int*>(q); q += (size_t)E * 4;
         int* s_mask = reinterpret_cast<int*>(q); q += (size_t)E * 4;
         int* s_on = reinterpret_cast<int*>(q);
-        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask, s_on);
+        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask, s_on, warm_l2);
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < NP; ++i) asm volatile("" ::"v"(warm[h][r][i]));
 
-    const int lane = lane_id();
-    const int ngr = (p.f + R - 1) / R, ngs = (p.fs + R - 1) / R;
-    const int r_items = rs.n_routed * ngr;
-    const int n_items = r_items + (rs.n_slots > rs.n_routed ? ngs : 0);
-    const int NC = p.d / EC;
-    const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
-    const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
-    const int NWB = blockDim.x / MOE_WAVE;
-    for (int item = blockIdx.x * NWB + wave_id(); item < n_items; item += gridDim.x * NWB) {
-        const int s = item < r_items ? item / ngr : rs.n_routed;
-        const int jg = item < r_items ? item % ngr : item - r_items;
+    const int n_items = s_items + rs.n_routed * ngr;
+    for (int item = item0; item < n_items; item += gridDim.x * NWB) {
+        const bool sh = item < s_items;
+        const int s = sh ? rs.n_routed : (item - s_items) / ngr;
+        const int jg = sh ? item : (item - s_items) % ngr;
         const int4 S = rs.slot[s];
-        const bool sh = s >= rs.n_routed;
         const int fc = sh ? p.fs : p.f;
         const int j0 = jg * R;
         const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)S.x * 2 * p.f * rb;
