@@ -346,3 +346,26 @@ def test_decode_routing_exact_ties(E, k, tied, T):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
     assert_close(host(res["out"]), ref["out"], what="ties")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_routing_signed_zero_inf_nan(T):
+    """Decode routing order on special logits: +0 and -0 tie (lower index first), -inf ranks below
+    every finite logit and NaN below -inf (so with k = 6 of 8 the NaN experts stay out)."""
+    E, k = 8, 6
+    s = mi.LayerSpec("specials", T, 128, 64, E, k, 0, 0, "bf16", "bf16", 1.0, 0.05, 0.05, seed=51)
+    x = mi.host_x(s)
+    wr, _ = mi.host_router(s)
+    wr = wr.copy()
+    special = [1, 2, 3, 4, 5, 7]
+    wr[special] = 0.0   # these experts' logits are their bias exactly
+    b = np.full(E, -1.0e4, np.float32)
+    b[[1, 7]] = np.nan
+    b[2], b[3], b[4], b[5] = -0.0, -np.inf, 0.0, 1.0
+    w = mi.host_experts(s)
+    ref = oracle.layer_forward(s, x, wr, b, w)
+    assert (ref["topk_idx"][:, :3] == [5, 2, 4]).all() and (ref["topk_idx"][:, 5] == 3).all()
+    res = moe.layer_forward(s, dev(x), dev(wr), dev(b), {n: dev(v) for n, v in w.items()})
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
+    assert_close(host(res["out"]), ref["out"], what="specials")
