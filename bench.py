@@ -67,13 +67,13 @@ KERNEL_SOURCES = {
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=27761.8, write_kib=54.3),
-    "c3_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=26278.2, write_kib=97.2),
-    "c3nv_decode_T1": dict(src="decode:95054e48d51c9b0a", fetch_kib=27810.9, write_kib=96.2),
-    "c4_stack": dict(src="decode:95054e48d51c9b0a", fetch_kib=26277.9, write_kib=97.0),
-    "c2_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=745945.2, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:da39dba84be6bf37", fetch_kib=2139238.7, write_kib=393216.0),
-    "c3_prefill_mx": dict(src="mx:7167d4a1ab5db82d", fetch_kib=1366076.8, write_kib=102114.5),
+    "c1_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=27770.0, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=26285.8, write_kib=97.6),
+    "c3nv_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=27814.2, write_kib=96.2),
+    "c4_stack": dict(src="decode:83778c19da44cadc", fetch_kib=26285.2, write_kib=97.5),
+    "c2_prefill": dict(src="gemm:f1d5b35a95ce90d8", fetch_kib=746563.7, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:f1d5b35a95ce90d8", fetch_kib=2129073.9, write_kib=393216.0),
+    "c3_prefill_mx": dict(src="mx:f640a6d2354f4b94", fetch_kib=1377996.2, write_kib=102178.8),
 }
 
 
