@@ -67,22 +67,31 @@ KERNEL_SOURCES = {
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=27770.0, write_kib=54.3),
-    "c3_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=26285.8, write_kib=97.6),
-    "c3nv_decode_T1": dict(src="decode:83778c19da44cadc", fetch_kib=27814.2, write_kib=96.2),
-    "c4_stack": dict(src="decode:83778c19da44cadc", fetch_kib=26285.2, write_kib=97.5),
-    "c2_prefill": dict(src="gemm:f1d5b35a95ce90d8", fetch_kib=746563.7, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:f1d5b35a95ce90d8", fetch_kib=2129073.9, write_kib=393216.0),
-    "c3_prefill_mx": dict(src="mx:f640a6d2354f4b94", fetch_kib=1377996.2, write_kib=102178.8),
+    "c1_decode_T1": dict(src="decode:0c7c3e0e57d4061c", fetch_kib=27770.0, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:0c7c3e0e57d4061c", fetch_kib=26285.8, write_kib=97.6),
+    "c3nv_decode_T1": dict(src="decode:0c7c3e0e57d4061c", fetch_kib=27814.2, write_kib=96.2),
+    "c4_stack": dict(src="decode:0c7c3e0e57d4061c", fetch_kib=26285.2, write_kib=97.5),
+    "c2_prefill": dict(src="gemm:6c720155cb6b1c9c", fetch_kib=746563.7, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:6c720155cb6b1c9c", fetch_kib=2129073.9, write_kib=393216.0),
+    "c3_prefill_mx": dict(src="mx:81115b7c99f1254b", fetch_kib=1377996.2, write_kib=102178.8),
 }
 
 
+def _code_only(src: str) -> str:
+    """C/HIP source without comments, whitespace runs collapsed (string literals kept as is)."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    body = tok.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(body.split())
+
+
 def source_digest(kind: str) -> str:
+    """Digest of the code (comments and layout excluded) of one kernel family's sources."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_16_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mixture_experts_16_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return f"{kind}:{h.hexdigest()[:16]}"
 
 
