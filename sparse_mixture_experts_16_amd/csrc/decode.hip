@@ -425,8 +425,8 @@ __device__ __forceinline__ void a_chunk(const float* row, int ncp, int c, float 
 template <int WT> struct DecAct { using T = uint16_t; };
 template <> struct DecAct<0> { using T = float; };
 
-template <int WT, int R, int U>
-__global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
+template <int WT, int R, int U, int TQ>
+__global__ void __launch_bounds__(512, (WT == 1 && TQ == 1) ? 8 : 1) dec_w13(DecFfnArgs p) {
     using W = WChunk<WT>;
     using A = typename DecAct<WT>::T;
     constexpr int EC = W::EC;
@@ -494,15 +494,15 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
         const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)S.x * 2 * p.f * rb;
         const uint8_t* sbp = (WT >= 2) ? (sh ? p.s13s : p.w13s + (int64_t)S.x * 2 * p.f * sb) : nullptr;
         const float gsc = sh ? p.gs13 : p.g13;
-        // the slot's tokens in ascending order, 4 at a time; one K step covers a row in the
+        // the slot's tokens in ascending order, TQ at a time; one K step covers a row in the
         // configured shapes, otherwise rows are re-streamed per group of tokens (cache hits)
         uint32_t mask = (uint32_t)S.w;
         int pos = S.y;
         while (mask) {
-            int tk[4];
+            int tk[TQ];
             int nq = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < TQ; ++q) {
                 tk[q] = -1;
                 if (mask) {
                     tk[q] = __ffs(mask) - 1;
@@ -510,11 +510,11 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
                     ++nq;
                 }
             }
-            float ag[R][4], au[R][4];
+            float ag[R][TQ], au[R][TQ];
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) ag[r][q] = au[r][q] = 0.0f;
+                for (int q = 0; q < TQ; ++q) ag[r][q] = au[r][q] = 0.0f;
             for (int st = 0; st < nsteps; ++st) {
                 const int c0 = st * MOE_WAVE * U;
                 W wg[R][U], wu[R][U];
@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
                         }
                     }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < TQ; ++q) {
                     if (tk[q] < 0) break;
                     const A* xr = reinterpret_cast<const A*>(p.x) + (int64_t)tk[q] * p.d;
 #pragma unroll
@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(512) dec_w13(DecFfnArgs p) {
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < TQ; ++q) {
                 if (q >= nq) break;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -822,11 +822,17 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                  (const uint8_t*)s2, s2s, a, out, T, d, f, n_shared ? fs : 0, fmax, k, accumulate ? 1 : 0,
                  (int)max_slots + n_shared, gsc[0], gsc[1], gsc[2], gsc[3]};
     const size_t lds = dec_route_lds_bytes(T, E, k);
-#define MOE_DW13(WTV, RV, UV)                                                                                    \
+#define MOE_DW13Q(WTV, RV, UV, TQV)                                                                              \
     do {                                                                                                         \
         const int64_t items = max_slots * ((f + RV - 1) / RV) + (n_shared ? (fs + RV - 1) / RV : 0);             \
-        const int res = resident_blocks((const void*)dec_w13<WTV, RV, UV>, 512, lds);                           \
-        MOE_LAUNCH(PROF_FFN_UP, (dec_w13<WTV, RV, UV>), dim3(dec_grid(items, res)), dim3(512), lds, st, p);    \
+        const int res = resident_blocks((const void*)dec_w13<WTV, RV, UV, TQV>, 512, lds);                      \
+        MOE_LAUNCH(PROF_FFN_UP, (dec_w13<WTV, RV, UV, TQV>), dim3(dec_grid(items, res)), dim3(512), lds, st, p); \
+    } while (0)
+    // one token needs a single accumulator per row (fewer registers, more resident wavefronts)
+#define MOE_DW13(WTV, RV, UV)                 \
+    do {                                      \
+        if (T == 1) MOE_DW13Q(WTV, RV, UV, 1); \
+        else MOE_DW13Q(WTV, RV, UV, 4);       \
     } while (0)
     // about 8 16-byte loads per lane in flight per item (HBM streams best at 4-8 per lane)
     if (wt == 0) MOE_DW13(0, 2, 1);
@@ -834,6 +840,7 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
     else if (wt == 2) MOE_DW13(2, 2, 2);
     else MOE_DW13(3, 1, 2);
 #undef MOE_DW13
+#undef MOE_DW13Q
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 #define MOE_DW2(WTV, RV, UV)                                                                                     \
