@@ -73,11 +73,13 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // k = 8*(l/32)..+7; B lane l: column l%32, same k; accumulator j of lane l: row
 // 8*(j/4) + 4*(l/32) + j%4, column l%32).
 //
-// K pipeline: a ring of three LDS stages filled straight from HBM by global_load_lds_dwordx4
-// (each lane's 16 bytes land at the wave's LDS base + 16 * lane; no register staging).  While
-// stage kt is consumed, stages kt+1 and kt+2 are in flight; the wait for stage kt is a
-// vmcnt(n) that still lets the next stage's loads be outstanding, followed by a bare
-// s_barrier, so the compiler's full vmcnt(0) of __syncthreads never drains the pipe.
+// K pipeline: a ring of NS LDS stages filled straight from HBM by global_load_lds_dwordx4
+// (each lane's 16 bytes land at the wave's LDS base + 16 * lane; no register staging).  With
+// three stages, while stage kt is consumed, stages kt+1 and kt+2 are in flight; the wait for
+// stage kt is a vmcnt(n) that still lets the next stage's loads be outstanding, followed by a
+// bare s_barrier, so the compiler's full vmcnt(0) of __syncthreads never drains the pipe.  With
+// two stages (the down projection's 256-column tiles, whose two A planes and 256 B rows would
+// not fit three deep at two workgroups per CU), stage kt+1 loads while stage kt is consumed.
 // Tile rows are 64 bytes (32 bf16) unpadded; 16-byte chunk c of row r sits at physical chunk
 // c ^ (((r >> 1) ^ (r >> 2)) & 3), which spreads every 8 (and 16) consecutive rows' fragment
 // reads over distinct banks.
@@ -90,9 +92,10 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // through the bf16 matrix cores.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
-template <int MODE, int WT, int BN, bool SPLIT, int NWN>
+template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3>
 __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 waves per SIMD: <= 256 registers
-    constexpr int BM = TBM, BK = 32, NS = 3;
+    constexpr int BM = TBM, BK = 32;
+    static_assert(NS == 2 || NS == 3, "ring depth");
     constexpr int THREADS = 128 * NWN;              // 2 wavefronts along M x NWN along N
     constexpr int NPL = SPLIT ? 2 : 1;              // A planes
     constexpr int WN = BN / NWN;                    // wave tile columns
@@ -287,15 +290,16 @@ __global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 wav
     // matrix-core time goes to the other workgroup on the CU
     const bool live = wm * 64 < mrows;
     issue(0);
-    if (nk > 1) issue(1);
+    if (NS == 3 && nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt % NS;
         asm volatile("" ::: "memory");
-        if (kt + 1 < nk) VM_WAIT(OPS);
+        // three stages: stage kt + 1 stays in flight; two: every wait drains the ring
+        if (NS == 3 && kt + 1 < nk) VM_WAIT(OPS);
         else VM_WAIT(0);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (kt + 2 < nk) issue(kt + 2);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
         if (!live) continue;
 
         uint32_t sc_w[NT32];
@@ -487,7 +491,18 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
-    constexpr int BN = 128, NWN = 2;
+    constexpr int NWN = 2;
+    if (d % 256 == 0) {
+        // 256 output columns per tile, two stages (the lo/hi A planes and 256 B rows fill 64 KB
+        // per stage pair; two workgroups per CU)
+        constexpr int BN = 256;
+        const int nt = d / BN;
+        const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
+        if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true, NWN, 2>), dim3(grid), dim3(128 * NWN), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true, NWN, 2>), dim3(grid), dim3(128 * NWN), 0, st, p);
+        return hipGetLastError();
+    }
+    constexpr int BN = 128;
     const int nt = (d + BN - 1) / BN;
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
     if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
