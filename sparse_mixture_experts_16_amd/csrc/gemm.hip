@@ -93,7 +93,7 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3>
-__global__ void __launch_bounds__(128 * NWN, 2) ggemm(GemmArgs p) {  // >= 2 waves per SIMD: <= 256 registers
+__global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p) {  // 2 waves per SIMD: <= 256 registers
     constexpr int BM = TBM, BK = 32;
     static_assert(NS == 2 || NS == 3, "ring depth");
     constexpr int THREADS = 128 * NWN;              // 2 wavefronts along M x NWN along N
@@ -478,6 +478,14 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             const uint8_t* mask, hipStream_t st) {
     GemmArgs p{x, perm, offsets, (const uint8_t*)w13, w13s, (const uint8_t*)s13, s13s, nullptr, a, nullptr,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
+    if (wt == 2 && f % 256 == 0 && (!n_shared || fs % 256 == 0)) {
+        // MXFP4 weights: 16 code bytes per row and stage, so a 128 x 512 tile (8 wavefronts, one
+        // workgroup per CU) halves the activation reads per weight row at little LDS cost
+        constexpr int BN = 512, NWN = 4;
+        const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
+        MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+        return hipGetLastError();
+    }
     constexpr int BN = 256, NWN = 2;  // 128 gate/up column pairs per tile, 4 wavefronts
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
     if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
