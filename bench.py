@@ -71,8 +71,8 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c3_decode_T1": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=26256.3, write_kib=96.8),
     "c3nv_decode_T1": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=27789.2, write_kib=96.2),
     "c4_stack": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=26256.1, write_kib=96.7),
-    "c2_prefill": dict(src="gemm:034b6610e6be841c", fetch_kib=762844.8, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:034b6610e6be841c", fetch_kib=2111571.8, write_kib=393216.0),
+    "c2_prefill": dict(src="gemm:3a79fcd2ca97bd29", fetch_kib=762210.1, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:3a79fcd2ca97bd29", fetch_kib=1327013.7, write_kib=393216.0),
     "c3_prefill_mx": dict(src="mx:81115b7c99f1254b", fetch_kib=1377996.2, write_kib=102178.8),
 }
 
