@@ -124,39 +124,62 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of device workspace the calls below need for this shape (0 on an invalid shape).
-   A workspace buffer must be zero-filled before its first use; every call leaves it ready
-   for the next one (the decode router keeps a completion counter in its first bytes). */
+   The contents of a workspace need no initialisation: every call writes each region it
+   reads before reading it. */
 size_t moe_workspace_size(const moe_shape* shape);
 
 /* Static description of a status code. */
 const char* moe_status_string(int status);
 
-/* Router: logits -> top-k selection -> gates.
+/* Router: logits -> top-k selection -> gates.  Each token activates k of the E routed
+   experts of the layer and the choice changes from token to token (dothoosh.com FreeToken
+   article, "FreeToken architecture and the sparsity puzzle": 6 of 256 experts per layer;
+   aihot.vn FreeToken article, "The gap it targets").  The pages give no gating formula; the
+   plain top-k softmax reading is computed: the k largest logits (ties -> lower expert index,
+   NaN below every number, +0 == -0), gates = softmax over those k (MOE_F_NO_RENORM: the full
+   softmax read at them).
    logits_in: NULL -> logits are computed from x, w_router, b_router; else a [T,E] f32
    array used as the logits (x, w_router, b_router ignored).  logits_out (nullable)
-   receives the logits used.  topk_idx, topk_w as described above. */
+   receives the logits used.  topk_idx [T,k] in descending-logit order, topk_w [T,k].
+   Errors: INVALID_ARG for a bad shape or a NULL/misaligned required pointer, WORKSPACE for
+   a short workspace; nothing is enqueued then. */
 int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
               const float* logits_in, int32_t* topk_idx, float* topk_w, float* logits_out,
               void* ws, size_t ws_bytes, void* stream);
 
-/* Grouping of tokens by expert: stable counting sort of the flat pairs
-   p = t*k + j by expert id.  counts[e], offsets = exclusive prefix sum [E+1],
-   perm = pairs in ascending (expert, p) order, inv_perm[perm[i]] = i.
-   Every topk_idx entry must lie in [0, E). */
+/* Grouping of tokens by expert.  A prefill batch sends thousands of tokens to nearly every
+   expert at once (dothoosh.com FreeToken article, "FreeToken architecture and the sparsity
+   puzzle", the first failure mode of per-token expert caching), so the pairs are grouped per
+   expert before the expert FFNs run as one grouped GEMM: a stable counting sort of the flat
+   pairs p = t*k + j by expert id.  counts[e] [E], offsets = exclusive prefix sum [E+1],
+   perm [T*k] = pairs in ascending (expert, p) order, inv_perm[perm[i]] = i (all int32,
+   device).  Every topk_idx entry must lie in [0, E) (not checked on the device).  Errors as
+   moe_route. */
 int moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                 int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Expert SwiGLU FFNs on the grouped pairs (gate/up, down, shared expert, 4-bit weights):
-   y_sorted[i] = y_e(x[perm[i] / k]) for the expert e whose segment
-   [offsets[e], offsets[e+1]) holds slot i; y_shared[t] = shared(x[t]) (NULL if
-   n_shared = 0).  perm/offsets as produced by moe_permute. */
+/* Expert SwiGLU FFNs on the grouped pairs.  Only the selected experts compute, each over the
+   tokens routed to it (dothoosh.com FreeToken article, "FreeToken architecture and the
+   sparsity puzzle": 13B of 284B parameters active per token), with BF16 or 4-bit expert
+   weights (same article, "Benchmarks and real performance": MXFP4), beside the always-on
+   shared expert when n_shared = 1 (dothoosh.com TurboFieldfare article, "Background: Gemma 4
+   26B A4B": 8 of 128 routed + 1 shared).  y_sorted[i] = y_e(x[perm[i] / k]) for the expert e
+   whose segment [offsets[e], offsets[e+1]) holds slot i, y_e(v) = W2_e (silu(Wg_e v) *
+   (Wu_e v)); y_shared[t] = shared(x[t]) (NULL if n_shared = 0).  perm/offsets as produced by
+   moe_permute (a slot outside every segment is left unwritten).  T <= 32 runs the grouped
+   GEMV kernels, larger T the grouped MFMA GEMM (MOE_F_FORCE_* override).  Errors as
+   moe_route, plus INVALID_ARG for missing weight or scale pointers. */
 int moe_grouped_ffn(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
                     const moe_weights* weights, void* y_sorted, void* y_shared,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* Gate-weighted combine: out[t] = sum over j in ascending expert order
+/* Gate-weighted combine.  The experts' partial results add up exactly to the layer's output
+   (dothoosh.com FreeToken article, "FreeToken architecture and the sparsity puzzle",
+   mechanism 1: the GPU's and the CPU's partial sums merge with no estimate; ai4bro.com
+   FreeToken article, "Key points").  out[t] = sum over j in ascending expert order
    (= ascending inv_perm[t*k+j]) of topk_w[t,j] * y_sorted[inv_perm[t*k+j]],
-   + y_shared[t] (nullable), accumulated in fp32; with MOE_F_ACCUMULATE added to out. */
+   + y_shared[t] (nullable), accumulated in fp32 and rounded once to the act dtype; with
+   MOE_F_ACCUMULATE added to out.  Uses no workspace.  Errors as moe_route. */
 int moe_combine(const moe_shape* shape, const void* y_sorted, const int32_t* inv_perm, const float* topk_w,
                 const void* y_shared, void* out, void* stream);
 
@@ -179,12 +202,15 @@ int moe_layer_forward_masked(const moe_shape* shape, const void* x, const void* 
                              int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Residual stack of n_layers MoE layers on the fp32 residual stream
-   h [T, d_model]: for each layer l, x = act(h / sqrt(mean(h^2) + 1e-6)) rounded to
-   the act dtype, then h += layer_l(x) in fp32.  w_router, b_router and weights are
-   HOST arrays of n_layers entries (each holding device pointers); b_router may be
-   NULL.  Routing is recomputed in every layer. */
+   h [T, d_model] (DeepSeek-V4-Flash: 43 layers, each routing 6 of 256 experts afresh;
+   dothoosh.com FreeToken article, "FreeToken architecture and the sparsity puzzle"): for
+   each layer l, x = act(h / sqrt(mean(h^2) + 1e-6)) rounded to the act dtype, then
+   h += layer_l(x) in fp32.  w_router, b_router and weights are HOST arrays of n_layers
+   entries (each holding device pointers); b_router may be NULL.  Routing is recomputed in
+   every layer; topk_idx_out (nullable, DEVICE [n_layers, T, k] int32) receives each layer's
+   selection.  Errors as moe_layer_forward. */
 int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const void* const* w_router,
-                      const float* const* b_router, const moe_weights* weights,
+                      const float* const* b_router, const moe_weights* weights, int32_t* topk_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* MXFP4 -> f32 dequantisation on its own: out[r*K + j] =

@@ -60,7 +60,7 @@ _lib.moe_grouped_ffn.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _v
 _lib.moe_combine.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp, _sz, _vp]
-_lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _sz, _vp]
+_lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
 _lib.moe_nvfp4_dequant.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp]
 _lib.moe_mxfp8_quantize.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _vp]
@@ -121,7 +121,7 @@ def workspace(shape: Shape, device="cuda"):
     dev = torch.device(device)
     cur = _ws_cache.get(dev)
     if cur is None or cur.numel() < n:
-        cur = torch.zeros(n, dtype=torch.uint8, device=dev)  # a fresh workspace must start zero-filled
+        cur = torch.empty(n, dtype=torch.uint8, device=dev)  # needs no initialisation
         _ws_cache[dev] = cur
     return cur
 
@@ -190,14 +190,15 @@ def layer_forward_masked_raw(shape: Shape, x, w_router, b_router, weights: Weigh
                                          _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward_masked")
 
 
-def stack_forward(shape: Shape, h, w_routers, b_routers, weights_list, ws=None, stream=None):
+def stack_forward(shape: Shape, h, w_routers, b_routers, weights_list, ws=None, stream=None, topk_idx_out=None):
+    """moe_stack_forward; topk_idx_out (optional) is a device int32 tensor [n_layers, T, k]."""
     n = len(weights_list)
     ws = workspace(shape) if ws is None else ws
     wr = (_vp * n)(*[_ptr(t) for t in w_routers])
     br = (_vp * n)(*[_ptr(t) for t in b_routers]) if b_routers is not None else None
     W = (Weights * n)(*weights_list)
-    _check(_lib.moe_stack_forward(ctypes.byref(shape), n, _ptr(h), wr, br, W, _ptr(ws), ws.numel(),
-                                  _stream(stream)), "moe_stack_forward")
+    _check(_lib.moe_stack_forward(ctypes.byref(shape), n, _ptr(h), wr, br, W, _ptr(topk_idx_out), _ptr(ws),
+                                  ws.numel(), _stream(stream)), "moe_stack_forward")
 
 
 def mxfp4_dequant(codes, scales, out, stream=None):

@@ -24,7 +24,7 @@ int act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 // Workspace regions (byte offsets from ws).
 struct Layout {
-    size_t ticket, logits, topk_idx, topk_w, counts, offsets, perm, inv, act_list, tile_off, meta, blk, slots, pos_tok,
+    size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, act_list, tile_off, meta, blk, slots, pos_tok,
         pos_gate, a, y, ysh, xn, total;
 };
 
@@ -38,7 +38,6 @@ Layout layout(const moe_shape* s) {
     const size_t nblk = P > PERMUTE_SMALL_MAX ? (P + pc - 1) / pc : 0;
     const size_t fmax = fs > f ? fs : f;
     size_t o = 0;
-    L.ticket = o; o = up(o + 4);   // zero while no call runs (see moe_workspace_size)
     L.logits = o; o = up(o + T * E * 4);
     L.topk_idx = o; o = up(o + P * 4);
     L.topk_w = o; o = up(o + P * 4);
@@ -56,8 +55,11 @@ Layout layout(const moe_shape* s) {
     // fp32 rows of width fmax at decode, two bf16 planes at prefill
     const size_t a_dec = (P + T) * fmax * 4, a_pre = (P * f + T * fs) * 4;
     L.a = o; o = up(o + (a_dec > a_pre ? a_dec : a_pre));
-    L.y = o; o = up(o + P * d * ab);  // also the router K-split scratch (written only after routing)
-    L.ysh = o; o = up(o + T * d * ab);
+    // y_sorted / y_shared: fp32 inside the layer at prefill (the combine sums unrounded expert
+    // outputs), the act dtype for the step calls; also the router K-split scratch (written only
+    // after routing) and the MX path's x codes
+    L.y = o; o = up(o + P * d * 4);
+    L.ysh = o; o = up(o + T * d * 4);
     L.xn = o; o = up(o + T * d * ab);
     L.total = o;
     return L;
@@ -149,11 +151,11 @@ void tensor_scales(const moe_shape* s, const moe_weights* w, float g[4]) {
     g[3] = nv ? w->s2_gscale : 1.0f;
 }
 
-// Routed + shared FFNs given ws-resident permute results; writes either the fused combine into
-// `out` (decode, T <= 64) or y_sorted / y_shared.
+// Routed + shared FFNs given ws-resident permute results: y_sorted / y_shared in the act dtype,
+// or in fp32 (y_f32).
 int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* act_list,
             const int32_t* tile_off, const int32_t* meta, const moe_weights* w, void* ws, const Layout& L,
-            void* y_sorted, void* y_shared, const uint8_t* mask, hipStream_t st) {
+            void* y_sorted, void* y_shared, bool y_f32, const uint8_t* mask, hipStream_t st) {
     const int wt = s->weight_dtype;
     const int fs = s->n_shared ? s->shared_d_ff : 0;
     if (use_gemm(s) && (s->flags & MOE_F_MX_GEMM)) {
@@ -167,9 +169,9 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
         MOE_TRY(launch_mx_quant_rows(MOE_BF16, x, xq, xs, T, d, st));
         MOE_TRY(launch_mxgemm_w13(xq, xs, perm, offsets, w->w13, w->w13_scale, w->s13, w->s13_scale, aq, aqs, s->T,
                                   s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, mask, st));
-        MOE_TRY(launch_mxgemm_w2(aq, aqs, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, (uint16_t*)y_sorted,
-                                 (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
-                                 s->n_shared, mask, st));
+        MOE_TRY(launch_mxgemm_w2(aq, aqs, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, y_sorted, y_shared,
+                                 y_f32, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, mask,
+                                 st));
         return MOE_OK;
     }
     if (use_gemm(s)) {
@@ -177,9 +179,9 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
         MOE_TRY(launch_ggemm_w13(wt, (const uint16_t*)x, perm, offsets, tile_off, meta, w->w13, w->w13_scale,
                                  w->s13, w->s13_scale, a, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
                                  s->n_shared, mask, st));
-        MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale,
-                                (uint16_t*)y_sorted, (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
-                                s->n_experts, s->n_shared, mask, st));
+        MOE_TRY(launch_ggemm_w2(wt, a, offsets, tile_off, meta, w->w2, w->w2_scale, w->s2, w->s2_scale, y_sorted,
+                                y_shared, y_f32, s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts,
+                                s->n_shared, mask, st));
         return MOE_OK;
     }
     float* a = at<float>(ws, L.a);
@@ -187,7 +189,7 @@ int run_ffn(const moe_shape* s, const void* x, const int32_t* perm, const int32_
     tensor_scales(s, w, gs);
     MOE_TRY(launch_gemv_w13(wt, x, perm, offsets, act_list, meta, w->w13, w->w13_scale, w->s13, w->s13_scale, a,
                             s->T, s->d_model, s->d_ff, fs, s->top_k, s->n_experts, s->n_shared, gs[0], gs[2], st));
-    MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
+    MOE_TRY(launch_gemv_w2_sorted(wt, s->act_dtype == MOE_BF16 && !y_f32, a, perm, offsets, act_list, meta, w->w2, w->w2_scale,
                                   w->s2, w->s2_scale, y_sorted, y_shared, s->T, s->d_model, s->d_ff, fs, s->top_k,
                                   s->n_experts, s->n_shared, gs[1], gs[3], st));
     return MOE_OK;
@@ -255,10 +257,12 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     }
     void* y = at<void>(ws, L.y);
     void* ysh = s->n_shared ? at<void>(ws, L.ysh) : nullptr;
-    int rc = run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y, ysh, mask, st);
+    // the expert outputs reach the combine in fp32: rounding them to bf16 first would add an
+    // error relative to each expert's output, which a near-cancelling sum can exceed
+    int rc = run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y, ysh, true, mask, st);
     if (rc != MOE_OK) return rc;
-    MOE_TRY(launch_combine(s->act_dtype == MOE_BF16 ? 1 : 0, out_dtype == MOE_BF16 ? 1 : 0, y, inv, g, ysh, out, T,
-                           d, k, accumulate, idx, mask, E, st));
+    MOE_TRY(launch_combine(0, out_dtype == MOE_BF16 ? 1 : 0, y, inv, g, ysh, out, T, d, k, accumulate, idx, mask, E,
+                           st));
     return MOE_OK;
 }
 
@@ -354,7 +358,7 @@ int moe_grouped_ffn(const moe_shape* s, const void* x, const int32_t* perm, cons
     int32_t* tile_off = at<int32_t>(ws, L.tile_off);
     int32_t* meta = at<int32_t>(ws, L.meta);
     MOE_TRY(launch_active_from_offsets(offsets, s->n_experts, GEMM_BM, act_list, tile_off, meta, st));
-    return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, nullptr, st);
+    return run_ffn(s, x, perm, offsets, act_list, tile_off, meta, w, ws, L, y_sorted, y_shared, false, nullptr, st);
 }
 
 // The two contractions of the MX prefill path as separate calls (MXFP4 weights, bf16 act, the
@@ -392,9 +396,9 @@ int moe_mx_down(const moe_shape* s, const uint8_t* a_codes, const uint8_t* a_sca
     if (rc != MOE_OK || s->T == 0) return rc;
     if (!ptr_ok(a_codes) || !ptr_ok(a_scales) || !ptr_ok(offsets) || !ptr_ok(y_sorted)) return MOE_ERR_INVALID_ARG;
     if (s->n_shared ? !ptr_ok(y_shared) : y_shared != nullptr) return MOE_ERR_INVALID_ARG;
-    MOE_TRY(launch_mxgemm_w2(a_codes, a_scales, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, (uint16_t*)y_sorted,
-                             (uint16_t*)y_shared, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0,
-                             s->top_k, s->n_experts, s->n_shared, nullptr, (hipStream_t)stream));
+    MOE_TRY(launch_mxgemm_w2(a_codes, a_scales, offsets, w->w2, w->w2_scale, w->s2, w->s2_scale, y_sorted, y_shared,
+                             false, s->T, s->d_model, s->d_ff, s->n_shared ? s->shared_d_ff : 0, s->top_k,
+                             s->n_experts, s->n_shared, nullptr, (hipStream_t)stream));
     return MOE_OK;
 }
 
@@ -439,13 +443,19 @@ int moe_layer_forward_masked(const moe_shape* s, const void* x, const void* w_ro
     return layer_entry(s, x, w_router, b_router, w, expert_mask, true, out, topk_idx_out, ws, ws_bytes, stream);
 }
 
+// Layer l's [T, k] block of the stack's optional selection output.
+static int32_t* layer_idx(int32_t* base, int l, const moe_shape* s) {
+    return base ? base + (int64_t)l * s->T * s->top_k : nullptr;
+}
+
 int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void* const* w_router,
-                      const float* const* b_router, const moe_weights* w, void* ws, size_t ws_bytes, void* stream) {
+                      const float* const* b_router, const moe_weights* w, int32_t* topk_idx_out, void* ws,
+                      size_t ws_bytes, void* stream) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
     if (n_layers < 0 || !w_router || !w) return MOE_ERR_INVALID_ARG;
     if (s->T == 0 || n_layers == 0) return MOE_OK;
-    if (!ptr_ok(h)) return MOE_ERR_INVALID_ARG;
+    if (!ptr_ok(h) || (topk_idx_out && !aligned16(topk_idx_out))) return MOE_ERR_INVALID_ARG;
     for (int l = 0; l < n_layers; ++l) {
         if ((rc = check_weights(s, &w[l])) != MOE_OK) return rc;
         if (!ptr_ok(w_router[l])) return MOE_ERR_INVALID_ARG;
@@ -458,16 +468,16 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
     if (use_decode(s)) {
         // decode: the logits kernel normalises h itself and leaves x for the FFN kernels
         for (int l = 0; l < n_layers; ++l) {
-            rc = run_decode(s, h, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr,
-                            true, ws, L, nullptr, st);
+            rc = run_decode(s, h, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true,
+                            layer_idx(topk_idx_out, l, s), true, ws, L, nullptr, st);
             if (rc != MOE_OK) return rc;
         }
         return MOE_OK;
     }
     for (int l = 0; l < n_layers; ++l) {
         MOE_TRY(launch_rmsnorm(s->act_dtype == MOE_BF16 ? 1 : 0, h, xn, s->T, s->d_model, 1e-6f, st));
-        rc = run_layer(s, xn, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true, nullptr, ws,
-                       L, nullptr, st);
+        rc = run_layer(s, xn, w_router[l], b_router ? b_router[l] : nullptr, &w[l], h, MOE_F32, true,
+                       layer_idx(topk_idx_out, l, s), ws, L, nullptr, st);
         if (rc != MOE_OK) return rc;
     }
     return MOE_OK;

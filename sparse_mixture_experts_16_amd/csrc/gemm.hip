@@ -37,8 +37,8 @@ struct GemmArgs {
     const uint8_t* sw;        // shared expert weights
     const uint8_t* swsc;
     const float* bias;        // ROUTER: b [E] or NULL
-    void* out;                // W13: a hi plane (bf16); W2: y (bf16) [P, d]; ROUTER: logits (f32) [T, E]
-    uint16_t* out_sh;         // W2: y_shared [T, d]
+    void* out;                // W13: a hi plane (bf16); W2: y (bf16 or f32) [P, d]; ROUTER: logits (f32) [T, E]
+    void* out_sh;             // W2: y_shared [T, d], the dtype of y
     int64_t lo_off;           // elements from the a hi plane to the a lo plane
     int T, d, f, fs, k, E, n_shared;
     const uint8_t* mask;      // nullable [E + 1]: groups whose byte is 0 get no tiles
@@ -92,7 +92,9 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // through the bf16 matrix cores.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
-template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3>
+// YF32 (down projection only): y is written in fp32 straight from the accumulators, so the
+// combine that follows sums unrounded expert outputs.
+template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 = false>
 __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p) {  // 2 waves per SIMD: <= 256 registers
     constexpr int BM = TBM, BK = 32;
     static_assert(NS == 2 || NS == 3, "ring depth");
@@ -354,6 +356,23 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                     if (n < N) o[n] = acc[ms][ns][j] + (!part && p.bias ? p.bias[n] : 0.0f);
                 }
             }
+    } else if constexpr (MODE == MODE_W2 && YF32) {
+        // fp32 y from the accumulators: the 32 lanes holding one row write 128 contiguous bytes
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
+                if (r >= mrows) continue;
+                const int row = m0 + r;
+                float* o = shared ? reinterpret_cast<float*>(p.out_sh) + (int64_t)row * p.d
+                                  : reinterpret_cast<float*>(p.out) + (int64_t)(base + row) * p.d;
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns) {
+                    const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
+                    if (n < N) o[n] = acc[ms][ns][j];
+                }
+            }
     } else {
         // Stage the tile's bf16 outputs in LDS (the ring is free once every wavefront is past
         // its last fragment read), one plane at a time, then store whole 16-byte row chunks.
@@ -405,7 +424,7 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                     o = reinterpret_cast<uint16_t*>(p.out) + (pl ? p.lo_off : 0) +
                         (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f) + col0 + ch * 8;
                 else
-                    o = (shared ? p.out_sh + (int64_t)row * p.d
+                    o = (shared ? reinterpret_cast<uint16_t*>(p.out_sh) + (int64_t)row * p.d
                                 : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
                 *reinterpret_cast<uint4*>(o) = v;
             }
@@ -494,27 +513,28 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
 }
 
 hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t*, const int32_t*,
-                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y,
-                           uint16_t* y_shared, int T, int d, int f, int fs, int k, int E, int n_shared,
+                           const void* w2, const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* y,
+                           void* y_shared, bool y_f32, int T, int d, int f, int fs, int k, int E, int n_shared,
                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
     constexpr int NWN = 2;
-    if (d % 256 == 0) {
-        // 256 output columns per tile, two stages (the lo/hi A planes and 256 B rows fill 64 KB
-        // per stage pair; two workgroups per CU)
-        constexpr int BN = 256;
-        const int nt = d / BN;
-        const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-        if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true, NWN, 2>), dim3(grid), dim3(128 * NWN), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true, NWN, 2>), dim3(grid), dim3(128 * NWN), 0, st, p);
-        return hipGetLastError();
-    }
-    constexpr int BN = 128;
-    const int nt = (d + BN - 1) / BN;
-    const unsigned grid = grid8(max_tiles(T, k, E, n_shared, nt, nt));
-    if (wt == 1) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BN, true, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
-    else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BN, true, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+#define MOE_W2(BNV, NSV)                                                                                         \
+    do {                                                                                                         \
+        const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (d + BNV - 1) / BNV, (d + BNV - 1) / BNV));     \
+        if (wt == 1 && y_f32)                                                                                    \
+            MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BNV, true, NWN, NSV, true>), dim3(grid), dim3(128 * NWN), 0, st, p); \
+        else if (wt == 1)                                                                                        \
+            MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 1, BNV, true, NWN, NSV>), dim3(grid), dim3(128 * NWN), 0, st, p); \
+        else if (y_f32)                                                                                          \
+            MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BNV, true, NWN, NSV, true>), dim3(grid), dim3(128 * NWN), 0, st, p); \
+        else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm<MODE_W2, 2, BNV, true, NWN, NSV>), dim3(grid), dim3(128 * NWN), 0, st, p); \
+    } while (0)
+    // 256 output columns per tile, two stages (the lo/hi A planes and 256 B rows fill 64 KB per
+    // stage pair; two workgroups per CU); else 128 columns three deep
+    if (d % 256 == 0) MOE_W2(256, 2);
+    else MOE_W2(128, 3);
+#undef MOE_W2
     return hipGetLastError();
 }
 

@@ -70,12 +70,12 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
                             int E, int n_shared, const uint8_t* mask, hipStream_t st);
 hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, const int32_t* tile_off,
                            const int32_t* meta, const void* w2, const uint8_t* w2s, const void* s2,
-                           const uint8_t* s2s, uint16_t* y, uint16_t* y_shared, int T, int d, int f, int fs, int k,
-                           int E, int n_shared, const uint8_t* mask, hipStream_t st);
+                           const uint8_t* s2s, void* y, void* y_shared, bool y_f32, int T, int d, int f, int fs,
+                           int k, int E, int n_shared, const uint8_t* mask, hipStream_t st);
 
 // MX prefill (MXFP4 weights on the scaled fp8 x fp4 matrix cores, activations quantised to MXFP8):
 // x -> codes [rows, d] + E8M0 scales [rows, d/32]; gate/up (+ SwiGLU, a quantised in the
-// epilogue into codes [P*f + T*fs] and scales [(P*f + T*fs)/32]); down projection to bf16.
+// epilogue into codes [P*f + T*fs] and scales [(P*f + T*fs)/32]); down projection to bf16 or f32.
 // x_dtype 0: f32 rows, 1: bf16 rows; K % 32 == 0
 hipError_t launch_mx_quant_rows(int x_dtype, const void* x, uint8_t* q, uint8_t* sc, int64_t rows, int64_t K,
                                 hipStream_t st);
@@ -84,8 +84,8 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
                              uint8_t* aqs, int T, int d, int f, int fs, int k, int E, int n_shared,
                              const uint8_t* mask, hipStream_t st);
 hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t* offsets, const void* w2,
-                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y, uint16_t* y_shared,
-                            int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
+                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* y, void* y_shared,
+                            bool y_f32, int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
                             hipStream_t st);
 
 // Decode path (T <= 32, T*E <= 8192): router logits, then the FFN kernels (the gate/up kernel

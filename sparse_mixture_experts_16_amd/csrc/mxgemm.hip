@@ -139,8 +139,8 @@ struct MxGemmArgs {
     const uint8_t* swsc;
     uint8_t* aq;             // W13 out: a codes, laid out as the W2 A operand
     uint8_t* aqs;            // W13 out: a scales
-    uint16_t* y;             // W2 out: y_sorted [P, d] bf16
-    uint16_t* y_sh;          // W2 out: y_shared [T, d] bf16
+    void* y;                 // W2 out: y_sorted [P, d] bf16 (f32 with YF32)
+    void* y_sh;              // W2 out: y_shared [T, d], the dtype of y
     int T, d, f, fs, k, E, n_shared;
     const uint8_t* mask;     // nullable [E + 1]: groups whose byte is 0 get no tiles
 };
@@ -163,7 +163,8 @@ __device__ __forceinline__ int btile_swz(int r) {
 // workgroups per CU; BM = 256: 512 threads, one per CU).  BK: K elements per stage (64: A rows of
 // 64 bytes, B rows of 32; 128: 128 and 64).  NS: ring depth.  SCB: scale bytes fetched per row at a
 // time (4 or 16; 16 needs K % 512 == 0).
-template <int MODE, int BM, int BN, int NS, int SCB, int BK>
+// YF32 (down projection only): y in fp32 straight from the accumulators.
+template <int MODE, int BM, int BN, int NS, int SCB, int BK, bool YF32 = false>
 __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
     constexpr int NWN = 2, THREADS = BM * 2;
     static_assert(BM == 128 || BM == 256, "tile rows");
@@ -437,6 +438,20 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
                 sbase[qr * (rowbytes / 32) + col0 / 32 + cb] = (uint8_t)sb;
             }
         }
+    } else if constexpr (YF32) {
+        // fp32 y from the accumulators: the 32 lanes holding one row write 128 contiguous bytes
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int r = wm * 64 + ms * 32 + (j >> 2) * 8 + hk * 4 + (j & 3);
+                if (r >= mrows) continue;
+                const int row = m0 + r;
+                float* o = (shared ? reinterpret_cast<float*>(p.y_sh) + (int64_t)row * p.d
+                                   : reinterpret_cast<float*>(p.y) + (int64_t)(base + row) * p.d) + nt * BN;
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns) o[wn * WN + ns * 32 + l32] = acc[ms][ns][j];
+            }
     } else {
         // bf16 outputs staged in LDS, then whole 16-byte row chunks stored
         uint16_t* o_st = reinterpret_cast<uint16_t*>(smem);
@@ -463,8 +478,9 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
                 if (r >= mrows) continue;
                 const int row = m0 + r;
                 const uint4 v = *reinterpret_cast<const uint4*>(&o_st[(i / CH) * OP + ch * 8]);
-                uint16_t* o =
-                    (shared ? p.y_sh + (int64_t)row * p.d : p.y + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+                uint16_t* o = (shared ? reinterpret_cast<uint16_t*>(p.y_sh) + (int64_t)row * p.d
+                                      : reinterpret_cast<uint16_t*>(p.y) + (int64_t)(base + row) * p.d) +
+                              col0 + ch * 8;
                 *reinterpret_cast<uint4*>(o) = v;
             }
         }
@@ -508,25 +524,26 @@ hipError_t launch_mxgemm_w13(const uint8_t* xq, const uint8_t* xs, const int32_t
 }
 
 hipError_t launch_mxgemm_w2(const uint8_t* aq, const uint8_t* aqs, const int32_t* offsets, const void* w2,
-                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, uint16_t* y, uint16_t* y_shared,
-                            int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
+                            const uint8_t* w2s, const void* s2, const uint8_t* s2s, void* y, void* y_shared,
+                            bool y_f32, int T, int d, int f, int fs, int k, int E, int n_shared, const uint8_t* mask,
                             hipStream_t st) {
     MxGemmArgs p{aq, aqs, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, nullptr,
                  y, y_shared, T, d, f, fs, k, E, n_shared, mask};
     const bool scb16 = f % 512 == 0 && (!n_shared || fs % 512 == 0);
-    if (d % 256 == 0) {
-        constexpr int BM = MX_BM;
-        const int nt = d / 256;
-        const unsigned grid = mx_grid8(mx_max_tiles(BM, T, k, E, n_shared, nt, nt));
-        if (scb16)
-            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 16, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BM, 256, MX_NS, 4, MX_BK>), dim3(grid), dim3(2 * BM), 0, st, p);
-    } else {
-        const int nt = d / 128;
-        const unsigned grid = mx_grid8(mx_max_tiles(128, T, k, E, n_shared, nt, nt));
-        if (scb16) MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 128, 3, 16, 64>), dim3(grid), dim3(256), 0, st, p);
-        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, 128, 128, 3, 4, 64>), dim3(grid), dim3(256), 0, st, p);
-    }
+#define MOE_MXW2(BMV, BNV, NSV, BKV)                                                                              \
+    do {                                                                                                          \
+        const unsigned grid = mx_grid8(mx_max_tiles(BMV, T, k, E, n_shared, d / BNV, d / BNV));                   \
+        if (scb16 && y_f32)                                                                                       \
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BMV, BNV, NSV, 16, BKV, true>), dim3(grid), dim3(2 * BMV), 0, st, p); \
+        else if (scb16)                                                                                           \
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BMV, BNV, NSV, 16, BKV>), dim3(grid), dim3(2 * BMV), 0, st, p); \
+        else if (y_f32)                                                                                           \
+            MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BMV, BNV, NSV, 4, BKV, true>), dim3(grid), dim3(2 * BMV), 0, st, p); \
+        else MOE_LAUNCH(PROF_FFN_DOWN, (mxgemm<MX_W2, BMV, BNV, NSV, 4, BKV>), dim3(grid), dim3(2 * BMV), 0, st, p); \
+    } while (0)
+    if (d % 256 == 0) MOE_MXW2(MX_BM, 256, MX_NS, MX_BK);
+    else MOE_MXW2(128, 128, 3, 64);
+#undef MOE_MXW2
     return hipGetLastError();
 }
 

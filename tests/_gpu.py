@@ -53,3 +53,44 @@ def margin_x(spec, layer: int = 0, tau_rel: float = 1e-3, b=None, max_rounds: in
         x[bad] = mi.host_x(spec, layer, attempts, rows=bad)
         _, l64[bad] = oracle.router_logits(spec, np.ascontiguousarray(x[bad]), wr, b)
     raise RuntimeError("could not draw margin-guaranteed tokens")
+
+
+def tile_boundary_tokens(idx: np.ndarray, E: int, T: int, n_shared: int, bm: int = 128) -> np.ndarray:
+    """Tokens whose rows sit at the first or last sorted position of every m-tile of every expert
+    (so every expert's first and last slot, and every ragged last tile, is among them), plus the
+    shared expert's tile edges and the first and last token."""
+    k = idx.shape[1]
+    order = np.argsort(idx.reshape(-1), kind="stable")  # sorted position -> pair
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    pos = []
+    for e in range(E):
+        for m0 in range(offs[e], offs[e + 1], bm):
+            pos += [m0, min(m0 + bm, offs[e + 1]) - 1]
+    toks = set((order[np.array(pos, np.int64)] // k).tolist()) if pos else set()
+    if n_shared:
+        for m0 in range(0, T, bm):
+            toks |= {m0, min(m0 + bm, T) - 1}
+    toks |= {0, T - 1}
+    return np.array(sorted(toks), np.int64)
+
+
+def oracle_on_tokens(s, x, wr, b, tokens, flags: int = 0):
+    """The oracle layer on the listed tokens (rows are independent), generating only the experts
+    those tokens select: route with all E experts, evaluate the selected experts compacted.
+    Returns the output and the compacted routing and weights it used."""
+    xs = np.ascontiguousarray(x[tokens])
+    l32s, _ = oracle.router_logits(s, xs, wr, b)
+    idx_s, g_s = oracle.topk(s, l32s)
+    need = sorted(set(idx_s.reshape(-1).tolist()))
+    w = mi.host_experts(s, experts=need)
+    sh = mi.host_experts(s, shared=True) if s.n_shared else None
+    remap = np.full(s.E, -1, np.int64)
+    remap[need] = np.arange(len(need))
+    idx_c = remap[idx_s].astype(np.int32)
+    sc = mi.LayerSpec(s.name, len(tokens), s.d, s.f, len(need), s.k, s.n_shared, s.f_shared, s.act, s.wt,
+                      s.sigma_x, s.sigma_w, s.sigma_r)
+    c, o, p, iv = oracle.permute(sc, idx_c)
+    ys, ysh = oracle.grouped_ffn(sc, xs, p, o, w, sh, flags=flags)
+    return dict(out=oracle.combine(sc, ys, iv, idx_c, g_s, ysh), spec=sc, xs=xs, idx=idx_s, idx_c=idx_c, g=g_s,
+                perm=p, offsets=o, inv=iv, w=w, sh=sh, need=need)

@@ -143,8 +143,14 @@ def test_other_entry_points_validate():
     assert L.moe_mx_down(ctypes.byref(_shape(weight_dtype=moe.MOE_MXFP4, d_model=256, d_ff=128, T=0)), None, None,
                          None, ctypes.byref(W4), None, None, None) == moe.MOE_OK
     arr = (ctypes.c_void_p * 1)(FAKE)
-    assert L.moe_stack_forward(ctypes.byref(s), -1, FAKE, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE + 8, arr, None, ctypes.byref(W), FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_forward(ctypes.byref(s), -1, FAKE, arr, None, ctypes.byref(W), None, FAKE, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE + 8, arr, None, ctypes.byref(W), None, FAKE, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE, arr, None, ctypes.byref(W), FAKE + 4, FAKE, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_forward(ctypes.byref(s), 1, FAKE, arr, None, ctypes.byref(W), None, FAKE, 1,
+                               None) == moe.MOE_ERR_WORKSPACE
     # the partial layer needs its expert mask, 16-byte aligned, and validates like the full layer
     masked = lambda s_, m, out=FAKE: L.moe_layer_forward_masked(ctypes.byref(s_), FAKE, FAKE, None, ctypes.byref(W), m,
                                                                out, None, FAKE, 1 << 40, None)

@@ -369,3 +369,28 @@ def test_decode_routing_signed_zero_inf_nan(T):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
     assert_close(host(res["out"]), ref["out"], what="specials")
+
+
+@pytest.mark.parametrize("s", [mi.spec("c1", T=4), mi.spec("c3", T=1),
+                               mi.LayerSpec("ws_gemm", 333, 256, 128, 16, 4, 1, 192, "bf16", "bf16", 1.0, 0.05, 0.05,
+                                            seed=21)], ids=lambda s: f"{s.name}_T{s.T}")
+def test_workspace_needs_no_initialisation(s):
+    """The same layer through a workspace full of 0xFF bytes and through a zeroed one: bit-equal
+    outputs and routing (no kernel reads a workspace region before writing it)."""
+    x, wr, b, _ = margin_x(s)
+    w, sh, wd, shd = _weights(s)
+    shape = moe.make_shape(s)
+    W = moe.make_weights(wd, shd)
+    n = moe.workspace_size(shape)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty((s.T, s.d), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+        moe.layer_forward_raw(shape, dev(x), dev(wr), dev(b), W, out, idx, ws)
+        torch.cuda.synchronize()
+        outs.append((out, idx))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ref = oracle.layer_forward(s, x, wr, b, w, sh)
+    np.testing.assert_array_equal(host(outs[1][1]), ref["topk_idx"])
+    assert_close(host(outs[1][0]), ref["out"], what=f"{s.name} T={s.T} through a 0xFF workspace")

@@ -1,11 +1,13 @@
 """GPU parity of the prefill path (grouped MFMA GEMM, MFMA router logits) against the oracle.
 
 Small shapes are compared element by element over every output (ragged last tiles, several
-m-tiles per expert, experts with no tokens).  The full-size prefill workloads (bf16 128-expert
-top-8 + shared at T=4096, uniform and Zipf-skewed; MXFP4 256-expert top-6 at T=8192) run in the
-same launch configuration as the bench: routing is checked bit for bit on every token, and the
-layer output on a sample of tokens that the oracle evaluates one by one (tokens are independent
-rows of the layer, so layer(x)[sample] = layer(x[sample])).
+m-tiles per expert, experts with no tokens, 128- and 256-column down tiles, 128 x 256 and
+128 x 512 gate/up tiles with and without a shared group).  The full-size prefill workloads run in
+the same launch configuration as the bench, routing checked bit for bit on every token: the bf16
+128-expert top-8 + shared layer at T=4096 (uniform and Zipf-skewed) on every output, the MXFP4
+256-expert top-6 layer at T=8192 on every token that sits at the first or last row of an m-tile
+of some expert (tokens are independent rows of the layer, so layer(x)[sample] = layer(x[sample])
+and the oracle evaluates the sample with only the experts it selects).
 """
 from __future__ import annotations
 
@@ -14,7 +16,7 @@ import pytest
 
 import moe_inputs as mi
 import oracle
-from _gpu import dev, host, margin_x
+from _gpu import dev, host, margin_x, oracle_on_tokens, tile_boundary_tokens
 from _helpers import assert_close
 
 torch = pytest.importorskip("torch")
@@ -27,6 +29,12 @@ SMALL = [
     mi.LayerSpec("g_bf16_noshared", 200, 512, 192, 24, 3, 0, 0, "bf16", "bf16", 1.0, 0.05, 0.05, seed=22),
     mi.LayerSpec("g_mxfp4", 257, 256, 128, 12, 2, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=23),
     mi.LayerSpec("g_mxfp4_shared", 64, 256, 128, 8, 8, 1, 128, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=24),
+    # d_model not a multiple of 256: the down projection's 128-column tiles
+    mi.LayerSpec("g_bf16_d192", 140, 192, 128, 8, 2, 1, 64, "bf16", "bf16", 1.0, 0.05, 0.05, seed=27),
+    mi.LayerSpec("g_bf16_d320", 97, 320, 192, 12, 3, 1, 128, "bf16", "bf16", 1.0, 0.05, 0.05, seed=28),
+    # MXFP4 with d_ff and shared d_ff multiples of 256: the 128 x 512 gate/up tiles, shared group included
+    mi.LayerSpec("g_mxfp4_f256_shared256", 150, 256, 256, 8, 2, 1, 256, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=29),
+    mi.LayerSpec("g_mxfp4_f256_shared512", 70, 384, 256, 10, 3, 1, 512, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=30),
 ]
 
 
@@ -82,7 +90,7 @@ def test_forced_gemm_and_gemv_agree_with_oracle(name, T):
         assert_close(host(res["out"]), ref["out"], what=f"{name} T={T} flag={flag}")
 
 
-def _full_size_case(name, T, n_sample=48, seed=0):
+def _full_size_case(name, T, all_tokens):
     s = mi.spec(name, T=T)
     x, wr, b, _ = margin_x(s)
     # GPU: weights generated in device memory; oracle: the same bytes generated on the host.
@@ -94,41 +102,27 @@ def _full_size_case(name, T, n_sample=48, seed=0):
     ref_idx, _ = oracle.topk(s, l32)
     np.testing.assert_array_equal(host(res["topk_idx"]), ref_idx)
     counts = np.bincount(ref_idx.reshape(-1), minlength=s.E)
-    rng = np.random.default_rng(seed)
-    sample = np.sort(rng.choice(s.T, size=n_sample, replace=False))
-    sample[0], sample[-1] = 0, s.T - 1  # first and last token (last m-tile tails)
-    xs = np.ascontiguousarray(x[sample])
-    need = sorted(set(ref_idx[sample].reshape(-1).tolist()))
-    w = mi.host_experts(s, experts=need)
-    remap = np.full(s.E, -1, np.int64)
-    remap[need] = np.arange(len(need))
-    # Oracle on the sampled tokens with the needed experts only: route with all E experts,
-    # then evaluate the selected experts from the compacted weight set.
-    sh = mi.host_experts(s, shared=True) if s.n_shared else None
-    l32s, _ = oracle.router_logits(s, xs, wr, b)
-    idx_s, g_s = oracle.topk(s, l32s)
-    idx_c = remap[idx_s].astype(np.int32)
-    sc = mi.LayerSpec(s.name, len(sample), s.d, s.f, len(need), s.k, s.n_shared, s.f_shared, s.act, s.wt,
-                      s.sigma_x, s.sigma_w, s.sigma_r)
-    c, o, p, iv = oracle.permute(sc, idx_c)
-    ys, ysh = oracle.grouped_ffn(sc, xs, p, o, w, sh)
-    ref = oracle.combine(sc, ys, iv, idx_c, g_s, ysh)
-    got = host(res["out"])[sample]
-    assert_close(got, ref, what=f"{name} sampled out")
+    tokens = np.arange(T) if all_tokens else tile_boundary_tokens(ref_idx, s.E, T, s.n_shared)
+    print(f"{name}: comparing {len(tokens)} of {T} tokens element by element", flush=True)
+    ref = oracle_on_tokens(s, x, wr, b, tokens)
+    assert_close(host(res["out"])[tokens], ref["out"], what=f"{name} out")
     return counts
 
 
 def test_prefill_c2_full_size():
-    counts = _full_size_case("c2", 4096)
+    """Every one of the 4096 tokens."""
+    counts = _full_size_case("c2", 4096, all_tokens=True)
     assert counts.sum() == 4096 * 8 and (counts > 0).all()
 
 
 def test_prefill_c2_skew_full_size():
-    counts = _full_size_case("c2_skew", 4096)
+    """Every one of the 4096 tokens."""
+    counts = _full_size_case("c2_skew", 4096, all_tokens=True)
     assert counts.sum() == 4096 * 8
     assert counts.max() > 4 * counts.mean()  # the Zipf prior concentrates the load
 
 
 def test_prefill_c3_full_size():
-    counts = _full_size_case("c3", 8192, n_sample=32)
+    """The tokens at the first and last row of every m-tile of every expert."""
+    counts = _full_size_case("c3", 8192, all_tokens=False)
     assert counts.sum() == 8192 * 6
