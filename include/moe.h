@@ -74,7 +74,8 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1,  /* NULL/misaligned pointer, k not in [1,E], negative sizes, ... */
     MOE_ERR_UNSUPPORTED = -2,  /* valid but not implemented: dtype pair, E > 1024, k > 64, ... */
     MOE_ERR_WORKSPACE = -3,    /* ws_bytes < moe_workspace_size(shape) */
-    MOE_ERR_HIP = -4           /* a HIP launch reported an error */
+    MOE_ERR_HIP = -4,          /* a HIP launch reported an error */
+    MOE_ERR_SCRATCH_LIMIT = -5 /* moe_layer_forward_noalloc: the shape needs more scratch than it holds */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_NVFP4 = 3 } moe_dtype;
@@ -188,6 +189,23 @@ int moe_combine(const moe_shape* shape, const void* y_sorted, const int32_t* inv
 int moe_layer_forward(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
                       const moe_weights* weights, void* out, int32_t* topk_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+   results, with the workspace taken from a scratch area the library holds in device memory
+   instead of from the caller.  The scratch area is MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU,
+   set up on the first call on each device (its address is looked up, nothing is allocated)
+   and kept until the process ends.  Shapes whose moe_workspace_size exceeds it (prefill
+   batches of more than a few hundred tokens at the benchmark shapes) return
+   MOE_ERR_SCRATCH_LIMIT with nothing enqueued; use moe_layer_forward with a caller workspace
+   for those.  No kernel needs the scratch area zeroed, and every call rewrites what it reads.
+   All calls on one GPU share its scratch area, so calls that overlap in time on one GPU (two
+   streams, two threads) race and must be serialised by the caller.  The call itself performs
+   no allocation (no hipMalloc, no hipFree, no allocating library routine).  Other arguments
+   and errors as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                              const moe_weights* weights, void* out, int32_t* topk_idx_out, void* stream);
 
 /* Partial layer (the exact merge of partial expert sums; FreeToken/dothoosh, "Architecture and
    the sparsity puzzle", mechanism 1: the GPU's and the CPU's partial results add up to the

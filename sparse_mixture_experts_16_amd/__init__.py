@@ -21,13 +21,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_F32, MOE_BF16, MOE_MXFP4, MOE_NVFP4 = 0, 1, 2, 3
 F_NO_RENORM, F_ACCUMULATE, F_FORCE_GEMV, F_FORCE_GEMM, F_MX_GEMM = 1 << 0, 1 << 1, 1 << 3, 1 << 4, 1 << 5
 MAX_EXPERTS, MAX_TOPK = 1024, 64
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4, "nvfp4": MOE_NVFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
-           "moe_combine", "moe_layer_forward", "moe_layer_forward_masked", "moe_stack_forward", "moe_mxfp4_dequant",
+           "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_masked",
+           "moe_stack_forward", "moe_mxfp4_dequant",
            "moe_nvfp4_dequant", "moe_mxfp8_quantize", "moe_mx_gate_up", "moe_mx_down",
            "moe_profile_kernel"]
 KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
@@ -59,6 +62,7 @@ _lib.moe_permute.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_grouped_ffn.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_combine.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_layer_forward_noalloc.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp]
 _lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _vp, _sz, _vp]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
@@ -179,6 +183,14 @@ def layer_forward_raw(shape: Shape, x, w_router, b_router, weights: Weights, out
     _check(_lib.moe_layer_forward(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
                                   ctypes.byref(weights), _ptr(out), _ptr(topk_idx_out), _ptr(ws), ws.numel(),
                                   _stream(stream)), "moe_layer_forward")
+
+
+def layer_forward_noalloc_raw(shape: Shape, x, w_router, b_router, weights: Weights, out, topk_idx_out=None,
+                              stream=None):
+    """moe_layer_forward_noalloc: the layer on the library's own per-GPU scratch area."""
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
+                                          ctypes.byref(weights), _ptr(out), _ptr(topk_idx_out), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def layer_forward_masked_raw(shape: Shape, x, w_router, b_router, weights: Weights, expert_mask, out,

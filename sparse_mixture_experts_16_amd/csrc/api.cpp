@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -268,6 +270,34 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
 
 }  // namespace
 
+// Scratch area of moe_layer_forward_noalloc: one per GPU (each device holds its own copy of this
+// array), looked up once per device; host code uses only the looked-up address.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The current device's scratch address, looked up on the first call on that device.
+hipError_t scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 namespace moe {
 void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop) {
     if (cls == g_prof_kernel) {
@@ -291,6 +321,7 @@ const char* moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_SCRATCH_LIMIT: return "shape needs more scratch than moe_layer_forward_noalloc holds (64 MiB)";
         default: return "unknown status";
     }
 }
@@ -415,9 +446,10 @@ int moe_combine(const moe_shape* s, const void* y_sorted, const int32_t* inv_per
     return MOE_OK;
 }
 
-static int layer_entry(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
-                       const moe_weights* w, const uint8_t* expert_mask, bool masked, void* out,
-                       int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of the layer calls (everything but the workspace).
+static int check_layer_args(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                            const moe_weights* w, const uint8_t* expert_mask, bool masked, void* out,
+                            int32_t* topk_idx_out) {
     int rc = check_shape(s);
     if (rc != MOE_OK) return rc;
     if (masked && !ptr_ok(expert_mask)) return MOE_ERR_INVALID_ARG;
@@ -425,6 +457,14 @@ static int layer_entry(const moe_shape* s, const void* x, const void* w_router, 
     if ((rc = check_weights(s, w)) != MOE_OK) return rc;
     if (!ptr_ok(x) || !ptr_ok(w_router) || !ptr_ok(out)) return MOE_ERR_INVALID_ARG;
     if ((b_router && !aligned16(b_router)) || (topk_idx_out && !aligned16(topk_idx_out))) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+static int layer_entry(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                       const moe_weights* w, const uint8_t* expert_mask, bool masked, void* out,
+                       int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+    const int rc = check_layer_args(s, x, w_router, b_router, w, expert_mask, masked, out, topk_idx_out);
+    if (rc != MOE_OK || s->T == 0) return rc;
     const Layout L = layout(s);
     if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     return run_layer(s, x, w_router, b_router, w, out, s->act_dtype, (s->flags & MOE_F_ACCUMULATE) != 0,
@@ -435,6 +475,17 @@ int moe_layer_forward(const moe_shape* s, const void* x, const void* w_router, c
                       const moe_weights* w, void* out, int32_t* topk_idx_out, void* ws, size_t ws_bytes,
                       void* stream) {
     return layer_entry(s, x, w_router, b_router, w, nullptr, false, out, topk_idx_out, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_noalloc(const moe_shape* s, const void* x, const void* w_router, const float* b_router,
+                              const moe_weights* w, void* out, int32_t* topk_idx_out, void* stream) {
+    const int rc = check_layer_args(s, x, w_router, b_router, w, nullptr, false, out, topk_idx_out);
+    if (rc != MOE_OK || s->T == 0) return rc;
+    if (layout(s).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (scratch_ptr(&ws) != hipSuccess) return MOE_ERR_HIP;
+    return layer_entry(s, x, w_router, b_router, w, nullptr, false, out, topk_idx_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                       stream);
 }
 
 int moe_layer_forward_masked(const moe_shape* s, const void* x, const void* w_router, const float* b_router,

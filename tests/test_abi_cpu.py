@@ -161,6 +161,20 @@ def test_other_entry_points_validate():
     assert masked(_shape(T=0), FAKE) == moe.MOE_OK
 
 
+def test_noalloc_validates_before_any_device_call():
+    L = moe.lib()
+    W = moe.Weights(w13=FAKE, w2=FAKE)
+    call = lambda s_, x=FAKE, out=FAKE: L.moe_layer_forward_noalloc(ctypes.byref(s_), x, FAKE, None, ctypes.byref(W),
+                                                                    out, None, None)
+    assert call(_shape(top_k=0)) == moe.MOE_ERR_INVALID_ARG
+    assert call(_shape(), x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(_shape(), out=FAKE + 2) == moe.MOE_ERR_INVALID_ARG
+    assert call(_shape(T=0), x=None, out=None) == moe.MOE_OK
+    big = _shape(T=4096, d_model=2048, d_ff=768, n_experts=128, top_k=8)
+    assert moe.workspace_size(big) > moe.NOALLOC_SCRATCH_BYTES
+    assert call(big) == moe.MOE_ERR_SCRATCH_LIMIT
+
+
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, 5):
+    for st in (0, -1, -2, -3, -4, -5, 5):
         assert isinstance(moe.lib().moe_status_string(st), bytes)
