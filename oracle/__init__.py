@@ -51,6 +51,7 @@ def lib():
         L.moe_ref_e4m3_to_f32.argtypes = [vp, i64, vp]
         L.moe_ref_nvfp4_dequant.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp]
         L.moe_ref_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp]
+        L.moe_ref_mx_dot.argtypes = [vp, vp, vp, vp, i64, vp]
         L.moe_ref_router_logits.argtypes = [sp, vp, vp, vp, vp, vp]
         L.moe_ref_topk.argtypes = [sp, vp, vp, vp]
         L.moe_ref_permute.argtypes = [sp, vp, vp, vp, vp, vp]
@@ -123,6 +124,18 @@ def mxfp8_quantize(v: np.ndarray):
     scales = np.empty((rows, K // 32), np.uint8)
     _rc(lib().moe_ref_mxfp8_quantize(_p(v), rows, K, _p(codes), _p(scales)), "mxfp8_quantize")
     return codes, scales
+
+
+def mx_dot(xc: np.ndarray, xs: np.ndarray, wc: np.ndarray, ws: np.ndarray) -> float:
+    """The MX path's dot product of one MXFP8 row (E4M3 codes [K], E8M0 scales [K/32]) and one
+    MXFP4 row (packed codes [K/2], E8M0 scales [K/32]) as the matrix core sums it."""
+    xc, xs = np.ascontiguousarray(xc, np.uint8), np.ascontiguousarray(xs, np.uint8)
+    wc, ws = np.ascontiguousarray(wc, np.uint8), np.ascontiguousarray(ws, np.uint8)
+    K = xc.size
+    assert wc.size * 2 == K and xs.size * 32 == K and ws.size * 32 == K
+    out = ctypes.c_double()
+    _rc(lib().moe_ref_mx_dot(_p(xc), _p(xs), _p(wc), _p(ws), K, ctypes.addressof(out)), "mx_dot")
+    return out.value
 
 
 def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
