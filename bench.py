@@ -2,9 +2,10 @@
 
 A step is one pass of the whole layer (router logits, top-k + gates, permute, grouped
 expert FFNs, combine; for the stack, 43 such layers with the RMS-norm residual glue)
-over one batch of synthetic tokens already resident in HBM.  The headline workload is
-the decode layer of the 128-expert top-8 + shared bf16 configuration at T=1; the other
-workloads run as a sweep and are reported beside it in the same JSON line.
+over one batch of synthetic tokens already resident in HBM.  The headline workload is the
+largest single-GPU configuration, the 43-layer MXFP4 stack of the 256-expert top-6 layer
+decoding one token (all 147 GB of expert weights resident); every other workload runs as a
+sweep entry with the same fields (roofline object, CPU baseline) in the same JSON line.
 
 Decode steps draw a fresh token batch from a pool of 256 batches and rotate through
 several copies of the layer's weights (like successive layers of a model), so the
@@ -13,7 +14,16 @@ several copies of the layer's weights (like successive layers of a model), so th
 Timing: hipEvents on the stream the library launches on (torch's current stream).
 Pass 1 times K steps end to end (value, ms_per_step).  Pass 2 repeats K steps with the
 library's timing hook bracketing the gate/up FFN kernel (the largest share of the
-layer's bytes and flops) to get that kernel's average duration for the roofline.
+layer's bytes and flops) to get that kernel's average duration for the roofline; pass 3
+does the same for the down projection.  The device's own peaks (an HBM read stream, the
+bf16 and fp8 x fp4 matrix instructions) are measured once and every fraction is also
+reported against them.
+
+The CPU baseline is the oracle as it stands (plain C, fp64 sums, OpenMP over output
+elements) on a bounded sample of each workload's tokens, timed on the host's cores; for
+the 43-layer stack it is three sampled layers (0, 21, 42), scaled by 43.  The oracle's
+single-threaded rates on the tiny, bf16 decode and MXFP4 decode layers come from child
+processes with one OpenMP thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-sweep]
 """
@@ -52,7 +62,10 @@ WORKLOADS = {
     "c3nv_decode_T8": ("c3nv", 8, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c4_stack": ("c4", 1, 1, "43-layer MXFP4 stack of the E=256 top-6 layer, T=1, RMS-norm residual"),
 }
-HEADLINE = "c1_decode_T1"
+# the tiny fp32 layer is a parity case, not a GPU workload; the oracle's single-threaded rate on it
+# is reported beside the others
+CPU_ONLY = {"c0_tiny_T16": ("c0", 16, 1, "tiny fp32 layer, E=8 top-2, d=256, f=128, T=16")}
+HEADLINE = "c4_stack"
 MX_WORKLOADS = {"c3_prefill_mx"}  # run with MOE_F_MX_GEMM
 POOL = 256
 
@@ -191,7 +204,10 @@ def _timed(hip, stream, step, steps, warmup, profile=None):
     moe.profile_kernel(-1)
     torch.cuda.synchronize()
     for a, b in evs:
-        kern.append(hip.elapsed_ms(a, b))
+        try:
+            kern.append(hip.elapsed_ms(a, b))
+        except RuntimeError:  # no launch of that kernel class in the step
+            hip.lib.hipGetLastError()  # clear the failed query's error
         hip.destroy(a)
         hip.destroy(b)
     return None, kern
@@ -241,7 +257,7 @@ def run_layer_workload(hip, name, steps, warmup):
     sh_up, sh_down = expert_bytes(s, s.f_shared) if s.n_shared else (0, 0)
     ms = total / steps
     rec = dict(workload=name, desc=desc, T=T, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
-               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3),
+               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3) if k_down else None,
                experts_hit_per_step=float(uniq.mean()),
                experts_never_hit=int((counts == 0).sum()), load_max_over_mean=float(counts.max() / counts.mean()))
     if decode:
@@ -321,7 +337,7 @@ def run_stack_workload(hip, steps, warmup):
     rec = dict(workload="c4_stack", desc=WORKLOADS["c4_stack"][3], T=1, ms_per_step=ms, tokens_per_s=1.0 / (ms * 1e-3),
                bound="hbm", alg_bytes_per_step=float(layer_bytes * s.n_layers),
                step_GBps=layer_bytes * s.n_layers / (ms * 1e-3) / 1e9,
-               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3))
+               ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3) if k_down else None)
     rec["step_frac_hbm"] = rec["step_GBps"] / HBM_PEAK_GBS
     # the hook's events bracket the last layer's launch of the step only
     rec["ffn_up_alg_bytes"] = float(s.k * up_b)
@@ -341,24 +357,201 @@ def _to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(seconds: float = 12.0):
-    """The oracle, as it stands, on the headline workload: C1 decode layer, one token at a time."""
+# ------------------------------------------------------------------------------------------------
+# Device peaks (libmoe_peaks.so)
+# ------------------------------------------------------------------------------------------------
+def measure_peaks(hip):
+    """The HBM read stream over a 4 GiB buffer (far beyond the 256 MB Infinity Cache), the same
+    stream cut into 80 MB reads (one decode layer's weights), and the bf16 and fp8 x fp4 matrix
+    instructions on register operands, each the best of a few launch shapes."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_16_amd", "libmoe_peaks.so"))
+    lib.peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    out = torch.empty(cus * 64 * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for r in range(reps):
+            fn(r)
+        hip.record(e1, stream)
+        ms = hip.elapsed_ms(e0, e1) / reps
+        hip.destroy(e0)
+        hip.destroy(e1)
+        return ms
+
+    res = {}
+    best = 0.0
+    for bpc in (4, 8, 16):
+        ms = timed(lambda r=0: lib.peak_hbm_read(buf.data_ptr(), nbytes, cus * bpc, out.data_ptr(), stream), 5)
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    res["hbm_read_GBps"] = best
+    win = 80 << 20  # one MXFP4 decode layer's active-expert bytes, read from a moving place
+    nwin = nbytes // win
+    best = 0.0
+    for bpc in (2, 4, 8):
+        ms = timed(lambda r=0: lib.peak_hbm_read(buf.data_ptr() + (r % nwin) * win, win, cus * bpc, out.data_ptr(),
+                                                 stream), 2 * nwin)
+        best = max(best, win / (ms * 1e-3) / 1e9)
+    res["hbm_read_80MB_GBps"] = best
+    nacc = 8
+    for kind, name, kdim in ((0, "bf16_TFLOPs", 16), (1, "fp8xfp4_TFLOPs", 64)):
+        best = 0.0
+        for wgs in (1, 2):
+            iters = 2000
+            ms = timed(lambda r=0: lib.peak_mfma(kind, cus * wgs, iters, out.data_ptr(), stream), 3)
+            flops = cus * wgs * 4 * iters * nacc * 2.0 * 32 * 32 * kdim
+            best = max(best, flops / (ms * 1e-3) / 1e12)
+        res[name] = best
+    del buf, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline(rec, peaks):
+    """The roofline object of one workload: its dominant kernel (the gate/up FFN kernel) against
+    the spec peak and the measured one, with the whole step's fraction beside it."""
+    mx = rec["workload"] in MX_WORKLOADS
+    if rec["bound"] == "hbm":
+        r = dict(bound="hbm", achieved=rec["ffn_up_GBps"], peak=HBM_PEAK_GBS, unit="GB/s", frac=rec["ffn_up_frac"],
+                 traffic=traffic_bytes(rec["workload"]), kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
+                 alg_bytes_per_launch=rec["ffn_up_alg_bytes"], avg_launch_us=rec["ffn_up_us"],
+                 step_frac=rec["step_frac_hbm"])
+        if peaks:
+            r["measured_peak"] = peaks["hbm_read_GBps"]
+            r["frac_of_measured_peak"] = rec["ffn_up_GBps"] / peaks["hbm_read_GBps"]
+            r["step_frac_of_measured_peak"] = rec["step_GBps"] / peaks["hbm_read_GBps"]
+    else:
+        peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+        r = dict(bound="mfma", achieved=rec["ffn_up_TFLOPs"], peak=peak, unit="TFLOP/s", frac=rec["ffn_up_frac"],
+                 traffic=traffic_bytes(rec["workload"]),
+                 kernel="FFN gate/up + SwiGLU (prefill grouped MFMA GEMM" + (", fp8 x fp4)" if mx else ", bf16)"),
+                 alg_flops_per_launch=rec["ffn_up_alg_flops"], avg_launch_us=rec["ffn_up_us"],
+                 step_frac=rec["step_frac_mfma"])
+        if peaks:
+            mp = peaks["fp8xfp4_TFLOPs" if mx else "bf16_TFLOPs"]
+            r["measured_peak"] = mp
+            r["frac_of_measured_peak"] = rec["ffn_up_TFLOPs"] / mp
+            r["step_frac_of_measured_peak"] = rec["step_TFLOPs"] / mp
+    return r
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on bounded samples of each workload
+# ------------------------------------------------------------------------------------------------
+_host_expert_cache = {}
+
+
+def _host_experts_cached(s, layer, experts):
+    """Host weights of the listed experts (generated once per (config, layer, expert))."""
+    import moe_inputs as mi
+    missing = [e for e in experts if (s.name, layer, e) not in _host_expert_cache]
+    if missing:
+        w = mi.host_experts(s, layer, experts=missing)
+        for i, e in enumerate(missing):
+            _host_expert_cache[(s.name, layer, e)] = {k: (v[i] if isinstance(v, np.ndarray) else v) for k, v in w.items()}
+    parts = [_host_expert_cache[(s.name, layer, e)] for e in experts]
+    return {k: (np.ascontiguousarray(np.stack([p[k] for p in parts])) if isinstance(parts[0][k], np.ndarray)
+                else parts[0][k]) for k in parts[0]}
+
+
+def _oracle_layer_run(s, x, wr, b, layer=0, flags=0, h=None):
+    """Prepare one oracle evaluation of the layer on the token rows x (or, with h, of the stack
+    layer on the residual rows h): the router over all E experts, the FFNs of the selected experts
+    (generated here, outside the timed call).  Returns the timed callable."""
     import moe_inputs as mi
     import oracle
-    s = mi.spec("c1", T=1)
+    xin = oracle.rmsnorm(h, dtype=s.act) if h is not None else x
+    l32, _ = oracle.router_logits(s, xin, wr, b)
+    idx, _ = oracle.topk(s, l32)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    w = _host_experts_cached(s, layer, need)
+    sh = mi.host_experts(s, layer, shared=True) if s.n_shared else None
+    remap = np.full(s.E, -1, np.int64)
+    remap[need] = np.arange(len(need))
+
+    def run():
+        xr = oracle.rmsnorm(h, dtype=s.act) if h is not None else x
+        l32r, _ = oracle.router_logits(s, xr, wr, b)
+        ir, g = oracle.topk(s, l32r)
+        ic = remap[ir].astype(np.int32)
+        sc = mi.LayerSpec(s.name, xr.shape[0], s.d, s.f, len(need), s.k, s.n_shared, s.f_shared, s.act, s.wt,
+                          s.sigma_x, s.sigma_w, s.sigma_r)
+        _, o, p, iv = oracle.permute(sc, ic)
+        ys, ysh = oracle.grouped_ffn(sc, xr, p, o, w, sh, flags=flags)
+        return oracle.combine(sc, ys, iv, ic, g, ysh)
+    return run
+
+
+def cpu_baseline(name: str, seconds: float):
+    """tokens/s of the oracle on a bounded sample of workload `name`: the sample's token batches
+    are drawn like the benchmark's (decode: the pool's batches in turn; prefill: single tokens of
+    the batch, whose rows are independent); each batch's selected experts are generated before its
+    timed call."""
+    import moe_inputs as mi
+    import oracle
+    cfg, T, _, desc = WORKLOADS[name] if name in WORKLOADS else CPU_ONLY[name]
+    mx = name in MX_WORKLOADS
+    flags = oracle.MX_GEMM if mx else 0
+    if cfg == "c4":
+        s = mi.spec("c4")
+        h0 = mi.host_h0(mi.spec("c4", T=1))
+        per_layer = []
+        for layer in (0, 21, 42):
+            wr, b = mi.host_router(s, layer)
+            run = _oracle_layer_run(s, None, wr, b, layer=layer, h=h0)
+            t0 = time.perf_counter()
+            n = 0
+            while n < 1 or time.perf_counter() - t0 < seconds / 3:
+                run()
+                n += 1
+            per_layer.append((time.perf_counter() - t0) / n)
+        step = float(np.mean(per_layer)) * s.n_layers
+        return dict(value=1.0 / step, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                    sample=f"one token through layers 0, 21 and 42 of the stack ({', '.join(f'{t * 1e3:.0f}' for t in per_layer)} "
+                           f"ms each, the six selected experts of each generated beforehand), mean x 43 layers: extrapolated")
+    s = mi.spec(cfg, T=T)
     wr, b = mi.host_router(s)
-    w = mi.host_experts(s)
-    sh = mi.host_experts(s, shared=True)
-    xs = mi.host_x(mi.spec("c1", T=POOL))
-    n = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        oracle.layer_forward(s, np.ascontiguousarray(xs[n % POOL:n % POOL + 1]), wr, b, w, sh)
-        n += 1
-    dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} single-token decode layers of the bf16 E=128 top-8 + shared layer (d=2048, f=768), "
-                       f"{dt:.1f} s of fp64 CPU work")
+    decode = T <= 32
+    rows = T if decode else 1
+    xs = mi.host_x(mi.spec(cfg, T=max(64, rows * 4)))
+    done = tokens = 0
+    busy = 0.0
+    t_wall = time.perf_counter()
+    while (done < 1 or busy < seconds) and time.perf_counter() - t_wall < 4 * seconds:
+        x = np.ascontiguousarray(xs[(done * rows) % len(xs):(done * rows) % len(xs) + rows])
+        run = _oracle_layer_run(s, x, wr, b, flags=flags)
+        t0 = time.perf_counter()
+        run()
+        busy += time.perf_counter() - t0
+        done += 1
+        tokens += rows
+    what = f"{done} batches of {rows} token(s)" if decode else f"{done} single tokens of the T={T} batch"
+    return dict(value=tokens / busy, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{what}: {desc}; {busy:.1f} s of timed fp64 CPU work (expert weights generated beforehand)")
+
+
+def cpu_single_thread(names, seconds):
+    """The oracle's single-threaded rates, each in a child process with OMP_NUM_THREADS=1."""
+    import subprocess
+    out = {}
+    for n in names:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-only", n, "--cpu-seconds", str(seconds)],
+                           capture_output=True, text=True, env=env, timeout=600)
+        try:
+            out[n] = json.loads(r.stdout.strip().splitlines()[-1])
+        except Exception:  # keep the line printable
+            out[n] = {"error": (r.stderr or r.stdout)[-300:]}
+    return out
 
 
 def main():
@@ -369,10 +562,16 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--sweep-list", default="")
+    ap.add_argument("--cpu-only", default="", help="print only the oracle's rate on this workload (no GPU)")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 256 MiB device copy (reference for the traffic counters)")
     args = ap.parse_args()
+    if args.cpu_only:
+        print(json.dumps(cpu_baseline(args.cpu_only, args.cpu_seconds)))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(the layer's multi-GPU sharding is a design note, not built)"}))
@@ -384,12 +583,17 @@ def main():
     import sparse_mixture_experts_16_amd  # noqa: F401  (fails loudly without the HIP library)
     hip = Hip()
     torch.cuda.init()
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] device peaks ...", file=sys.stderr, flush=True)
+        peaks = measure_peaks(hip)
 
     def run(name, steps, warmup):
         print(f"[bench] {name} ...", file=sys.stderr, flush=True)
-        if name == "c4_stack":
-            return run_stack_workload(hip, steps, warmup)
-        return run_layer_workload(hip, name, steps, warmup)
+        rec = run_stack_workload(hip, steps, warmup) if name == "c4_stack" else run_layer_workload(hip, name, steps,
+                                                                                                   warmup)
+        rec["roofline"] = roofline(rec, peaks)
+        return rec
 
     head = run(args.workload, args.steps, args.warmup)
     sweep = {}
@@ -401,16 +605,14 @@ def main():
             except Exception as exc:  # keep the line printable; the failure is reported in it
                 sweep[n] = {"error": repr(exc)}
                 print(f"[bench] {n} failed: {exc!r}", file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu else cpu_baseline()
-    if head["bound"] == "hbm":
-        roof = dict(bound="hbm", achieved=head["ffn_up_GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
-                    alg_bytes_per_launch=head["ffn_up_alg_bytes"], avg_launch_us=head["ffn_up_us"])
-    else:
-        roof = dict(bound="mfma", achieved=head["ffn_up_TFLOPs"],
-                    peak=FP8_PEAK_TFLOPS if head["workload"] in MX_WORKLOADS else BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=head["ffn_up_frac"], traffic=traffic_bytes(head["workload"]), kernel="FFN gate/up + SwiGLU (prefill grouped MFMA GEMM)",
-                    alg_flops_per_launch=head["ffn_up_alg_flops"], avg_launch_us=head["ffn_up_us"])
+    cpu = cpu_single = None
+    if not args.no_cpu:
+        print("[bench] oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(head["workload"], 12.0)
+        for n, rec in sweep.items():
+            if "error" not in rec:
+                rec["cpu_baseline"] = cpu_baseline(n, 2.0)
+        cpu_single = cpu_single_thread(["c0_tiny_T16", "c1_decode_T1", "c3_decode_T1"], 3.0)
     line = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA util %",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -419,7 +621,9 @@ def main():
         "config": {"workload": head["desc"], "name": head["workload"], "T": head["T"],
                    **{key: head[key] for key in ("experts_hit_per_step", "step_GBps", "step_frac_hbm",
                                                  "step_TFLOPs", "step_frac_mfma") if key in head}},
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": head["roofline"], "cpu_baseline": cpu,
+        "cpu_single_thread": cpu_single,
+        "measured_peaks": peaks,
         "kernels_us": {key: head[key] for key in ("ffn_up_us", "ffn_down_us") if key in head},
         "sweep": sweep,
     }

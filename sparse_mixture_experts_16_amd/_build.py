@@ -30,16 +30,25 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+PEAKS_SRC = "peaks.hip"
+PEAKS_LIB = os.path.join(HERE, "libmoe_peaks.so")
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    os.replace(tmp, lib)
+    print(f"built {lib}", flush=True)
+
+
 def build(extra_flags=()) -> str:
+    """libmoe.so (the layer) and libmoe_peaks.so (the benchmark's device peak probes)."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra_flags)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    print(f"built {LIB}", flush=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + [PEAKS_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     return LIB
 
 

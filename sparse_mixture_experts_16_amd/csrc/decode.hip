@@ -64,7 +64,7 @@ struct DecLogitsArgs {
     int T, d, E, prenorm;
 };
 
-// One wavefront per (router row, token): grid = (E/4, T).  Every load of a pass (up to 8
+// One wavefront per (router row, token): grid = (E, T) of one-wavefront workgroups.  Every load of a pass (up to 8
 // 16-byte chunks of the row and of the token per lane) is issued before any arithmetic, so a
 // wavefront waits for one round trip per pass.  With the residual stack (prenorm) each
 // wavefront first takes its token's RMS from h (fp32) and reads x = bf16(h * inv_rms), the value
@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256) dec_logits(DecLogitsArgs p) {
     const int t = blockIdx.y, d = p.d, NC = d / V;
     const float* h = reinterpret_cast<const float*>(p.x) + (int64_t)t * d;
     float inv = 1.0f;
-    const int e = blockIdx.x * 4 + wv;
+    const int e = blockIdx.x * (blockDim.x / MOE_WAVE) + wv;
     if (p.prenorm && NC <= MOE_WAVE * NB) {
         // The wavefront's lanes hold the whole row of h between them: its chunks give the RMS
         // (one wave-wide sum) and then x, from a single round trip together with W_r's row.
@@ -776,7 +776,9 @@ bool dec_supported(int T, int E, int k) {
 hipError_t launch_dec_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits, void* xn,
                              int T, int d, int E, bool prenorm, hipStream_t st) {
     DecLogitsArgs p{x, wr, b, logits, xn, T, d, E, prenorm ? 1 : 0};
-    const dim3 grid((E + 3) / 4, T), block(256);
+    // one wavefront per workgroup: the router rows spread over up to E compute units instead of
+    // E / 4 (each wavefront's loads all go out at once; fewer per CU means less queueing)
+    const dim3 grid(E, T), block(MOE_WAVE);
     if (act_dtype == 0) hipLaunchKernelGGL((dec_logits<float>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((dec_logits<uint16_t>), grid, block, 0, st, p);
     return hipGetLastError();
