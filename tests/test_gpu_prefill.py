@@ -105,7 +105,12 @@ def _full_size_case(name, T, all_tokens):
     tokens = np.arange(T) if all_tokens else tile_boundary_tokens(ref_idx, s.E, T, s.n_shared)
     print(f"{name}: comparing {len(tokens)} of {T} tokens element by element", flush=True)
     ref = oracle_on_tokens(s, x, wr, b, tokens)
-    assert_close(host(res["out"])[tokens], ref["out"], what=f"{name} out")
+    got, want = host(res["out"])[tokens], ref["out"]
+    rms = float(np.sqrt(np.mean(want * want)))
+    ratio = np.abs(got - want) / (1e-2 * rms + 2e-2 * np.abs(want))
+    print(f"{name}: largest error / bound {ratio.max():.3f}; {int((ratio > 0.5).sum())} elements above half the bound",
+          flush=True)
+    assert_close(got, want, what=f"{name} out")
     return counts
 
 
