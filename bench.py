@@ -61,6 +61,8 @@ WORKLOADS = {
     "c3nv_decode_T1": ("c3nv", 1, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=1"),
     "c3nv_decode_T8": ("c3nv", 8, 4, "decode, NVFP4 weights, E=256 top-6, d=4096, f=2048, T=8"),
     "c4_stack": ("c4", 1, 1, "43-layer MXFP4 stack of the E=256 top-6 layer, T=1, RMS-norm residual"),
+    "c4_stack_persistent": ("c4", 1, 1, "43-layer MXFP4 stack of the E=256 top-6 layer, T=1, RMS-norm residual, "
+                                        "one persistent cooperative launch (grid barriers between the steps)"),
 }
 # the tiny fp32 layer is a parity case, not a GPU workload; the oracle's single-threaded rate on it
 # is reported beside the others
@@ -289,7 +291,7 @@ def run_layer_workload(hip, name, steps, warmup):
     return rec
 
 
-def run_stack_workload(hip, steps, warmup):
+def run_stack_workload(hip, steps, warmup, persistent=False):
     import torch
     import moe_inputs as mi
     import sparse_mixture_experts_16_amd as moe
@@ -312,6 +314,9 @@ def run_stack_workload(hip, steps, warmup):
     def step(i):
         h.copy_(h0[i % POOL].view(1, -1))
         moe.stack_forward(shape, h, wrs, bs, Ws, ws)
+
+    if persistent:
+        return _run_stack_persistent(hip, steps, warmup, s, shape, h, h0, wrs, bs, Ws, keep, stream)
 
     # timed as replays of one captured graph of the 43 layers; the fresh token is copied in
     # before each replay (inside the timed region)
@@ -344,6 +349,38 @@ def run_stack_workload(hip, steps, warmup):
     rec["ffn_up_GBps"] = s.k * up_b / (np.mean(k_up) * 1e-3) / 1e9
     rec["ffn_up_frac"] = rec["ffn_up_GBps"] / HBM_PEAK_GBS
     del keep, Ws, wrs, bs, ws
+    moe._ws_cache.clear()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def _run_stack_persistent(hip, steps, warmup, s, shape, h, h0, wrs, bs, Ws, keep, stream):
+    """The same stack as one cooperative launch per token (moe_stack_forward_persistent), launched
+    eagerly; the fresh token is copied in before each launch (inside the timed region)."""
+    import torch
+    import sparse_mixture_experts_16_amd as moe
+    pws = torch.empty(moe.stack_persistent_workspace_size(shape, s.n_layers), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        h.copy_(h0[i % POOL].view(1, -1))
+        moe.stack_forward_persistent(shape, h, wrs, bs, Ws, pws)
+
+    total, _ = _timed(hip, stream, step, steps, warmup)
+    if moe.stack_persistent_status(pws) != 0:
+        raise RuntimeError("persistent stack: a grid-barrier wait ran out")
+    ms = total / steps
+    up_b, down_b = expert_bytes(s)
+    layer_bytes = s.k * (up_b + down_b)
+    step_bytes = float(layer_bytes * s.n_layers)
+    rec = dict(workload="c4_stack_persistent", desc=WORKLOADS["c4_stack_persistent"][3], T=1, ms_per_step=ms,
+               tokens_per_s=1.0 / (ms * 1e-3), bound="hbm", alg_bytes_per_step=step_bytes,
+               step_GBps=step_bytes / (ms * 1e-3) / 1e9)
+    rec["step_frac_hbm"] = rec["step_GBps"] / HBM_PEAK_GBS
+    # one kernel does the whole step: its roofline is the step's (the launch also holds the
+    # barrier-word clear and the token copy)
+    rec.update(ffn_up_alg_bytes=step_bytes, ffn_up_us=ms * 1e3, ffn_up_GBps=rec["step_GBps"],
+               ffn_up_frac=rec["step_frac_hbm"], roof_kernel="dec_stack (the whole 43-layer step, one launch)")
+    del keep, Ws, wrs, bs, pws
     moe._ws_cache.clear()
     torch.cuda.empty_cache()
     return rec
@@ -422,7 +459,8 @@ def roofline(rec, peaks):
     mx = rec["workload"] in MX_WORKLOADS
     if rec["bound"] == "hbm":
         r = dict(bound="hbm", achieved=rec["ffn_up_GBps"], peak=HBM_PEAK_GBS, unit="GB/s", frac=rec["ffn_up_frac"],
-                 traffic=traffic_bytes(rec["workload"]), kernel="FFN gate/up + SwiGLU (decode grouped GEMV)",
+                 traffic=traffic_bytes(rec["workload"]),
+                 kernel=rec.get("roof_kernel", "FFN gate/up + SwiGLU (decode grouped GEMV)"),
                  alg_bytes_per_launch=rec["ffn_up_alg_bytes"], avg_launch_us=rec["ffn_up_us"],
                  step_frac=rec["step_frac_hbm"])
         if peaks:
@@ -590,8 +628,10 @@ def main():
 
     def run(name, steps, warmup):
         print(f"[bench] {name} ...", file=sys.stderr, flush=True)
-        rec = run_stack_workload(hip, steps, warmup) if name == "c4_stack" else run_layer_workload(hip, name, steps,
-                                                                                                   warmup)
+        if name in ("c4_stack", "c4_stack_persistent"):
+            rec = run_stack_workload(hip, steps, warmup, persistent=name == "c4_stack_persistent")
+        else:
+            rec = run_layer_workload(hip, name, steps, warmup)
         rec["roofline"] = roofline(rec, peaks)
         return rec
 

@@ -231,6 +231,29 @@ int moe_stack_forward(const moe_shape* shape, int32_t n_layers, float* h, const 
                       const float* const* b_router, const moe_weights* weights, int32_t* topk_idx_out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* moe_stack_forward for one token as ONE persistent launch per 48 layers (the 43-layer decode
+   of DeepSeek-V4-Flash, 6 of 256 experts per layer; dothoosh.com FreeToken article, "FreeToken
+   architecture and the sparsity puzzle"): the same three steps per layer and the same results
+   bit for bit, with grid-wide barriers between them instead of kernel boundaries.  Supported:
+   T = 1, bf16 activations, MXFP4 weights, no shared expert, d_model <= 4096 and d_ff <= 2048
+   (multiples of 32); else MOE_ERR_UNSUPPORTED with nothing enqueued.  The launch is cooperative
+   (all workgroups resident); a barrier wait that runs out of polls (moe_stack_persistent_set_spin_limit,
+   default 2^20, about a second) makes every workgroup leave, the call's results are then
+   undefined and moe_stack_persistent_status reports 1.  ws: at least
+   moe_stack_persistent_workspace_size(shape, n_layers) bytes (0 = unsupported shape), no
+   initialisation needed.  Other arguments and errors as moe_stack_forward. */
+size_t moe_stack_persistent_workspace_size(const moe_shape* shape, int32_t n_layers);
+int moe_stack_forward_persistent(const moe_shape* shape, int32_t n_layers, float* h, const void* const* w_router,
+                                 const float* const* b_router, const moe_weights* weights, int32_t* topk_idx_out,
+                                 void* ws, size_t ws_bytes, void* stream);
+/* Synchronises `stream`, then *status = 0 (the last moe_stack_forward_persistent on ws ran to
+   the end) or 1 (a barrier wait ran out).  INVALID_ARG for a NULL or misaligned ws or NULL
+   status; HIP for a failed copy. */
+int moe_stack_persistent_status(const void* ws, int32_t* status, void* stream);
+/* Polls of one barrier wait before moe_stack_forward_persistent gives up (>= 0; 0 gives up at
+   the first wait that has to poll).  Process-wide; for tests of the time-out path. */
+int moe_stack_persistent_set_spin_limit(int32_t spins);
+
 /* MXFP4 -> f32 dequantisation on its own: out[r*K + j] =
    (-1)^b3 * M[code & 7] * 2^(s - 127) with M = {0, .5, 1, 1.5, 2, 3, 4, 6},
    NaN for s = 0xFF; codes [rows, K/2], scales [rows, K/32]; K % 32 == 0. */

@@ -30,7 +30,8 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4, "nvfp4": MOE_NVFP4}
 
 EXPORTS = ["moe_workspace_size", "moe_status_string", "moe_route", "moe_permute", "moe_grouped_ffn",
            "moe_combine", "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_masked",
-           "moe_stack_forward", "moe_mxfp4_dequant",
+           "moe_stack_forward", "moe_stack_persistent_workspace_size", "moe_stack_forward_persistent",
+           "moe_stack_persistent_status", "moe_stack_persistent_set_spin_limit", "moe_mxfp4_dequant",
            "moe_nvfp4_dequant", "moe_mxfp8_quantize", "moe_mx_gate_up", "moe_mx_down",
            "moe_profile_kernel"]
 KERNEL_FFN_UP, KERNEL_FFN_DOWN = 0, 1
@@ -65,6 +66,11 @@ _lib.moe_layer_forward.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _sz, 
 _lib.moe_layer_forward_noalloc.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp]
 _lib.moe_layer_forward_masked.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_stack_forward.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _vp, _sz, _vp]
+_lib.moe_stack_persistent_workspace_size.argtypes = [_SP, _i32]
+_lib.moe_stack_forward_persistent.argtypes = [_SP, _i32, _vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _WP, _vp, _vp,
+                                              _sz, _vp]
+_lib.moe_stack_persistent_status.argtypes = [_vp, ctypes.POINTER(_i32), _vp]
+_lib.moe_stack_persistent_set_spin_limit.argtypes = [_i32]
 _lib.moe_mxfp4_dequant.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
 _lib.moe_nvfp4_dequant.argtypes = [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _vp]
 _lib.moe_mxfp8_quantize.argtypes = [_vp, _i32, _i64, _i64, _vp, _vp, _vp]
@@ -73,6 +79,7 @@ _lib.moe_mx_down.argtypes = [_SP, _vp, _vp, _vp, _WP, _vp, _vp, _vp]
 _lib.moe_profile_kernel.argtypes = [ctypes.c_int, _vp, _vp]
 for _n in EXPORTS[2:]:
     getattr(_lib, _n).restype = ctypes.c_int
+_lib.moe_stack_persistent_workspace_size.restype = _sz
 
 
 class MoeError(RuntimeError):
@@ -211,6 +218,34 @@ def stack_forward(shape: Shape, h, w_routers, b_routers, weights_list, ws=None, 
     W = (Weights * n)(*weights_list)
     _check(_lib.moe_stack_forward(ctypes.byref(shape), n, _ptr(h), wr, br, W, _ptr(topk_idx_out), _ptr(ws),
                                   ws.numel(), _stream(stream)), "moe_stack_forward")
+
+
+def stack_persistent_workspace_size(shape: Shape, n_layers: int) -> int:
+    """Bytes of workspace moe_stack_forward_persistent needs (0: shape not supported)."""
+    return int(_lib.moe_stack_persistent_workspace_size(ctypes.byref(shape), n_layers))
+
+
+def stack_forward_persistent(shape: Shape, h, w_routers, b_routers, weights_list, ws, stream=None, topk_idx_out=None):
+    """moe_stack_forward_persistent (one token, the whole stack in one cooperative launch per 48 layers);
+    ws: a device uint8 tensor of at least stack_persistent_workspace_size bytes."""
+    n = len(weights_list)
+    wr = (_vp * n)(*[_ptr(t) for t in w_routers])
+    br = (_vp * n)(*[_ptr(t) for t in b_routers]) if b_routers is not None else None
+    W = (Weights * n)(*weights_list)
+    _check(_lib.moe_stack_forward_persistent(ctypes.byref(shape), n, _ptr(h), wr, br, W, _ptr(topk_idx_out),
+                                             _ptr(ws), ws.numel(), _stream(stream)), "moe_stack_forward_persistent")
+
+
+def stack_persistent_status(ws, stream=None) -> int:
+    """Synchronises the stream; 0, or 1 if a grid-barrier wait of the last call ran out."""
+    v = _i32(0)
+    _check(_lib.moe_stack_persistent_status(_ptr(ws), ctypes.byref(v), _stream(stream)), "moe_stack_persistent_status")
+    return int(v.value)
+
+
+def stack_persistent_set_spin_limit(spins: int):
+    """Polls of a grid-barrier wait before it gives up (default 1 << 20)."""
+    _check(_lib.moe_stack_persistent_set_spin_limit(spins), "moe_stack_persistent_set_spin_limit")
 
 
 def mxfp4_dequant(codes, scales, out, stream=None):

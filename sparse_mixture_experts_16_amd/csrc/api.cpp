@@ -298,6 +298,50 @@ hipError_t scratch_ptr(void** out) {
 }
 }  // namespace
 
+namespace {
+// Workspace of moe_stack_forward_persistent: the barrier words, then one region per layer of a
+// launch for its logits, x, a and (between layers) h, each region 256-byte aligned.
+struct StackLayout {
+    size_t bar, logits, xn, a, hbuf, total;
+    int64_t sh_lg, sh_xn, sh_a, sh_h;  // elements per region
+    int lc;                             // layers per launch
+};
+
+StackLayout stack_layout(const moe_shape* s, int n_layers) {
+    StackLayout L{};
+    const size_t d = (size_t)s->d_model, f = (size_t)s->d_ff, E = (size_t)s->n_experts, k = (size_t)s->top_k;
+    L.lc = n_layers < STACK_LAYERS_PER_LAUNCH ? n_layers : STACK_LAYERS_PER_LAUNCH;
+    const size_t lc = L.lc < 1 ? 1 : (size_t)L.lc;
+    // h between layers: one 128-byte line per 8-row block
+    const size_t lg_b = up(E * 4), xn_b = up(d * 2), a_b = up(k * f * 4), h_b = up((d + 7) / 8 * 128);
+    L.sh_lg = (int64_t)(lg_b / 4);
+    L.sh_xn = (int64_t)(xn_b / 2);
+    L.sh_a = (int64_t)(a_b / 4);
+    L.sh_h = (int64_t)(h_b / 4);
+    size_t o = 0;
+    L.bar = o; o = up(o + (size_t)dec_stack_bar_ints() * 4);
+    L.logits = o; o += lc * lg_b;
+    L.xn = o; o += lc * xn_b;
+    L.a = o; o += lc * a_b;
+    L.hbuf = o; o += (lc - 1) * h_b;
+    L.total = up(o);
+    return L;
+}
+
+int g_stack_spin_limit = 1 << 20;
+
+// The shapes whose decode stack runs as dec_logits (single pass), dec_w13 and dec_w2c1 with
+// MXFP4 weights, one token and no shared expert.
+int check_stack_persistent(const moe_shape* s) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (s->T != 1 || s->act_dtype != MOE_BF16 || s->weight_dtype != MOE_MXFP4 || s->n_shared != 0 || !use_decode(s) ||
+        !dec_stack_supported(s->d_model, s->d_ff, s->n_experts, s->top_k))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+}  // namespace
+
 namespace moe {
 void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop) {
     if (cls == g_prof_kernel) {
@@ -531,6 +575,64 @@ int moe_stack_forward(const moe_shape* s, int32_t n_layers, float* h, const void
                        layer_idx(topk_idx_out, l, s), ws, L, nullptr, st);
         if (rc != MOE_OK) return rc;
     }
+    return MOE_OK;
+}
+
+
+size_t moe_stack_persistent_workspace_size(const moe_shape* s, int32_t n_layers) {
+    if (n_layers < 1 || check_stack_persistent(s) != MOE_OK) return 0;
+    return stack_layout(s, n_layers).total;
+}
+
+int moe_stack_forward_persistent(const moe_shape* s, int32_t n_layers, float* h, const void* const* w_router,
+                                 const float* const* b_router, const moe_weights* w, int32_t* topk_idx_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != MOE_OK) return rc;
+    if (n_layers < 0 || !w_router || !w) return MOE_ERR_INVALID_ARG;
+    if (s->T == 0 || n_layers == 0) return MOE_OK;
+    if ((rc = check_stack_persistent(s)) != MOE_OK) return rc;
+    if (!ptr_ok(h) || (topk_idx_out && !aligned16(topk_idx_out))) return MOE_ERR_INVALID_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((rc = check_weights(s, &w[l])) != MOE_OK) return rc;
+        if (!ptr_ok(w_router[l])) return MOE_ERR_INVALID_ARG;
+        if (b_router && b_router[l] && !aligned16(b_router[l])) return MOE_ERR_INVALID_ARG;
+    }
+    const StackLayout L = stack_layout(s, n_layers);
+    if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    StackLayerPtrs lp[STACK_LAYERS_PER_LAUNCH];
+    for (int l0 = 0; l0 < n_layers; l0 += L.lc) {
+        const int n = n_layers - l0 < L.lc ? n_layers - l0 : L.lc;
+        for (int j = 0; j < n; ++j) {
+            const moe_weights& wl = w[l0 + j];
+            lp[j] = StackLayerPtrs{w_router[l0 + j], b_router ? b_router[l0 + j] : nullptr, wl.w13, wl.w13_scale, wl.w2,
+                                   wl.w2_scale};
+        }
+        const hipError_t e = launch_dec_stack(
+            lp, n, h, at<float>(ws, L.hbuf), at<float>(ws, L.logits), at<uint16_t>(ws, L.xn), at<float>(ws, L.a),
+            topk_idx_out ? topk_idx_out + (int64_t)l0 * s->top_k : nullptr, at<int>(ws, L.bar), L.sh_h, L.sh_lg,
+            L.sh_xn, L.sh_a, s->d_model, s->d_ff, s->n_experts, s->top_k, (s->flags & MOE_F_NO_RENORM) != 0,
+            g_stack_spin_limit, l0 == 0, st);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+int moe_stack_persistent_status(const void* ws, int32_t* status, void* stream) {
+    if (!ws || !aligned16(ws) || !status) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t v = 0;
+    const char* p = reinterpret_cast<const char*>(ws) + (size_t)dec_stack_err_index() * 4;
+    if (hipMemcpyAsync(&v, p, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+    *status = v;
+    return MOE_OK;
+}
+
+int moe_stack_persistent_set_spin_limit(int32_t spins) {
+    if (spins < 0) return MOE_ERR_INVALID_ARG;
+    g_stack_spin_limit = spins;
     return MOE_OK;
 }
 

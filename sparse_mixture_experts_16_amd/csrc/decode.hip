@@ -280,14 +280,16 @@ __device__ __forceinline__ int dec_slot_scan(DecRoute& R, const int* s_cnt, cons
 }
 
 // `mid` runs once the logits are in LDS, before the top-k (the rest of the routing issues no
-// global loads, so loads that `mid` leaves in flight never delay it).
-template <typename Mid>
+// global loads, so loads that `mid` leaves in flight never delay it).  COH: the logits are read
+// with device-scope loads (written earlier in the same launch by other workgroups).
+template <bool COH = false, typename Mid>
 __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on,
                               Mid&& mid) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
-    for (int i = tid; i < T * E; i += blockDim.x) s_logits[i] = io.logits[i];
+    for (int i = tid; i < T * E; i += blockDim.x)
+        s_logits[i] = COH ? __hip_atomic_load(io.logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : io.logits[i];
     for (int e = tid; e < E; e += blockDim.x) {
         s_cnt[e] = 0;
         s_mask[e] = 0;
@@ -767,6 +769,398 @@ __global__ void __launch_bounds__(512, 2) dec_w2c1(DecFfnArgs p) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// dec_stack: the residual stack for one token, n_layers decode layers in ONE cooperative launch of
+// resident workgroups (the 43-layer decode of the FreeToken/dothoosh page, "Architecture and the
+// sparsity puzzle", without a kernel boundary between layers).  Each layer runs the three
+// launches above as phases separated by grid barriers:
+//   logits   wavefront wv of workgroup b computes router row e = b + G*wv exactly as dec_logits
+//            does, with its row of W_r loaded before the barrier that opens the phase;
+//   gate/up  every workgroup routes from the logits in LDS, issues the loads of the down
+//            projection's weight rows for its own output rows (the slot table decides them), then
+//            runs dec_w13's items; the down rows land while the gate/up stream runs;
+//   down     dec_w2c1 on those rows; writes h for the next layer.
+// The per-row arithmetic and every summation order are those of the three launches, so the
+// results are equal bit for bit.
+// Data that crosses workgroups goes through device-scope (sc1) stores, written through to memory.
+// Readers of lines that several workgroups write (logits, a) use device-scope loads; the rest
+// (x, written whole by one wavefront; h between layers, one 128-byte line per 8-row block) sit in
+// regions of their own per layer that no cache can hold from before the write.  A barrier therefore
+// needs the store completions (s_waitcnt vmcnt(0) at every thread) and the counters, and no cache
+// write-back or invalidation.  Barrier: per-group arrival counters (group = workgroup % 32, one
+// 256-byte line each), the group's last arrival bumps a top counter, the top's last arrival writes
+// the release value into one flag line per group.  Every wait is bounded: a wait that runs out
+// sets an error word, and every workgroup leaves at its next barrier, so the launch always ends.
+// ------------------------------------------------------------------------------------------------
+constexpr int STACK_GROUPS = 32, STACK_LINE = 64;  // ints per 256-byte line
+constexpr int STACK_ERR = (2 * STACK_GROUPS + 1) * STACK_LINE;  // index of the error word
+
+// Returns false when this wait, or one in another workgroup, ran out.
+__device__ __forceinline__ bool stack_barrier(int* bar, int idx, int spin_limit, int* s_ok) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int G = gridDim.x, g = blockIdx.x % STACK_GROUPS;
+        const int ng = G < STACK_GROUPS ? G : STACK_GROUPS;
+        const int in_g = (G - g + STACK_GROUPS - 1) / STACK_GROUPS;  // workgroups of group g
+        int* flags = bar + (STACK_GROUPS + 1) * STACK_LINE;
+        int* err = bar + STACK_ERR;
+        bool ok = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+        if (ok) {
+            const int old = __hip_atomic_fetch_add(bar + g * STACK_LINE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == (idx + 1) * in_g) {
+                const int t = __hip_atomic_fetch_add(bar + STACK_GROUPS * STACK_LINE, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if (t + 1 == (idx + 1) * ng)
+                    for (int r = 0; r < ng; ++r)
+                        __hip_atomic_store(flags + r * STACK_LINE, idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            const int* f = flags + g * STACK_LINE;
+            int spins = 0;
+            while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < idx + 1) {
+                if (++spins > spin_limit ||
+                    ((spins & 31) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)) {
+                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        *s_ok = ok ? 1 : 0;
+    }
+    __syncthreads();
+    return *s_ok != 0;
+}
+
+// Every store of this thread has completed (device-scope stores: reached memory).
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void store_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// a_chunk<32> with device-scope loads: the eight 16-byte pieces of chunk c of a row of `a`,
+// issued together and waited for in the same statement.
+__device__ __forceinline__ void a_chunk32_dev(const float* row, int ncp, int c, float (&out)[32]) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    u32x4_t v0, v1, v2, v3, v4, v5, v6, v7;
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx4 %4, %12, off sc1\n\t"
+        "global_load_dwordx4 %5, %13, off sc1\n\t"
+        "global_load_dwordx4 %6, %14, off sc1\n\t"
+        "global_load_dwordx4 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+        : "v"(r4 + (int64_t)0 * ncp + c), "v"(r4 + (int64_t)1 * ncp + c), "v"(r4 + (int64_t)2 * ncp + c),
+          "v"(r4 + (int64_t)3 * ncp + c), "v"(r4 + (int64_t)4 * ncp + c), "v"(r4 + (int64_t)5 * ncp + c),
+          "v"(r4 + (int64_t)6 * ncp + c), "v"(r4 + (int64_t)7 * ncp + c)
+        : "memory");
+    const u32x4_t v[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        out[4 * q] = __uint_as_float(v[q].x);
+        out[4 * q + 1] = __uint_as_float(v[q].y);
+        out[4 * q + 2] = __uint_as_float(v[q].z);
+        out[4 * q + 3] = __uint_as_float(v[q].w);
+    }
+}
+
+constexpr int STACK_MAX_LAYERS = STACK_LAYERS_PER_LAUNCH;
+constexpr int STACK_HB = 32;  // floats per 8-row block of h between layers (one 128-byte line)
+
+struct StackLayer {
+    const uint16_t* wr;   // [E, d] bf16
+    const float* br;      // [E] or NULL
+    const uint8_t* w13;   // MXFP4 codes [E, 2f, d/2]
+    const uint8_t* w13s;  // [E, 2f, d/32]
+    const uint8_t* w2;    // [E, d, f/2]
+    const uint8_t* w2s;   // [E, d, f/32]
+};
+
+struct StackArgs {
+    StackLayer layer[STACK_MAX_LAYERS];
+    float* h;          // [d], the caller's: the first layer's input, the last layer's output
+    float* hbuf;       // n_layers - 1 regions of sh_h floats: h between layers, 8-row blocks of STACK_HB
+    float* logits;     // n_layers regions of sh_lg floats
+    uint16_t* xn;      // n_layers regions of sh_xn elements: x = bf16(h * inv_rms)
+    float* a;          // n_layers regions of sh_a floats: k rows of f, chunk-transposed (a_off)
+    int32_t* idx_out;  // nullable [n_layers, k]
+    int* bar;          // barrier counters, flags and error word, zero at launch
+    int64_t sh_h, sh_lg, sh_xn, sh_a;
+    int n_layers, d, f, E, k, no_renorm, spin_limit;
+};
+
+template <int R13, int U13, int R2, int MAXU2>
+__global__ void __launch_bounds__(512, 2) dec_stack(StackArgs p) {
+    using W = WChunk<2>;
+    constexpr int EC = W::EC;   // 32 elements per weight chunk
+    constexpr int NW = 8;       // wavefronts per workgroup
+    static_assert(R2 == 8, "h between layers is kept in 8-row blocks");
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    __shared__ DecRoute rs;
+    __shared__ float s_part[2][NW][R2];
+    __shared__ float s_pg[MOE_MAX_K + 1];
+    __shared__ int s_ok;
+    const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
+    const int G = gridDim.x;
+    const int d = p.d, f = p.f, E = p.E, k = p.k;
+    const int NCX = d / 8;                         // 16-byte chunks of a bf16 row of d
+    const int NC13 = d / EC, NC2 = f / EC, ncp = f / EC;
+    const int64_t rb13 = row_bytes(2, d), sb13 = scale_row_bytes(2, d);
+    const int64_t rb2 = row_bytes(2, f), sb2 = scale_row_bytes(2, f);
+    const int ngr = (f + R13 - 1) / R13;
+    const int nsteps = (NC13 + MOE_WAVE * U13 - 1) / (MOE_WAVE * U13);
+    const int n_rb = (d + R2 - 1) / R2;            // 8-row blocks of the output
+
+    // this wavefront's router row, loaded ahead of the phase that uses it
+    const int e_mine = blockIdx.x + G * wv;
+    uint4 wc[8];
+    auto load_router_row = [&](int l) {
+        const uint4* w = reinterpret_cast<const uint4*>(p.layer[l].wr + (int64_t)(e_mine < E ? e_mine : E - 1) * d);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int c = lane + MOE_WAVE * b;
+            wc[b] = (e_mine < E && c < NCX) ? w[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+
+    // routing LDS (as dec_w13); the phases below read the table through these local pointers,
+    // which the compiler keeps as LDS addresses (through rs.* it would use flat loads, whose
+    // waits also drain every global load in flight)
+    unsigned char* q = dyn_lds;
+    int4* const s_slot = reinterpret_cast<int4*>(q); q += (size_t)(E + 1) * 16;
+    float* const s_logits = reinterpret_cast<float*>(q); q += (size_t)E * 4;
+    float* const s_gate = reinterpret_cast<float*>(q); q += (size_t)k * 4;
+    int* const s_sel = reinterpret_cast<int*>(q); q += (size_t)k * 4;
+    int* const s_cnt = reinterpret_cast<int*>(q); q += (size_t)E * 4;
+    int* const s_mask = reinterpret_cast<int*>(q); q += (size_t)E * 4;
+    int* const s_on = reinterpret_cast<int*>(q);
+    if (tid == 0) {
+        rs.slot = s_slot;
+        rs.gate = s_gate;
+        rs.sel = s_sel;
+    }
+    __syncthreads();
+
+    load_router_row(0);
+    int bi = 0;
+    for (int l = 0; l < p.n_layers; ++l) {
+        const StackLayer& Lw = p.layer[l];
+        const bool first = l == 0, last = l == p.n_layers - 1;
+        const float* hin = first ? p.h : p.hbuf + (int64_t)(l - 1) * p.sh_h;
+        float* hout = last ? p.h : p.hbuf + (int64_t)l * p.sh_h;
+        const int hstride = first ? 8 : STACK_HB;  // floats from one 8-element chunk of h to the next
+        float* lg = p.logits + (int64_t)l * p.sh_lg;
+        uint16_t* xn = p.xn + (int64_t)l * p.sh_xn;
+        float* a = p.a + (int64_t)l * p.sh_a;
+
+        // ---- logits: dec_logits' single-pass residual-stack branch
+        if (e_mine < E) {
+            float4 hv[8][2];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int c = lane + MOE_WAVE * b;
+                const float4* hc = reinterpret_cast<const float4*>(hin + (int64_t)c * hstride);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) hv[b][q] = c < NCX ? hc[q] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    ss = fmaf(hv[b][q].x, hv[b][q].x, ss); ss = fmaf(hv[b][q].y, hv[b][q].y, ss);
+                    ss = fmaf(hv[b][q].z, hv[b][q].z, ss); ss = fmaf(hv[b][q].w, hv[b][q].w, ss);
+                }
+            const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)d + 1e-6f);
+            float acc = 0.0f;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int c = lane + MOE_WAVE * b;
+                if (c < NCX) {
+                    const uint4 xc = make_uint4(pack_bf16x2(hv[b][0].x * inv, hv[b][0].y * inv),
+                                                pack_bf16x2(hv[b][0].z * inv, hv[b][0].w * inv),
+                                                pack_bf16x2(hv[b][1].x * inv, hv[b][1].y * inv),
+                                                pack_bf16x2(hv[b][1].z * inv, hv[b][1].w * inv));
+                    acc += dot_chunk<uint16_t>(wc[b], xc);
+                    if (e_mine == 0) {
+                        uint32_t* xo = reinterpret_cast<uint32_t*>(xn + (int64_t)c * 8);
+                        store_dev(xo, xc.x); store_dev(xo + 1, xc.y); store_dev(xo + 2, xc.z); store_dev(xo + 3, xc.w);
+                    }
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) store_dev(lg + e_mine, acc + (Lw.br ? Lw.br[e_mine] : 0.0f));
+        }
+        stores_done();
+        if (!stack_barrier(p.bar, bi++, p.spin_limit, &s_ok)) return;
+
+        // ---- routing (every workgroup, in LDS), then the down rows' loads, then gate/up
+        {
+            const DecRouteIO io{lg, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, E, k, 0, p.no_renorm, nullptr};
+            dec_route_lds<true>(io, rs, s_logits, s_cnt, s_mask, s_on, [] {});
+        }
+        const int n_slots = rs.n_slots, n_routed = rs.n_routed;
+        if (tid < n_slots) {
+            // the gate of each slot's position (one token: position = slot index)
+            const int4 S = s_slot[tid];
+            float g = 1.0f;
+            for (int j = 0; j < k; ++j)
+                if (s_sel[j] == S.x) g = s_gate[j];
+            s_pg[S.y] = g;
+        }
+        if (blockIdx.x == 0 && tid < k && p.idx_out) p.idx_out[(int64_t)l * k + tid] = s_sel[tid];
+        const uint8_t* const w13p = Lw.w13;
+        const uint8_t* const w13sp = Lw.w13s;
+        const uint8_t* const w2p = Lw.w2;
+        const uint8_t* const w2sp = Lw.w2s;
+        if (tid < 2 * NW * R2) (&s_part[0][0][0])[tid] = 0.0f;
+
+        // dec_w2c1's first batch of this workgroup's first row block, loaded now (a second
+        // block's would not fit the registers beside the gate/up stream's)
+        const int nu = n_slots * R2;
+        const int u_lo = wv * nu / NW, u_hi = (wv + 1) * nu / NW;
+        // (lanes past the row's chunks load its last chunk, which they never use: every branch
+        // here is wave-uniform, so the loads go out back to back)
+        const int c2 = lane < NC2 ? lane : NC2 - 1;
+        auto load_down = [&](W (&dst)[MAXU2], int rb, int b0) {
+            const int nb = min(MAXU2, u_hi - b0);
+#pragma unroll
+            for (int j = 0; j < MAXU2; ++j) {
+                const int u = b0 + j, s = u / R2, i = rb * R2 + u % R2;
+                if (j < nb && i < d) {
+                    const int e = s_slot[s].x;
+                    dst[j].load(w2p + ((int64_t)e * d + i) * rb2, w2sp + ((int64_t)e * d + i) * sb2, c2);
+                } else {
+                    dst[j].zero();
+                }
+            }
+        };
+        const int rb0 = blockIdx.x;
+        W w2r[MAXU2];
+        if (rb0 < n_rb && u_lo < u_hi) load_down(w2r, rb0, u_lo);
+        __syncthreads();  // s_pg, s_part
+
+        // gate/up items (dec_w13, one token)
+        {
+            const int n_items = n_routed * ngr;
+            const uint16_t* xr = xn;
+            for (int item = blockIdx.x * NW + wv; item < n_items; item += G * NW) {
+                const int s = item / ngr, jg = item % ngr;
+                const int4 S = s_slot[s];
+                const int j0 = jg * R13;
+                const uint8_t* wb = w13p + (int64_t)S.x * 2 * f * rb13;
+                const uint8_t* sbp = w13sp + (int64_t)S.x * 2 * f * sb13;
+                float ag[R13], au[R13];
+#pragma unroll
+                for (int r = 0; r < R13; ++r) ag[r] = au[r] = 0.0f;
+                for (int st = 0; st < nsteps; ++st) {
+                    const int c0 = st * MOE_WAVE * U13;
+                    W wg[R13][U13], wu[R13][U13];
+#pragma unroll
+                    for (int r = 0; r < R13; ++r)
+#pragma unroll
+                        for (int u = 0; u < U13; ++u) {
+                            const int c = c0 + lane + MOE_WAVE * u, j = j0 + r;
+                            if (c < NC13 && j < f) {
+                                wg[r][u].load(wb + (int64_t)j * rb13, sbp + (int64_t)j * sb13, c);
+                                wu[r][u].load(wb + (int64_t)(f + j) * rb13, sbp + (int64_t)(f + j) * sb13, c);
+                            } else {
+                                wg[r][u].zero();
+                                wu[r][u].zero();
+                            }
+                        }
+#pragma unroll
+                    for (int u = 0; u < U13; ++u) {
+                        const int c = c0 + lane + MOE_WAVE * u;
+                        if (c < NC13) {
+#pragma unroll
+                            for (int r = 0; r < R13; ++r) {
+                                ag[r] = wg[r][u].dot_bf16(xr + (int64_t)c * EC, ag[r]);
+                                au[r] = wu[r][u].dot_bf16(xr + (int64_t)c * EC, au[r]);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < R13; ++r) {
+                    const float g = wave_sum(ag[r]), u = wave_sum(au[r]);
+                    const int j = j0 + r;
+                    if (lane == 0 && j < f) store_dev(a + (int64_t)S.y * f + a_off<EC>(j, ncp), g / (1.0f + expf(-g)) * u);
+                }
+            }
+        }
+        stores_done();
+        if (!stack_barrier(p.bar, bi++, p.spin_limit, &s_ok)) return;
+
+        // ---- down projection + combine (dec_w2c1, one token) on this workgroup's row blocks, two
+        //      at a time (blocks rb and rb + G share the slots, so one read of each slot's `a`
+        //      serves both); wa holds block rb's first batch (loaded before the barrier) when pre
+        auto down_pair = [&](int rbA, int rbB, W (&wa)[MAXU2], bool pre) {
+            for (int b0 = u_lo; b0 < u_hi; b0 += MAXU2) {
+                if (!pre || b0 != u_lo) load_down(wa, rbA, b0);
+                W wb[MAXU2];
+                if (rbB >= 0) load_down(wb, rbB, b0);
+                const int nb = min(MAXU2, u_hi - b0);
+                int cur = -1;
+                float g = 0.0f;
+                float av[EC];
+#pragma unroll
+                for (int j = 0; j < MAXU2; ++j) {
+                    if (j < nb) {
+                        const int u = b0 + j, s = u / R2, r = u % R2;
+                        if (s != cur) {
+                            const int4 S = s_slot[s];
+                            g = s_pg[S.y];
+                            if (lane < NC2) a_chunk32_dev(a + (int64_t)S.y * f, ncp, lane, av);
+                            cur = s;
+                        }
+                        float acc = 0.0f;
+                        if (lane < NC2) acc = wa[j].dot_f32(av, acc);
+                        const float y = wave_sum(acc);
+                        if (lane == 0) s_part[0][wv][r] = fmaf(g, y, s_part[0][wv][r]);
+                        if (rbB >= 0) {
+                            float acc2 = 0.0f;
+                            if (lane < NC2) acc2 = wb[j].dot_f32(av, acc2);
+                            const float y2 = wave_sum(acc2);
+                            if (lane == 0) s_part[1][wv][r] = fmaf(g, y2, s_part[1][wv][r]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            const int hb = tid / R2, rt = tid % R2, rb = hb == 0 ? rbA : rbB;
+            if (tid < 2 * R2 && rb >= 0 && rb * R2 + rt < d) {
+                float v = 0.0f;
+#pragma unroll
+                for (int w8 = 0; w8 < NW; ++w8) v += s_part[hb][w8][rt];
+                const int i = rb * R2 + rt;
+                const float* hp = first ? hin + i : hin + (int64_t)rb * STACK_HB + rt;
+                const float prev = __hip_atomic_load(hp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                store_dev(last ? hout + i : hout + (int64_t)rb * STACK_HB + rt, prev + v);
+            }
+            __syncthreads();
+            if (tid < 2 * NW * R2) (&s_part[0][0][0])[tid] = 0.0f;
+        };
+        for (int rb = rb0; rb < n_rb; rb += 2 * G) down_pair(rb, rb + G < n_rb ? rb + G : -1, w2r, rb == rb0);
+        stores_done();
+        if (!last) load_router_row(l + 1);
+        if (!stack_barrier(p.bar, bi++, p.spin_limit, &s_ok)) return;
+    }
+}
+
+__global__ void stack_clear(int* bar, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) bar[i] = 0;
+}
+
+// ------------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------------
 bool dec_supported(int T, int E, int k) {
@@ -874,6 +1268,47 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
 #undef MOE_DW21
 #undef MOE_DW2
     return hipGetLastError();
+}
+
+
+int dec_stack_bar_ints() { return STACK_ERR + STACK_LINE; }
+int dec_stack_err_index() { return STACK_ERR; }
+
+bool dec_stack_supported(int d, int f, int E, int k) {
+    // x chunks of one row in one pass per lane (d <= 4096), one weight chunk per lane and row of
+    // the down projection (f <= 2048): the shapes whose three-launch path is dec_logits'
+    // single-pass branch and dec_w2c1
+    return d % 32 == 0 && d / 8 <= MOE_WAVE * 8 && f % 32 == 0 && f / 32 <= MOE_WAVE && dec_supported(1, E, k);
+}
+
+hipError_t launch_dec_stack(const StackLayerPtrs* layers, int n_layers, float* h, float* hbuf, float* logits,
+                            uint16_t* xn, float* a, int32_t* idx_out, int* bar, int64_t sh_h, int64_t sh_lg,
+                            int64_t sh_xn, int64_t sh_a, int d, int f, int E, int k, bool no_renorm, int spin_limit,
+                            bool clear_err, hipStream_t st) {
+    if (n_layers < 1 || n_layers > STACK_MAX_LAYERS) return hipErrorInvalidValue;
+    StackArgs p{};
+    for (int l = 0; l < n_layers; ++l)
+        p.layer[l] = StackLayer{(const uint16_t*)layers[l].wr, layers[l].br, (const uint8_t*)layers[l].w13,
+                                layers[l].w13s, (const uint8_t*)layers[l].w2, layers[l].w2s};
+    p.h = h; p.hbuf = hbuf; p.logits = logits; p.xn = xn; p.a = a; p.idx_out = idx_out; p.bar = bar;
+    p.sh_h = sh_h; p.sh_lg = sh_lg; p.sh_xn = sh_xn; p.sh_a = sh_a;
+    p.n_layers = n_layers; p.d = d; p.f = f; p.E = E; p.k = k; p.no_renorm = no_renorm ? 1 : 0;
+    p.spin_limit = spin_limit;
+    // the three-launch path's tiles: dec_w13<2, 2, 2, 1> and dec_w2c1<2, 8, 1, 6>
+    constexpr int R13 = 2, U13 = 2, R2 = 8, MAXU2 = 6;
+    const void* kern = reinterpret_cast<const void*>(&dec_stack<R13, U13, R2, MAXU2>);
+    const size_t lds = dec_route_lds_bytes(1, E, k);
+    const int resident = resident_blocks(kern, 512, lds);
+    const int n_rb = (d + R2 - 1) / R2;
+    const int G = resident < n_rb ? resident : n_rb;
+    if (G * 8 < E) return hipErrorInvalidConfiguration;  // a wavefront per router row
+    // counters and flags start at zero; the error word is cleared by the first launch of a call only,
+    // so that a timeout in an earlier launch of the same call stays visible
+    hipLaunchKernelGGL(stack_clear, dim3(1), dim3(256), 0, st, bar, clear_err ? dec_stack_bar_ints() : STACK_ERR);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void* args[] = {&p};
+    return hipLaunchCooperativeKernel(kern, dim3(G), dim3(512), args, (unsigned)lds, st);
 }
 
 }  // namespace moe

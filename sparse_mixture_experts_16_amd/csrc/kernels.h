@@ -101,6 +101,23 @@ hipError_t launch_dec_ffn(int wt, bool out_bf16, const void* x, const float* log
                           const uint8_t* mask, const float* gsc, hipStream_t st);  // gsc: g13, g2, gs13, gs2
 
 // mask (nullable, E + 1 bytes; needs idx): terms of experts whose byte is 0 are left out.
+// The decode stack for one token in one cooperative launch (MXFP4 weights, bf16 activations).
+struct StackLayerPtrs {
+    const void* wr;
+    const float* br;
+    const void* w13;
+    const uint8_t* w13s;
+    const void* w2;
+    const uint8_t* w2s;
+};
+constexpr int STACK_LAYERS_PER_LAUNCH = 48;
+int dec_stack_bar_ints();
+int dec_stack_err_index();
+bool dec_stack_supported(int d, int f, int E, int k);
+hipError_t launch_dec_stack(const StackLayerPtrs* layers, int n_layers, float* h, float* hbuf, float* logits,
+                            uint16_t* xn, float* a, int32_t* idx_out, int* bar, int64_t sh_h, int64_t sh_lg,
+                            int64_t sh_xn, int64_t sh_a, int d, int f, int E, int k, bool no_renorm, int spin_limit,
+                            bool clear_err, hipStream_t st);
 hipError_t launch_combine(int y_dtype, int out_dtype, const void* y, const int32_t* inv, const float* topk_w,
                           const void* ysh, void* out, int T, int d, int k, bool accumulate, const int32_t* idx,
                           const uint8_t* mask, int E, hipStream_t st);

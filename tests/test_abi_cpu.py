@@ -178,3 +178,40 @@ def test_noalloc_validates_before_any_device_call():
 def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5, 5):
         assert isinstance(moe.lib().moe_status_string(st), bytes)
+
+
+def test_stack_persistent_validation_on_host():
+    """The persistent stack takes one token, bf16 activations, MXFP4 weights, no shared expert and
+    the single-pass decode shapes; everything else is refused before any launch."""
+    L = moe.lib()
+    ok = _shape(T=1, d_model=512, d_ff=256, n_experts=16, top_k=4, weight_dtype=moe.MOE_MXFP4)
+    W4 = moe.Weights(w13=FAKE, w2=FAKE, w13_scale=FAKE, w2_scale=FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    Ws = (moe.Weights * 2)(W4, W4)
+    size = L.moe_stack_persistent_workspace_size
+    assert size(ctypes.byref(ok), 2) > 0
+    # the barrier words plus, per layer, logits, x, a and (between layers) h, each 256-byte aligned
+    up = lambda v: (v + 255) // 256 * 256
+    per = up(16 * 4) + up(512 * 2) + up(4 * 256 * 4)
+    assert size(ctypes.byref(ok), 2) == up(size(ctypes.byref(ok), 1) + per + up(512 // 8 * 128))
+    assert size(ctypes.byref(ok), 100) == size(ctypes.byref(ok), 48)  # 48 layers per launch, regions reused
+    for bad in (dict(T=2), dict(weight_dtype=moe.MOE_BF16), dict(weight_dtype=moe.MOE_NVFP4),
+                dict(n_shared=1, shared_d_ff=256), dict(d_model=4096 + 32), dict(d_ff=2048 + 32),
+                dict(flags=moe.F_FORCE_GEMM)):
+        s = _shape(**{**dict(T=1, d_model=512, d_ff=256, n_experts=16, top_k=4, weight_dtype=moe.MOE_MXFP4), **bad})
+        assert size(ctypes.byref(s), 2) == 0, bad
+        assert L.moe_stack_forward_persistent(ctypes.byref(s), 2, FAKE, arr, None, Ws, None, FAKE, 1 << 40,
+                                              None) == moe.MOE_ERR_UNSUPPORTED, bad
+    call = lambda n=2, h=FAKE, idx=None, ws=FAKE, nb=1 << 40, wr=arr: L.moe_stack_forward_persistent(
+        ctypes.byref(ok), n, h, wr, None, Ws, idx, ws, nb, None)
+    assert call(n=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(n=0) == moe.MOE_OK
+    assert call(h=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert call(idx=FAKE + 4) == moe.MOE_ERR_INVALID_ARG
+    assert call(wr=(ctypes.c_void_p * 2)(FAKE, None)) == moe.MOE_ERR_INVALID_ARG
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert call(nb=size(ctypes.byref(ok), 2) - 1) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_stack_persistent_set_spin_limit(-1) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_persistent_status(None, ctypes.byref(ctypes.c_int32()), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_persistent_status(FAKE + 4, ctypes.byref(ctypes.c_int32()), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stack_persistent_status(FAKE, None, None) == moe.MOE_ERR_INVALID_ARG

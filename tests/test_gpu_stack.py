@@ -4,7 +4,8 @@ the benchmark times: moe_stack_forward on the decode kernels.
 
 The stack runs in segments [0], [1, 21), [21], [22, 42), [42] so that the residual stream h is
 kept before and after layers 0, 21 and 42 (the same kernels in the same order as one call over
-all 43 layers, which is checked bit for bit at the end).  For each kept layer the oracle's stack
+all 43 layers, which is checked bit for bit at the end, as is the persistent stack: one
+cooperative launch for the 43 layers).  For each kept layer the oracle's stack
 layer is evaluated on the GPU's own h before it -- RMS norm, router over all 256 experts, top-6,
 and the FFNs of the six selected experts only, generated on the host -- and compared with the
 GPU's h after it: the selection bit for bit, h element by element at the layer tolerance taken
@@ -106,6 +107,15 @@ def test_stack_c4_full_shape_sampled_layers():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(h), after[42])
     np.testing.assert_array_equal(host(idx_one), gidx)
+    # and so does the persistent stack (one cooperative launch for the 43 layers)
+    pws = torch.empty(moe.stack_persistent_workspace_size(shape, L), dtype=torch.uint8, device="cuda")
+    h = dev(np.ascontiguousarray(h0s[chosen:chosen + 1]))
+    idx_p = torch.full((L, 1, s.k), -1, dtype=torch.int32, device="cuda")
+    moe.stack_forward_persistent(shape, h, wrs, bs, Ws, pws, topk_idx_out=idx_p)
+    assert moe.stack_persistent_status(pws) == 0
+    np.testing.assert_array_equal(host(h), after[42])
+    np.testing.assert_array_equal(host(idx_p), gidx)
+    print("c4 stack: the persistent launch equals the three-launch stack bit for bit", flush=True)
     del keep, Ws, wrs, bs
     moe._ws_cache.clear()
     torch.cuda.empty_cache()
