@@ -118,7 +118,9 @@ def traffic_bytes(workload: str):
 
 
 def copy_calibration():
-    """A plain 256 MiB device-to-device copy, 5 times (the counters' reference)."""
+    """The counters' references: a plain 256 MiB device-to-device copy, 5 times; then 5 reads each
+    of the same 256 MiB by the whole-line stream (peak_hbm_read) and in the prefill GEMM's
+    tile-row pattern (64-byte pieces of 4096-byte rows), through registers and through LDS."""
     import torch
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -128,7 +130,18 @@ def copy_calibration():
     for _ in range(5):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_16_amd", "libmoe_peaks.so"))
+    lib.peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.peak_rows64_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.empty(n // 256, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(5):
+        assert lib.peak_hbm_read(a.data_ptr(), n, 2048, out.data_ptr(), st) == 0
+    for dma in (0, 1):
+        for _ in range(5):
+            assert lib.peak_rows64_read(a.data_ptr(), n, dma, out.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "read_bytes_per_launch": n, "launches": 5}))
 
 
 def expert_bytes(s, f=None):

@@ -8,6 +8,10 @@
 //                    per wavefront (the dependent-issue latency is covered)
 //   peak_mfma_f8f4   v_mfma_scale_f32_32x32x64_f8f6f4 with fp8 (E4M3) x fp4 (E2M1) operands, the
 //                    instruction of the MX prefill path, likewise
+//   rows64_read      the prefill GEMM's tile-row pattern, for the read counters' calibration: rows
+//                    of 4096 bytes, a wavefront reads 64-byte pieces of 16 rows per instruction and
+//                    the next pieces of the same rows one instruction later; through registers or
+//                    through LDS (global_load_lds_dwordx4, as the GEMMs fill their rings)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +37,39 @@ __global__ void __launch_bounds__(256) hbm_read(const uint4* __restrict__ src, s
     for (; i < n_chunks; i += stride) {
         const uint4 v = src[i];
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+constexpr int ROW_BYTES = 4096, ROWS_PER_WAVE = 16;
+
+__global__ void __launch_bounds__(256) rows64_read(const uint8_t* __restrict__ src, int rows, uint32_t* out) {
+    const int lane = threadIdx.x & 63, wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+    const int r = wave * ROWS_PER_WAVE + (lane >> 2);
+    uint32_t acc = 0;
+    if (r < rows) {
+        const uint8_t* p = src + (size_t)r * ROW_BYTES + (lane & 3) * 16;
+        for (int k = 0; k < ROW_BYTES / 64; ++k) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p + k * 64);
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(256) rows64_dma(const uint8_t* __restrict__ src, int rows, uint32_t* out) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][4][1024];  // wavefront x ring slot x 64 lanes * 16 B
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+    const int r = wave * ROWS_PER_WAVE + (lane >> 2);
+    const uint8_t* p = src + (size_t)(r < rows ? r : 0) * ROW_BYTES + (lane & 3) * 16;
+    uint32_t acc = 0;
+    for (int k = 0; k < ROW_BYTES / 64; ++k) {
+        __builtin_amdgcn_global_load_lds(p + k * 64, &lds[wv][k & 3][0], 16, 0, 0);
+        if ((k & 3) == 3) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            for (int q = 0; q < 4; ++q) acc ^= *reinterpret_cast<volatile uint32_t*>(&lds[wv][q][lane * 16]);
+        }
     }
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
@@ -107,5 +144,16 @@ int peak_mfma(int kind, int blocks, int iters, void* out, void* stream) {
 }
 
 int peak_mfma_per_wave(void) { return NACC; }
+
+// Reads `bytes` (a multiple of 64 rows of 4096 bytes) in the tile-row pattern, through registers
+// (dma = 0) or through LDS (dma = 1); out receives bytes / 256 words.
+int peak_rows64_read(const void* src, size_t bytes, int dma, void* out, void* stream) {
+    if (!src || !out || bytes % ((size_t)ROW_BYTES * ROWS_PER_WAVE * 4)) return -1;
+    const int rows = (int)(bytes / ROW_BYTES);
+    const dim3 grid(rows / (ROWS_PER_WAVE * 4)), block(256);
+    if (dma) hipLaunchKernelGGL(rows64_dma, grid, block, 0, (hipStream_t)stream, (const uint8_t*)src, rows, (uint32_t*)out);
+    else hipLaunchKernelGGL(rows64_read, grid, block, 0, (hipStream_t)stream, (const uint8_t*)src, rows, (uint32_t*)out);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 }  // extern "C"
