@@ -80,15 +80,16 @@ KERNEL_SOURCES = {
     "gemm": ["gemm.hip", "common.h", "wchunk.h", "lds_dma.h"],
     "mx": ["mxgemm.hip", "common.h", "lds_dma.h"],
 }
-COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)
+COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)  # profiles/read_counters__calibration.txt
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=27752.8, write_kib=54.3),
-    "c3_decode_T1": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=26256.3, write_kib=96.8),
-    "c3nv_decode_T1": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=27789.2, write_kib=96.2),
-    "c4_stack": dict(src="decode:c5b63d35f7ebcacf", fetch_kib=26256.1, write_kib=96.7),
-    "c2_prefill": dict(src="gemm:3a79fcd2ca97bd29", fetch_kib=762210.1, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:3a79fcd2ca97bd29", fetch_kib=1327013.7, write_kib=393216.0),
-    "c3_prefill_mx": dict(src="mx:81115b7c99f1254b", fetch_kib=1377996.2, write_kib=102178.8),
+    "c1_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27754.0, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.8, write_kib=96.9),
+    "c3nv_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27785.7, write_kib=96.2),
+    "c4_stack": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.7, write_kib=96.9),
+    "c4_stack_persistent": dict(src="decode:dc923cfed949d19b", fetch_kib=1751458.2, write_kib=20210.0),
+    "c2_prefill": dict(src="gemm:e89b94fbdaec5e5a", fetch_kib=765423.5, write_kib=110592.0),
+    "c3_prefill": dict(src="gemm:e89b94fbdaec5e5a", fetch_kib=1326623.3, write_kib=393216.0),
+    "c3_prefill_mx": dict(src="mx:943e79b78702dd7d", fetch_kib=1386342.3, write_kib=102263.0),
 }
 
 
