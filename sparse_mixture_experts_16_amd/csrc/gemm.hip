@@ -207,6 +207,15 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
     const int mrows = min(BM, rows_g - m0);
     const int64_t wrb = row_bytes(WT, K * (MODE == MODE_ROUTER ? p.ksplit : 1)), wsb = K / 32;
 
+    // `a` (the gate/up output, the down projection's A) is stored in 32-column stage blocks: block
+    // s of the routed rows holds all P sorted rows' columns 32s .. 32s+31 (64 bytes a row), so a
+    // down-projection stage of an m-tile is one contiguous 8 KB run of whole 128-byte lines
+    // instead of 128 half-lines of separate rows; the shared expert's T rows follow in fs/32
+    // blocks of their own.  a_row0: element of row 0 of the group in block 0; a_blk: elements
+    // from one block to the next.
+    const int64_t a_row0 = shared ? (int64_t)P * p.f : (int64_t)base * 32;
+    const int64_t a_blk = shared ? (int64_t)p.T * 32 : (int64_t)P * 32;
+
     // ---- this thread's global sources.  A chunk slot s = i*256 + tid holds row s/4 at physical
     // chunk s%4; rows past the group's end re-read the tile's first row (their results are
     // never stored).
@@ -219,7 +228,7 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
         if (r >= mrows) r = 0;
         int64_t src;
         if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
-        else if (MODE == MODE_W2) src = shared ? (int64_t)P * p.f + (int64_t)(m0 + r) * p.fs : (int64_t)(base + m0 + r) * p.f;
+        else if (MODE == MODE_W2) src = a_row0 + (int64_t)(m0 + r) * 32;
         else src = (int64_t)(m0 + r) * p.d;
         asrc[i] = p.A + src + (int64_t)ks * K + c * 8;
     }
@@ -258,11 +267,12 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
     auto issue = [&](int kt) {
         const int st = kt % NS;
         const int k0 = kt * BK;
+        const int64_t ka = (MODE == MODE_W2) ? (int64_t)kt * a_blk : k0;  // A: the next stage block, else 32 columns on
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             uint16_t* dA = &sA[st][0][(i * THREADS + wv * 64) * 8];
-            dma16(asrc[i] + k0, dA);
-            if (SPLIT) dma16(asrc[i] + p.lo_off + k0, &sA[st][NPL - 1][(i * THREADS + wv * 64) * 8]);
+            dma16(asrc[i] + ka, dA);
+            if (SPLIT) dma16(asrc[i] + p.lo_off + ka, &sA[st][NPL - 1][(i * THREADS + wv * 64) * 8]);
         }
         if (WT == 1) {
 #pragma unroll
@@ -392,6 +402,7 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
         constexpr int CH = NCOL / 8;  // 16-byte chunks per staged row
         const int col0 = nt * NCOL;
         const int lim = (MODE == MODE_W13) ? fg : N;  // columns of this group's output rows
+        static_assert(MODE != MODE_W13 || NCOL % 32 == 0, "gate/up tiles cover whole 32-column blocks of a");
 #pragma unroll
         for (int pl = 0; pl < (MODE == MODE_W13 ? 2 : 1); ++pl) {
             __syncthreads();
@@ -414,19 +425,27 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                     }
                 }
             __syncthreads();
-            for (int i = tid; i < BM * CH; i += THREADS) {
-                const int r = i / CH, ch = i % CH;
-                if (r >= mrows || col0 + ch * 8 >= lim) continue;
-                const int row = m0 + r;
-                const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
-                uint16_t* o;
-                if constexpr (MODE == MODE_W13)
-                    o = reinterpret_cast<uint16_t*>(p.out) + (pl ? p.lo_off : 0) +
-                        (shared ? (int64_t)P * p.f + (int64_t)row * p.fs : (int64_t)(base + row) * p.f) + col0 + ch * 8;
-                else
-                    o = (shared ? reinterpret_cast<uint16_t*>(p.out_sh) + (int64_t)row * p.d
-                                : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
-                *reinterpret_cast<uint4*>(o) = v;
+            if constexpr (MODE == MODE_W13) {
+                // a in its 32-column blocks: consecutive threads write each block's rows in order
+                for (int i = tid; i < BM * CH; i += THREADS) {
+                    const int sl = i / (BM * 4), r = (i / 4) % BM, c4 = i % 4;
+                    const int col = col0 + sl * 32 + c4 * 8;
+                    if (r >= mrows || col >= lim) continue;
+                    const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + sl * 32 + c4 * 8]);
+                    uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (pl ? p.lo_off : 0) + a_row0 +
+                                  (int64_t)(col / 32) * a_blk + (int64_t)(m0 + r) * 32 + c4 * 8;
+                    *reinterpret_cast<uint4*>(o) = v;
+                }
+            } else {
+                for (int i = tid; i < BM * CH; i += THREADS) {
+                    const int r = i / CH, ch = i % CH;
+                    if (r >= mrows || col0 + ch * 8 >= lim) continue;
+                    const int row = m0 + r;
+                    const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
+                    uint16_t* o = (shared ? reinterpret_cast<uint16_t*>(p.out_sh) + (int64_t)row * p.d
+                                          : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+                    *reinterpret_cast<uint4*>(o) = v;
+                }
             }
         }
     }
@@ -479,7 +498,8 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     return hipGetLastError();
 }
 
-// The SwiGLU activation is stored as two bf16 planes (hi, then lo) of P*f + T*fs elements each.
+// The SwiGLU activation is stored as two bf16 planes (hi, then lo) of P*f + T*fs elements each,
+// each in 32-column blocks (routed rows, then the shared expert's; see the kernel).
 static int64_t a_lo_offset(int T, int k, int f, int fs, int n_shared) {
     return (int64_t)T * k * f + (n_shared ? (int64_t)T * fs : 0);
 }
