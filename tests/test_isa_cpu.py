@@ -57,3 +57,19 @@ def test_no_compiler_drain_before_fragment_reads(src, prefix, tmp_path):
     for name, lines in kernels.items():
         assert any(ln.startswith("global_load_lds") for ln in lines), name
         assert not _drains(lines), (name, _drains(lines)[:4])
+
+
+def test_persistent_stack_keeps_its_prefetch_in_flight(tmp_path):
+    """The persistent decode stack issues the down projection's weight rows right after the routing,
+    to land under the gate/up stream.  A flat load (a read of the LDS routing table through a
+    pointer the compiler cannot place in LDS) or a scratch reload (a register spill) makes the
+    compiler wait for every global load in flight before using it, which serialised that prefetch
+    row by row (routing phase 4.3 -> 10.3 us).  Neither may appear in the kernel."""
+    kernels = _kernels("decode.hip", "_ZN3moe9dec_stack", tmp_path)
+    assert kernels, "no dec_stack kernel found in decode.hip"
+    for name, lines in kernels.items():
+        flat = [ln for ln in lines if ln.startswith("flat_load")]
+        scratch = [ln for ln in lines if ln.startswith("scratch_") or ln.startswith("buffer_") and "off, s[0:3]" in ln]
+        assert not flat, (name, flat[:4])
+        assert not scratch, (name, scratch[:4])
+        assert any(ln.startswith("global_load_dwordx4") for ln in lines), name
