@@ -87,8 +87,8 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c3nv_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27785.7, write_kib=96.2),
     "c4_stack": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.7, write_kib=96.9),
     "c4_stack_persistent": dict(src="decode:dc923cfed949d19b", fetch_kib=1751458.2, write_kib=20210.0),
-    "c2_prefill": dict(src="gemm:e89b94fbdaec5e5a", fetch_kib=765423.5, write_kib=110592.0),
-    "c3_prefill": dict(src="gemm:e89b94fbdaec5e5a", fetch_kib=1326623.3, write_kib=393216.0),
+    "c2_prefill": dict(src="gemm:bf27ae36266f6e56", fetch_kib=759714.7, write_kib=110701.5),
+    "c3_prefill": dict(src="gemm:bf27ae36266f6e56", fetch_kib=1321401.0, write_kib=393472.4),
     "c3_prefill_mx": dict(src="mx:943e79b78702dd7d", fetch_kib=1386342.3, write_kib=102263.0),
 }
 
