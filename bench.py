@@ -77,8 +77,8 @@ POOL = 256
 # the digest of the kernel sources it was taken on; a different digest reports null.
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "common.h", "wchunk.h"],
-    "gemm": ["gemm.hip", "common.h", "wchunk.h", "lds_dma.h"],
-    "mx": ["mxgemm.hip", "common.h", "lds_dma.h"],
+    "gemm": ["gemm.hip", "common.h", "wchunk.h", "lds_dma.h", "mxfp8.h"],
+    "mx": ["mxgemm.hip", "common.h", "lds_dma.h", "mxfp8.h"],
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)  # profiles/read_counters__calibration.txt
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)

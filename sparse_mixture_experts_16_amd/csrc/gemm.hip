@@ -21,6 +21,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "mxfp8.h"
 #include "wchunk.h"
 
 namespace moe {
@@ -43,6 +44,8 @@ struct GemmArgs {
     int T, d, f, fs, k, E, n_shared;
     const uint8_t* mask;      // nullable [E + 1]: groups whose byte is 0 get no tiles
     int ksplit;               // ROUTER: K split over this many workgroups (fp32 partials, no bias) when > 1
+    uint8_t* lo_q;            // W13 with LOQ, and ggemm_w2q: the lo plane as E4M3 codes (32-column blocks,
+    uint8_t* lo_s;            //   as the hi plane) and its E8M0 scales [rows][K/32] (routed rows, then shared)
 };
 
 __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
@@ -91,10 +94,14 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 // YF32 (down projection only): y is written in fp32 straight from the accumulators, so the
 // combine that follows sums unrounded expert outputs.
-template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 = false>
+// LOQ (gate/up only): the lo plane is written as MXFP8 (E4M3 codes with an E8M0 scale per 32
+// columns) for ggemm_w2q instead of as bf16.
+template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 = false, bool LOQ = false>
 __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p) {  // 2 waves per SIMD: <= 256 registers
     constexpr int BM = TBM, BK = 32;
     static_assert(NS == 2 || NS == 3, "ring depth");
@@ -425,7 +432,31 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                     }
                 }
             __syncthreads();
-            if constexpr (MODE == MODE_W13) {
+            if (MODE == MODE_W13 && LOQ && pl == 1) {
+                // lo as MXFP8: one thread per (row, 32-column block) of the tile
+                for (int i = tid; i < BM * (NCOL / 32); i += THREADS) {
+                    const int r = i % BM, sl = i / BM;
+                    const int col = col0 + sl * 32;
+                    if (r >= mrows || col >= lim) continue;
+                    float v[32];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 t = *reinterpret_cast<const uint4*>(&o_st[r * OP + sl * 32 + q * 8]);
+                        v[8 * q] = bf16_lo(t.x); v[8 * q + 1] = bf16_hi(t.x);
+                        v[8 * q + 2] = bf16_lo(t.y); v[8 * q + 3] = bf16_hi(t.y);
+                        v[8 * q + 4] = bf16_lo(t.z); v[8 * q + 5] = bf16_hi(t.z);
+                        v[8 * q + 6] = bf16_lo(t.w); v[8 * q + 7] = bf16_hi(t.w);
+                    }
+                    uint32_t code[8];
+                    const uint32_t sb = mx_block(v, code);
+                    uint4* o = reinterpret_cast<uint4*>(p.lo_q + a_row0 + (int64_t)(col / 32) * a_blk + (int64_t)(m0 + r) * 32);
+                    o[0] = make_uint4(code[0], code[1], code[2], code[3]);
+                    o[1] = make_uint4(code[4], code[5], code[6], code[7]);
+                    const int64_t srow = shared ? (int64_t)P * (p.f / 32) + (int64_t)(m0 + r) * (p.fs / 32)
+                                                : (int64_t)(base + m0 + r) * (p.f / 32);
+                    p.lo_s[srow + col / 32] = (uint8_t)sb;
+                }
+            } else if constexpr (MODE == MODE_W13) {
                 // a in its 32-column blocks: consecutive threads write each block's rows in order
                 for (int i = tid; i < BM * CH; i += THREADS) {
                     const int sl = i / (BM * 4), r = (i / 4) % BM, c4 = i % 4;
@@ -447,6 +478,257 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                     *reinterpret_cast<uint4*>(o) = v;
                 }
             }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// ggemm_w2q: the down projection of the bf16 path with MXFP4 weights, y = a_hi . W + a_lo . W.
+// a_hi (bf16) meets the weights on the bf16 matrix cores as in ggemm<W2>; the correction a_lo =
+// a - a_hi, about 2^-8 of a, needs only a few significant bits and comes as MXFP8 (E4M3 codes,
+// one E8M0 scale per 32 columns), so it meets the stored E2M1 codes directly on the scaled
+// fp8 x fp4 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4): one 64-K instruction per 32 x 32
+// sub-tile instead of four bf16 ones, and half the bytes of a bf16 lo plane.  The quantised
+// correction keeps the error of a within 2^-4 of the largest |a_lo| of its 32-column block
+// (≈ 2^-12 of the block's |a|).
+//
+// K stages of 64: per stage and 128 x 256 tile, a_hi rows of 128 bytes (two 32-column blocks,
+// 16-byte chunk c of row r at c ^ ((r >> 1) & 7)), a_lo rows of 64 bytes (chunk_swz) and weight
+// rows of 32 code bytes (chunk h of row n at h ^ ((n >> 3) & 1)); E8M0 scales of two stages
+// (four 32-element blocks, one dword per row) every second stage; a two-stage ring.
+// The 64 K elements of a stage are assigned to the bf16 instructions so that lane half h of
+// instruction c holds K = 32h + 8c .. +7: the four instructions of a lane then use exactly the
+// 32 codes (K = 32h .. 32h+31) that the lane hands to the scaled instruction, expanded per
+// dword, and one scale byte covers them.
+// ------------------------------------------------------------------------------------------------
+template <bool YF32>
+__global__ void __launch_bounds__(256, 2) ggemm_w2q(GemmArgs p) {
+    constexpr int BM = TBM, BN = 256, BK = 64, NWN = 2, THREADS = 256;
+    constexpr int WN = BN / NWN, NT32 = WN / 32;
+    constexpr int SZ_AH = BM * 128, SZ_AL = BM * 64, SZ_B = BN * 32;
+    constexpr int SZ_STAGE = SZ_AH + SZ_AL + SZ_B;
+    constexpr int SZ_SC = 2 * (BN + BM) * 4;
+    constexpr int OP = BN + 8;
+    constexpr int SZ_O = YF32 ? 0 : BM * OP * 2;
+    constexpr int SZ_RING = (2 * SZ_STAGE + SZ_SC) > SZ_O ? (2 * SZ_STAGE + SZ_SC) : SZ_O;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SZ_RING + (MOE_MAX_E + 2) * 4];
+    uint8_t* const sAH = smem;
+    uint8_t* const sAL = smem + 2 * SZ_AH;
+    uint8_t* const sB = smem + 2 * (SZ_AH + SZ_AL);
+    uint32_t* const sSB = reinterpret_cast<uint32_t*>(smem + 2 * SZ_STAGE);  // [2][BN]
+    uint32_t* const sSA = sSB + 2 * BN;                                       // [2][BM]
+    int* s_pref = reinterpret_cast<int*>(smem + SZ_RING);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = wave_id(), wm = wv / NWN, wn = wv % NWN;
+    const int G = p.E + p.n_shared;
+    const int P = p.T * p.k;
+
+    // ---- the flat tile list of ggemm<W2>: group g has ceil(rows_g / BM) x ceil(d / BN) tiles
+    auto tiles_of = [&](int g) -> int {
+        const bool sh = g == p.E;
+        const int rows = (p.mask && !p.mask[g]) ? 0 : (sh ? p.T : p.offsets[g + 1] - p.offsets[g]);
+        return ((rows + BM - 1) / BM) * ((p.d + BN - 1) / BN);
+    };
+    if (wv == 0) {
+        const int per = (G + 63) / 64;
+        const int lo = min(lane * per, G), hi = min(lo + per, G);
+        int sum = 0;
+        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += u;
+        }
+        int run = incl - sum;
+        for (int g = lo; g < hi; ++g) {
+            s_pref[g] = run;
+            run += tiles_of(g);
+        }
+        if (lane == 63) s_pref[G] = incl;
+    }
+    __syncthreads();
+    const int total = s_pref[G];
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int t_lo = (int)(((int64_t)total * xcd) >> 3), t_hi = (int)(((int64_t)total * (xcd + 1)) >> 3);
+    if (t_lo + j >= t_hi) return;
+    const int L = t_lo + j;
+    int g = 0;
+    {
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pref[mid] <= L) lo = mid;
+            else hi = mid;
+        }
+        g = lo;
+    }
+    const bool shared = g == p.E;
+    const int K = shared ? p.fs : p.f, N = p.d;
+    const int rows_g = shared ? p.T : p.offsets[g + 1] - p.offsets[g];
+    const int base = shared ? 0 : p.offsets[g];
+    const int ntiles = (p.d + BN - 1) / BN;
+    const int local = L - s_pref[g];
+    const int mt = local / ntiles, nt = local % ntiles;
+    const int m0 = mt * BM;
+    const int mrows = min(BM, rows_g - m0);
+    const int64_t wrb = K / 2, wsb = K / 32;
+    const uint8_t* W = shared ? p.sw : p.w + (int64_t)g * N * wrb;
+    const uint8_t* WS = shared ? p.swsc : p.wsc + (int64_t)g * N * wsb;
+    // a in 32-column blocks (as ggemm writes it): element of the group's row 0 in block 0, and
+    // elements from one block to the next; the lo plane's bytes follow the same offsets
+    const int64_t a_row0 = shared ? (int64_t)P * p.f : (int64_t)base * 32;
+    const int64_t a_blk = shared ? (int64_t)p.T * 32 : (int64_t)P * 32;
+
+    // ---- this thread's global sources (rows past the group's end re-read the tile's first row)
+    const uint16_t* ahsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int s = i * THREADS + tid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+        const int rr = r < mrows ? r : 0;
+        ahsrc[i] = p.A + a_row0 + (int64_t)(c >> 2) * a_blk + (int64_t)(m0 + rr) * 32 + (c & 3) * 8;
+    }
+    const uint8_t* alsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = i * THREADS + tid, r = s >> 2, c = (s & 3) ^ chunk_swz(r);
+        const int rr = r < mrows ? r : 0;
+        alsrc[i] = p.lo_q + a_row0 + (int64_t)(c >> 1) * a_blk + (int64_t)(m0 + rr) * 32 + (c & 1) * 16;
+    }
+    const uint8_t* bsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int s = i * THREADS + tid, n = s >> 1, h = (s & 1) ^ ((n >> 3) & 1);
+        const int r = nt * BN + n;
+        bsrc[i] = W + (int64_t)(r < N ? r : 0) * wrb + h * 16;
+    }
+    const int rb = nt * BN + tid;
+    const uint8_t* bssrc = WS + (int64_t)(rb < N ? rb : 0) * wsb;
+    const int ra = tid < mrows ? tid : 0;
+    const uint8_t* assrc = p.lo_s + (shared ? (int64_t)P * (p.f / 32) + (int64_t)(m0 + ra) * (p.fs / 32)
+                                            : (int64_t)(base + m0 + ra) * (p.f / 32));
+
+    auto issue = [&](int kt) {
+        const int st = kt & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16(ahsrc[i] + (int64_t)(2 * kt) * a_blk, sAH + st * SZ_AH + (i * THREADS + wv * 64) * 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma16(alsrc[i] + (int64_t)(2 * kt) * a_blk, sAL + st * SZ_AL + (i * THREADS + wv * 64) * 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(bsrc[i] + kt * 32, sB + st * SZ_B + (i * THREADS + wv * 64) * 16);
+        if ((kt & 1) == 0) {
+            dma4(bssrc + 2 * kt, &sSB[((kt >> 1) & 1) * BN + wv * 64]);
+            if (tid < BM) dma4(assrc + 2 * kt, &sSA[((kt >> 1) & 1) * BM + wv * 64]);
+        }
+    };
+
+    f32x16_t acc[2][NT32];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < NT32; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    const int l32 = lane & 31, hk = lane >> 5;
+    const int nk = K / BK;
+    const bool live = wm * 64 < mrows;
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        asm volatile("" ::: "memory");
+        VM_WAIT(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + 1 < nk) issue(kt + 1);
+        if (!live) continue;
+        const int sbuf = (kt >> 1) & 1, sh8 = 8 * (2 * (kt & 1) + hk);
+        // the lane's 32 weight codes (K = 32hk .. +31 of this stage) and their scale, per column tile
+        v4u_t bq[NT32];
+        uint32_t bsc[NT32];
+#pragma unroll
+        for (int ns = 0; ns < NT32; ++ns) {
+            const int n = wn * WN + ns * 32 + l32;
+            bq[ns] = *reinterpret_cast<const v4u_t*>(sB + st * SZ_B + n * 32 + ((hk ^ ((n >> 3) & 1)) * 16));
+            bsc[ns] = (sSB[sbuf * BN + n] >> sh8) & 0xFFu;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x8v bfr[NT32];
+#pragma unroll
+            for (int ns = 0; ns < NT32; ++ns) bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(bq[ns][c], bsc[ns]));
+            bf16x8v af[2];
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                const int r = wm * 64 + ms * 32 + l32;
+                af[ms] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const v4u_t*>(
+                    sAH + st * SZ_AH + r * 128 + (((4 * hk + c) ^ ((r >> 1) & 7)) * 16)));
+            }
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+        }
+        // the correction: E4M3 bytes 0..15 at K = 16hk + 0..15 and 16..31 at K = 32 + 16hk + 0..15
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            const int r = wm * 64 + ms * 32 + l32;
+            const uint8_t* row = sAL + st * SZ_AL + r * 64;
+            const v4u_t lo = *reinterpret_cast<const v4u_t*>(row + ((hk ^ chunk_swz(r)) * 16));
+            const v4u_t hi = *reinterpret_cast<const v4u_t*>(row + (((2 + hk) ^ chunk_swz(r)) * 16));
+            const v8i_t aq = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const int sa = (int)((sSA[sbuf * BM + r] >> sh8) & 0xFFu);
+#pragma unroll
+            for (int ns = 0; ns < NT32; ++ns) {
+                const v8i_t bf = v8i_t{(int)bq[ns].x, (int)bq[ns].y, (int)bq[ns].z, (int)bq[ns].w, 0, 0, 0, 0};
+                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aq, bf, acc[ms][ns], 0, 4, 0, sa, 0,
+                                                                              (int)bsc[ns]);
+            }
+        }
+    }
+
+    // ---- epilogue: accumulator j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32
+    if constexpr (YF32) {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 64 + ms * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+                if (r >= mrows) continue;
+                const int row = m0 + r;
+                float* o = shared ? reinterpret_cast<float*>(p.out_sh) + (int64_t)row * p.d
+                                  : reinterpret_cast<float*>(p.out) + (int64_t)(base + row) * p.d;
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns) {
+                    const int n = nt * BN + wn * WN + ns * 32 + (lane & 31);
+                    if (n < N) o[n] = acc[ms][ns][e];
+                }
+            }
+    } else {
+        uint16_t* o_st = reinterpret_cast<uint16_t*>(smem);
+        __syncthreads();
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 64 + ms * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+#pragma unroll
+                for (int ns = 0; ns < NT32; ++ns) o_st[r * OP + wn * WN + ns * 32 + (lane & 31)] = f32_to_bf16(acc[ms][ns][e]);
+            }
+        __syncthreads();
+        constexpr int CH = BN / 8;
+        const int col0 = nt * BN;
+        for (int i = tid; i < BM * CH; i += THREADS) {
+            const int r = i / CH, ch = i % CH;
+            if (r >= mrows || col0 + ch * 8 >= N) continue;
+            const int row = m0 + r;
+            const uint4 v = *reinterpret_cast<const uint4*>(&o_st[r * OP + ch * 8]);
+            uint16_t* o = (shared ? reinterpret_cast<uint16_t*>(p.out_sh) + (int64_t)row * p.d
+                                  : reinterpret_cast<uint16_t*>(p.out) + (int64_t)(base + row) * p.d) + col0 + ch * 8;
+            *reinterpret_cast<uint4*>(o) = v;
         }
     }
 }
@@ -511,6 +793,17 @@ static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int sha
     return routed_mt * rows_nt + shared_mt * shared_nt;
 }
 
+// With MXFP4 weights and whole 256-column tiles, the lo plane of a goes to the down projection
+// as MXFP8 (ggemm_w2q); its codes follow the hi plane in the workspace, then its scales.
+static bool lo_fp8(int wt, int d, int f, int fs, int n_shared) {
+    return wt == 2 && d % 256 == 0 && f % 256 == 0 && (!n_shared || fs % 256 == 0);
+}
+static void lo_planes(GemmArgs& p, uint16_t* a, int T, int k, int f, int fs, int n_shared) {
+    const int64_t plane = a_lo_offset(T, k, f, fs, n_shared);
+    p.lo_q = reinterpret_cast<uint8_t*>(a + plane);
+    p.lo_s = p.lo_q + plane;
+}
+
 hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, const int32_t* offsets,
                             const int32_t*, const int32_t*, const void* w13, const uint8_t* w13s, const void* s13,
                             const uint8_t* s13s, uint16_t* a, int T, int d, int f, int fs, int k, int E, int n_shared,
@@ -522,7 +815,13 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
         // workgroup per CU) halves the activation reads per weight row at little LDS cost
         constexpr int BN = 512, NWN = 4;
         const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
-        MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+        if (lo_fp8(wt, d, f, fs, n_shared)) {
+            lo_planes(p, a, T, k, f, fs, n_shared);
+            MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 3, false, true>), dim3(grid), dim3(128 * NWN), 0,
+                       st, p);
+        } else {
+            MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+        }
         return hipGetLastError();
     }
     constexpr int BN = 256, NWN = 2;  // 128 gate/up column pairs per tile, 4 wavefronts
@@ -538,6 +837,13 @@ hipError_t launch_ggemm_w2(int wt, const uint16_t* a, const int32_t* offsets, co
                            const uint8_t* mask, hipStream_t st) {
     GemmArgs p{a, nullptr, offsets, (const uint8_t*)w2, w2s, (const uint8_t*)s2, s2s, nullptr, y, y_shared,
                a_lo_offset(T, k, f, fs, n_shared), T, d, f, fs, k, E, n_shared, mask, 1};
+    if (lo_fp8(wt, d, f, fs, n_shared)) {
+        lo_planes(p, const_cast<uint16_t*>(a), T, k, f, fs, n_shared);
+        const unsigned grid = grid8(max_tiles(T, k, E, n_shared, d / 256, d / 256));
+        if (y_f32) MOE_LAUNCH(PROF_FFN_DOWN, (ggemm_w2q<true>), dim3(grid), dim3(256), 0, st, p);
+        else MOE_LAUNCH(PROF_FFN_DOWN, (ggemm_w2q<false>), dim3(grid), dim3(256), 0, st, p);
+        return hipGetLastError();
+    }
     constexpr int NWN = 2;
 #define MOE_W2(BNV, NSV)                                                                                         \
     do {                                                                                                         \

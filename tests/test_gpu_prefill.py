@@ -32,7 +32,8 @@ SMALL = [
     # d_model not a multiple of 256: the down projection's 128-column tiles
     mi.LayerSpec("g_bf16_d192", 140, 192, 128, 8, 2, 1, 64, "bf16", "bf16", 1.0, 0.05, 0.05, seed=27),
     mi.LayerSpec("g_bf16_d320", 97, 320, 192, 12, 3, 1, 128, "bf16", "bf16", 1.0, 0.05, 0.05, seed=28),
-    # MXFP4 with d_ff and shared d_ff multiples of 256: the 128 x 512 gate/up tiles, shared group included
+    # MXFP4 with d_ff and shared d_ff multiples of 256: the 128 x 512 gate/up tiles, shared group
+    # included; with d_model a multiple of 256 too, the down projection's MXFP8 correction plane
     mi.LayerSpec("g_mxfp4_f256_shared256", 150, 256, 256, 8, 2, 1, 256, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=29),
     mi.LayerSpec("g_mxfp4_f256_shared512", 70, 384, 256, 10, 3, 1, 512, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=30),
 ]
@@ -55,7 +56,9 @@ def test_layer_forward_gemm_small(s):
     assert_close(host(res["out"]), ref["out"], what=s.name)
 
 
-@pytest.mark.parametrize("s", SMALL[:3], ids=lambda s: s.name)
+# the step call with bf16 y_sorted: bf16 weights, MXFP4 with a bf16 correction plane (d_ff 128), and
+# MXFP4 with the MXFP8 correction plane (d_model, d_ff and shared d_ff multiples of 256)
+@pytest.mark.parametrize("s", SMALL[:3] + SMALL[6:7], ids=lambda s: s.name)
 def test_grouped_ffn_gemm_small(s):
     x, wr, b, _ = margin_x(s)
     w = mi.host_experts(s)

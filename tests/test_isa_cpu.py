@@ -50,7 +50,8 @@ def _drains(lines: list[str]) -> list[str]:
     return bad
 
 
-@pytest.mark.parametrize("src,prefix", [("mxgemm.hip", "_ZN3moe6mxgemm"), ("gemm.hip", "_ZN3moe5ggemm")])
+@pytest.mark.parametrize("src,prefix", [("mxgemm.hip", "_ZN3moe6mxgemm"), ("gemm.hip", "_ZN3moe5ggemm"),
+                                        ("gemm.hip", "_ZN3moe9ggemm_w2q")])
 def test_no_compiler_drain_before_fragment_reads(src, prefix, tmp_path):
     kernels = _kernels(src, prefix, tmp_path)
     assert kernels, f"no {prefix} kernels found in {src}"
