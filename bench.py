@@ -87,9 +87,9 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c3nv_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27785.7, write_kib=96.2),
     "c4_stack": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.7, write_kib=96.9),
     "c4_stack_persistent": dict(src="decode:dc923cfed949d19b", fetch_kib=1751458.2, write_kib=20210.0),
-    "c2_prefill": dict(src="gemm:bf27ae36266f6e56", fetch_kib=759714.7, write_kib=110701.5),
-    "c3_prefill": dict(src="gemm:bf27ae36266f6e56", fetch_kib=1321401.0, write_kib=393472.4),
-    "c3_prefill_mx": dict(src="mx:943e79b78702dd7d", fetch_kib=1386342.3, write_kib=102263.0),
+    "c2_prefill": dict(src="gemm:10d87a3fb01b1dc3", fetch_kib=756137.8, write_kib=110703.0),
+    "c3_prefill": dict(src="gemm:10d87a3fb01b1dc3", fetch_kib=1317828.2, write_kib=298389.8),
+    "c3_prefill_mx": dict(src="mx:a8543ccbbdad988e", fetch_kib=1382364.4, write_kib=102270.3),
 }
 
 
