@@ -279,6 +279,72 @@ __device__ __forceinline__ int dec_slot_scan(DecRoute& R, const int* s_cnt, cons
     return pa;
 }
 
+// One token with the top-k renormalised gates and up to 256 experts (the decode step):
+// wavefront 0 routes alone, with
+// the token's logits (and on flags) loaded straight into its registers -- no LDS copy, no
+// per-expert counts, masks or scan, and a single barrier.  With one token every picked expert
+// holds one pair, so the slot table follows from ranking the k picks among themselves: a pick's
+// first sorted position is the number of picks with a lower expert id, its slot the number of
+// active picks with a lower id.  Selections, gates and table equal the general path's.
+template <bool COH, int KPL, typename Mid>
+__device__ void dec_route_one(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_on, Mid&& mid) {
+    const int lane = lane_id(), wv = wave_id();
+    const int E = io.E, k = io.k;
+    float lg[KPL];
+    uint32_t on = 0u;  // bit j: entry j of the lane is left in
+    int shared_on = 0;
+    if (wv == 0) {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int e = lane * KPL + j;
+            lg[j] = 0.0f;
+            if (e < E) {
+                lg[j] = COH ? __hip_atomic_load(io.logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : io.logits[e];
+                if (!io.emask || io.emask[e]) on |= 1u << j;
+            }
+        }
+        shared_on = io.n_shared && (!io.emask || io.emask[E]);
+    }
+    mid();
+    if (wv == 0) {
+        uint32_t key[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int e = lane * KPL + j;
+            key[j] = e < E ? sel_ord(lg[j]) : 0u;
+            if (e < E) {
+                s_logits[e] = lg[j];
+                s_on[e] = (on >> j) & 1u;
+            }
+        }
+        const int my_sel = wave_topk<KPL>(key, k);
+        const bool pick = lane < k;
+        const float m = s_logits[__builtin_amdgcn_readlane(my_sel, 0)];
+        const float term = pick ? expf(s_logits[my_sel] - m) : 0.0f;
+        const float den = wave_sum(term);
+        const bool act = pick && s_on[my_sel];
+        int pos = 0, slot = 0;
+        for (int j = 0; j < k; ++j) {
+            const int sj = __builtin_amdgcn_readlane(my_sel, j);
+            const int aj = __builtin_amdgcn_readlane((int)act, j);
+            pos += sj < my_sel;
+            slot += (aj && sj < my_sel) ? 1 : 0;
+        }
+        if (pick) {
+            R.sel[lane] = my_sel;
+            R.gate[lane] = term / den;
+        }
+        if (act) R.slot[slot] = make_int4(my_sel, pos, 1, 1);
+        const int n_act = __popcll(__ballot(act));
+        if (lane == 0) {
+            R.n_routed = n_act;
+            R.n_slots = n_act + shared_on;
+            if (shared_on) R.slot[n_act] = make_int4(E, k, 1, 1);
+        }
+    }
+    __syncthreads();
+}
+
 // `mid` runs once the logits are in LDS, before the top-k (the rest of the routing issues no
 // global loads, so loads that `mid` leaves in flight never delay it).  COH: the logits are read
 // with device-scope loads (written earlier in the same launch by other workgroups).
@@ -288,6 +354,12 @@ __device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
+    if (T == 1 && !io.no_renorm && E <= 256) {
+        if (E <= 64) dec_route_one<COH, 1>(io, R, s_logits, s_on, mid);
+        else if (E <= 128) dec_route_one<COH, 2>(io, R, s_logits, s_on, mid);
+        else dec_route_one<COH, 4>(io, R, s_logits, s_on, mid);
+        return;
+    }
     for (int i = tid; i < T * E; i += blockDim.x)
         s_logits[i] = COH ? __hip_atomic_load(io.logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : io.logits[i];
     for (int e = tid; e < E; e += blockDim.x) {
@@ -490,7 +562,9 @@ __global__ void __launch_bounds__(512, (WT == 1 && TQ == 1) ? 8 : 1) dec_w13(Dec
         const bool sh = item < s_items;
         const int s = sh ? rs.n_routed : (item - s_items) / ngr;
         const int jg = sh ? item : (item - s_items) % ngr;
-        const int4 S = rs.slot[s];
+        // the table sits at the start of the dynamic LDS: read it through that address (a
+        // pointer kept in the shared routing struct is a generic one, read by flat loads)
+        const int4 S = reinterpret_cast<const int4*>(dyn_lds)[s];
         const int fc = sh ? p.fs : p.f;
         const int j0 = jg * R;
         const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)S.x * 2 * p.f * rb;
