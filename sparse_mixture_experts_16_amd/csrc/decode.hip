@@ -218,6 +218,18 @@ struct DecRoute {
     int* sel;     // [T * k]
 };
 
+// The routing's LDS arrays, as pointers the caller derives from its own LDS (so the compiler
+// addresses them as LDS).
+struct DecRouteLds {
+    int4* slot;     // [E + 1]
+    float* logits;  // [T * E]
+    float* gate;    // [T * k]
+    int* sel;       // [T * k]
+    int* cnt;       // [E]
+    int* mask;      // [E]
+    int* on;        // [E + 1]
+};
+
 // Dynamic LDS carve-up of the routing prologue: slots, logits, gates, experts, counts, masks.
 __host__ __device__ inline size_t dec_route_lds_bytes(int T, int E, int k) {
     return (size_t)(E + 1) * 16 + (size_t)T * E * 4 + (size_t)T * k * 8 + (size_t)E * 8 + (size_t)(E + 1) * 4 + 16;
@@ -286,10 +298,14 @@ __device__ __forceinline__ int dec_slot_scan(DecRoute& R, const int* s_cnt, cons
 // holds one pair, so the slot table follows from ranking the k picks among themselves: a pick's
 // first sorted position is the number of picks with a lower expert id, its slot the number of
 // active picks with a lower id.  Selections, gates and table equal the general path's.
+// The table, picks and gates are written through the caller's LDS pointers (pointers read back
+// from the shared routing struct are generic ones: flat stores).
 template <bool COH, int KPL, typename Mid>
-__device__ void dec_route_one(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_on, Mid&& mid) {
+__device__ void dec_route_one(const DecRouteIO& io, DecRoute& R, const DecRouteLds& L, Mid&& mid) {
     const int lane = lane_id(), wv = wave_id();
     const int E = io.E, k = io.k;
+    float* const s_logits = L.logits;
+    int* const s_on = L.on;
     float lg[KPL];
     uint32_t on = 0u;  // bit j: entry j of the lane is left in
     int shared_on = 0;
@@ -331,15 +347,15 @@ __device__ void dec_route_one(const DecRouteIO& io, DecRoute& R, float* s_logits
             slot += (aj && sj < my_sel) ? 1 : 0;
         }
         if (pick) {
-            R.sel[lane] = my_sel;
-            R.gate[lane] = term / den;
+            L.sel[lane] = my_sel;
+            L.gate[lane] = term / den;
         }
-        if (act) R.slot[slot] = make_int4(my_sel, pos, 1, 1);
+        if (act) L.slot[slot] = make_int4(my_sel, pos, 1, 1);
         const int n_act = __popcll(__ballot(act));
         if (lane == 0) {
             R.n_routed = n_act;
             R.n_slots = n_act + shared_on;
-            if (shared_on) R.slot[n_act] = make_int4(E, k, 1, 1);
+            if (shared_on) L.slot[n_act] = make_int4(E, k, 1, 1);
         }
     }
     __syncthreads();
@@ -349,15 +365,18 @@ __device__ void dec_route_one(const DecRouteIO& io, DecRoute& R, float* s_logits
 // global loads, so loads that `mid` leaves in flight never delay it).  COH: the logits are read
 // with device-scope loads (written earlier in the same launch by other workgroups).
 template <bool COH = false, typename Mid>
-__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, float* s_logits, int* s_cnt, int* s_mask, int* s_on,
-                              Mid&& mid) {
+__device__ void dec_route_lds(const DecRouteIO& io, DecRoute& R, const DecRouteLds& L, Mid&& mid) {
     const int lane = lane_id(), wv = wave_id(), tid = threadIdx.x;
     const int NW = blockDim.x / MOE_WAVE;
     const int T = io.T, E = io.E, k = io.k;
+    float* const s_logits = L.logits;
+    int* const s_cnt = L.cnt;
+    int* const s_mask = L.mask;
+    int* const s_on = L.on;
     if (T == 1 && !io.no_renorm && E <= 256) {
-        if (E <= 64) dec_route_one<COH, 1>(io, R, s_logits, s_on, mid);
-        else if (E <= 128) dec_route_one<COH, 2>(io, R, s_logits, s_on, mid);
-        else dec_route_one<COH, 4>(io, R, s_logits, s_on, mid);
+        if (E <= 64) dec_route_one<COH, 1>(io, R, L, mid);
+        else if (E <= 128) dec_route_one<COH, 2>(io, R, L, mid);
+        else dec_route_one<COH, 4>(io, R, L, mid);
         return;
     }
     for (int i = tid; i < T * E; i += blockDim.x)
@@ -541,12 +560,15 @@ __global__ void __launch_bounds__(512, (WT == 1 && TQ == 1) ? 8 : 1) dec_w13(Dec
         unsigned char* q = dyn_lds;
         rs.slot = reinterpret_cast<int4*>(q); q += (size_t)(E + 1) * 16;
         float* s_logits = reinterpret_cast<float*>(q); q += (size_t)T * E * 4;
-        rs.gate = reinterpret_cast<float*>(q); q += (size_t)T * k * 4;
-        rs.sel = reinterpret_cast<int*>(q); q += (size_t)T * k * 4;
+        float* rs_gate = reinterpret_cast<float*>(q); q += (size_t)T * k * 4;
+        int* rs_sel = reinterpret_cast<int*>(q); q += (size_t)T * k * 4;
+        rs.gate = rs_gate;
+        rs.sel = rs_sel;
         int* s_cnt = reinterpret_cast<int*>(q); q += (size_t)E * 4;
         int* s_mask = reinterpret_cast<int*>(q); q += (size_t)E * 4;
         int* s_on = reinterpret_cast<int*>(q);
-        dec_route_lds(p.rt, rs, s_logits, s_cnt, s_mask, s_on, warm_l2);
+        const DecRouteLds L{reinterpret_cast<int4*>(dyn_lds), s_logits, rs_gate, rs_sel, s_cnt, s_mask, s_on};
+        dec_route_lds(p.rt, rs, L, warm_l2);
     }
     // an empty asm that takes the warming dwords as inputs keeps their loads (the values
     // themselves are never used) and lets their registers go here
@@ -1079,7 +1101,8 @@ __global__ void __launch_bounds__(512, 2) dec_stack(StackArgs p) {
         // ---- routing (every workgroup, in LDS), then the down rows' loads, then gate/up
         {
             const DecRouteIO io{lg, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, E, k, 0, p.no_renorm, nullptr};
-            dec_route_lds<true>(io, rs, s_logits, s_cnt, s_mask, s_on, [] {});
+            const DecRouteLds L{s_slot, s_logits, s_gate, s_sel, s_cnt, s_mask, s_on};
+            dec_route_lds<true>(io, rs, L, [] {});
         }
         const int n_slots = rs.n_slots, n_routed = rs.n_routed;
         if (tid < n_slots) {
