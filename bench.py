@@ -82,11 +82,11 @@ KERNEL_SOURCES = {
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)  # profiles/read_counters__calibration.txt
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27754.0, write_kib=54.3),
-    "c3_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.8, write_kib=96.9),
-    "c3nv_decode_T1": dict(src="decode:dc923cfed949d19b", fetch_kib=27785.7, write_kib=96.2),
-    "c4_stack": dict(src="decode:dc923cfed949d19b", fetch_kib=26256.7, write_kib=96.9),
-    "c4_stack_persistent": dict(src="decode:dc923cfed949d19b", fetch_kib=1751458.2, write_kib=20210.0),
+    "c1_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=27752.8, write_kib=54.4),
+    "c3_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=26249.3, write_kib=96.8),
+    "c3nv_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=27769.8, write_kib=96.2),
+    "c4_stack": dict(src="decode:e7bf335d72a637b6", fetch_kib=26249.0, write_kib=96.7),
+    "c4_stack_persistent": dict(src="decode:e7bf335d72a637b6", fetch_kib=1751431.0, write_kib=20210.0),
     "c2_prefill": dict(src="gemm:10d87a3fb01b1dc3", fetch_kib=756137.8, write_kib=110703.0),
     "c3_prefill": dict(src="gemm:10d87a3fb01b1dc3", fetch_kib=1317828.2, write_kib=298389.8),
     "c3_prefill_mx": dict(src="mx:a8543ccbbdad988e", fetch_kib=1382364.4, write_kib=102270.3),
