@@ -59,7 +59,9 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4); a 0xFF scale gives NaN.
+// 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4); a 0xFF scale gives NaN.  The NaN case is
+// a select, not a branch: a branch closes the basic block, and the compiler's wait insertion
+// then drains every LDS read in flight at it, one fragment at a time.
 __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     const float sc = e8m0_to_f32(s);
     uint4 r;
@@ -67,7 +69,13 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     r.y = cvt2(w, sc, 1);
     r.z = cvt2(w, sc, 2);
     r.w = cvt2(w, sc, 3);
-    if (s == 255u) r = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    // (the empty asm pins the converts ahead of the select, so they are not sunk under it)
+    asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+    const bool nan = s == 255u;
+    r.x = nan ? 0x7FC07FC0u : r.x;
+    r.y = nan ? 0x7FC07FC0u : r.y;
+    r.z = nan ? 0x7FC07FC0u : r.z;
+    r.w = nan ? 0x7FC07FC0u : r.w;
     return r;
 }
 
@@ -326,6 +334,16 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
 #pragma unroll
             for (int ns = 0; ns < NT32; ++ns) sc_w[ns] = sS[(kt >> 2) & 1][wn * WN + ns * 32 + l32];
         }
+        // MXFP4: every code word of the stage read from LDS up front (the two K halves of a
+        // lane's row are 8 bytes apart: one ds_read2 each), then expanded per K half
+        uint32_t cw[BK / 16][NT32];
+        if (WT == 2) {
+#pragma unroll
+            for (int ns = 0; ns < NT32; ++ns)
+#pragma unroll
+                for (int kk = 0; kk < BK / 16; ++kk)
+                    cw[kk][ns] = *reinterpret_cast<const uint32_t*>(&sB[st][(wn * WN + ns * 32 + l32) * BROW + kk * 4 + hk * 2]);
+        }
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int fc = kk ? fc1 : fc0;
@@ -336,9 +354,8 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
                 if (WT == 1) {
                     bfr[ns] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(&sB[st][n * BROW + fc]));
                 } else {
-                    const uint32_t cw = *reinterpret_cast<const uint32_t*>(&sB[st][n * BROW + kk * 4 + hk * 2]);
                     const uint32_t s8 = (sc_w[ns] >> (8 * (kt & 3))) & 0xFFu;
-                    bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(cw, s8));
+                    bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(cw[kk][ns], s8));
                 }
             }
 #pragma unroll
