@@ -59,6 +59,14 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w, float sc, int sel) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// LDS swizzles of the long-stage tiles: x rows of BK bf16 (128 or 256 bytes), chunk c of row r at
+// c ^ a_swz(r); MXFP4 code rows of BK/2 bytes, chunk h of row n at h ^ b_swz(n).  Each spreads
+// the rows that 8 consecutive lanes read over distinct banks.
+template <int BK>
+__device__ __forceinline__ int a_swz(int r) { return BK == 64 ? ((r >> 1) & 7) : (r & 15); }
+template <int BK>
+__device__ __forceinline__ int b_swz(int n) { return BK == 64 ? ((n >> 3) & 1) : chunk_swz(n); }
+
 // 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4); a 0xFF scale gives NaN.  The NaN case is
 // a select, not a branch: a branch closes the basic block, and the compiler's wait insertion
 // then drains every LDS read in flight at it, one fragment at a time.
@@ -98,10 +106,10 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // chunk per row; each B fragment (8 codes, one dword) is expanded at read time with the
 // scaled bf16 converts (exact: E2M1 x 2^k fits bf16).  The E8M0 scales travel as one dword
 // (4 consecutive blocks) per row every fourth stage into a double-buffered LDS row list.
-// KB = 64 (MXFP4 gate/up): 64-element stages, 128-byte x rows (chunk c of row r at
-// c ^ ((r >> 1) & 7)) and two code chunks per weight row (chunk h of row n at h ^ ((n >> 3) & 1)),
-// the scale dword every second stage; inside a stage K is permuted so that MFMA c of lane half h
-// takes K = 32h + 8c .. +7: the lane's 32 codes of one block feed all four of its MFMAs.
+// KB = 64 or 128 (MXFP4 gate/up): long stages, x rows of 128 or 256 bytes and 2 or 4 code
+// chunks per weight row (swizzled by a_swz / b_swz), the scale dword every second or every
+// stage; inside each 64 of a stage K is permuted so that MFMA c of lane half h takes
+// K = 32h + 8c .. +7: the lane's 32 codes of one block feed four of its MFMAs.
 // SPLIT: the A operand comes as two bf16 planes a = hi + lo (lo = a - hi rounded to bf16), and
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
@@ -117,8 +125,9 @@ template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 =
 __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p) {  // 2 waves per SIMD: <= 256 registers
     constexpr int BM = TBM, BK = KB;
     // 64-element stages: MXFP4 gate/up only (x rows of 128 bytes, 32 code bytes per weight row)
-    static_assert(KB == 32 || (KB == 64 && WT == 2 && MODE == MODE_W13 && !SPLIT), "stage depth");
-    constexpr int SPG = BK == 64 ? 2 : 4;           // stages per MXFP4 scale dword (4 blocks of 32)
+    static_assert(KB == 32 || ((KB == 64 || KB == 128) && WT == 2 && MODE == MODE_W13 && !SPLIT), "stage depth");
+    constexpr int SPG = 128 / BK;                   // stages per MXFP4 scale dword (4 blocks of 32)
+    constexpr int CPR = BK / 32;                    // MXFP4 code chunks (blocks) per weight row and stage
     static_assert(NS == 2 || NS == 3, "ring depth");
     constexpr int THREADS = 128 * NWN;              // 2 wavefronts along M x NWN along N
     constexpr int NPL = SPLIT ? 2 : 1;              // A planes
@@ -127,11 +136,11 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
     constexpr int ROWE = BK;                        // bf16 elements per LDS tile row (64 or 128 B)
     constexpr int BROW = (WT == 1) ? 32 : BK / 4;   // uint16 per LDS B row (bf16: 64 B, MXFP4 codes: 16 or 32 B)
     constexpr int NA = BM * (BK / 8) / THREADS;     // A chunks per thread per plane
-    constexpr int NB = (WT == 1) ? BN * 4 / THREADS : (BN * (BK / 32) + THREADS - 1) / THREADS;  // B chunks per thread (max)
-    static_assert(BK == 32 || (BN * 2) % THREADS == 0, "64-element stages: every thread loads whole B chunks");
+    constexpr int NB = (WT == 1) ? BN * 4 / THREADS : (BN * CPR + THREADS - 1) / THREADS;  // B chunks per thread (max)
+    static_assert(BK == 32 || (BN * CPR) % THREADS == 0, "long stages: every thread loads whole B chunks");
     static_assert(NA >= 1 && (WT != 1 || NB >= 1), "tile / thread count");
     // vector-memory ops one stage adds per thread, counted for the wave that issues the fewest
-    constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BK == 64 ? NB : (BN >= THREADS ? 1 : 0)));
+    constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BK > 32 ? NB : (BN >= THREADS ? 1 : 0)));
     static_assert(OPS < 16, "vmcnt immediate");
     // One LDS object carved by offsets.  Fragment reads are loads of plain (vector) types: the
     // compiler's wait insertion drains every LDS-DMA load in flight before an LDS read that carries
@@ -246,9 +255,10 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
     const uint16_t* asrc[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        // 64-byte rows: chunk c of row r at c ^ chunk_swz(r); 128-byte rows: at c ^ ((r >> 1) & 7)
-        int r = BK == 64 ? (i * THREADS + tid) >> 3 : i * (THREADS / 4) + (tid >> 2);
-        const int c = BK == 64 ? ((tid & 7) ^ ((r >> 1) & 7)) : (pc ^ chunk_swz(r));
+        // 64-byte rows: chunk c of row r at c ^ chunk_swz(r); 128-byte rows: at c ^ ((r >> 1) & 7);
+        // 256-byte rows: at c ^ (r & 15)
+        int r = BK == 32 ? i * (THREADS / 4) + (tid >> 2) : (i * THREADS + tid) / (BK / 8);
+        const int c = BK == 32 ? (pc ^ chunk_swz(r)) : ((tid % (BK / 8)) ^ a_swz<BK>(r));
         if (r >= mrows) r = 0;
         int64_t src;
         if (MODE == MODE_W13) src = shared ? (int64_t)(m0 + r) * p.d : (int64_t)(p.perm[base + m0 + r] / p.k) * p.d;
@@ -279,12 +289,12 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
             const int n = i * (THREADS / 4) + (tid >> 2);
             bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (int64_t)ks * K * 2 + (pc ^ chunk_swz(n)) * 16;
         }
-    } else if (BK == 64) {
-        // two 16-byte code chunks (two 32-element blocks) per B row, chunk h of row n at
-        // h ^ ((n >> 3) & 1); the row's scale dword (4 blocks = 2 stages) every second stage
+    } else if (BK > 32) {
+        // CPR 16-byte code chunks (32-element blocks) per B row, chunk h of row n at
+        // h ^ b_swz(n); the row's scale dword (4 blocks) every SPG stages
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int sidx = i * THREADS + tid, n = sidx >> 1, h = (sidx & 1) ^ ((n >> 3) & 1);
+            const int sidx = i * THREADS + tid, n = sidx / CPR, h = (sidx % CPR) ^ b_swz<BK>(n);
             bsrc[i] = W + (int64_t)wrow_of(n) * wrb + h * 16;
         }
         s_on = tid < BN;
@@ -308,7 +318,7 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
             dma16(asrc[i] + ka, dA);
             if (SPLIT) dma16(asrc[i] + p.lo_off + ka, &sA[st][NPL - 1][(i * THREADS + wv * 64) * 8]);
         }
-        if (WT == 1 || BK == 64) {
+        if (WT == 1 || BK > 32) {
 #pragma unroll
             for (int i = 0; i < NB; ++i)
                 dma16(bsrc[i] + (WT == 1 ? (int64_t)k0 * 2 : (int64_t)k0 / 2), &sB[st][(i * THREADS + wv * 64) * 8]);
@@ -353,38 +363,43 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
 #pragma unroll
             for (int ns = 0; ns < NT32; ++ns) sc_w[ns] = sS[(kt / SPG) & 1][wn * WN + ns * 32 + l32];
         }
-        if constexpr (BK == 64) {
-            // 64-element stage, K permuted inside it as the down projection's kernel does: MFMA c
-            // of lane half h covers K = 32h + 8c .. +7, so a lane's 32 codes (one 16-byte chunk,
-            // the 32-element block 2 (kt & 1) + h of its row's scale dword) serve all four MFMAs,
-            // and the A fragment of MFMA c is chunk 4h + c of the row
+        if constexpr (BK > 32) {
+            // long stage, K permuted inside each 64 of it as the down projection's kernel does:
+            // MFMA c of 64-group q and lane half h covers K = 64q + 32h + 8c .. +7, so a lane's 32
+            // codes (one 16-byte chunk: block 2q + h of the stage) serve four MFMAs, and the A
+            // fragment of that MFMA is chunk 8q + 4h + c of the row
             const uint8_t* const sBs = reinterpret_cast<const uint8_t*>(&sB[st][0]);
             const uint8_t* const sAs = reinterpret_cast<const uint8_t*>(&sA[st][0][0]);
-            v4u_t bq[NT32];
-            uint32_t bsc[NT32];
+            const int blk0 = BK == 64 ? 2 * (kt & 1) : 0;  // the stage's first block in the scale dword
 #pragma unroll
-            for (int ns = 0; ns < NT32; ++ns) {
-                const int n = wn * WN + ns * 32 + l32;
-                bq[ns] = *reinterpret_cast<const v4u_t*>(sBs + n * 32 + ((hk ^ ((n >> 3) & 1)) * 16));
-                bsc[ns] = (sc_w[ns] >> (8 * (2 * (kt & 1) + hk))) & 0xFFu;
-            }
+            for (int q = 0; q < BK / 64; ++q) {
+                v4u_t bq[NT32];
+                uint32_t bsc[NT32];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                bf16x8v bfr[NT32];
-#pragma unroll
-                for (int ns = 0; ns < NT32; ++ns) bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(bq[ns][c], bsc[ns]));
-                bf16x8v af[2];
-#pragma unroll
-                for (int ms = 0; ms < 2; ++ms) {
-                    const int r = wm * 64 + ms * 32 + l32;
-                    af[ms] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const v4u_t*>(
-                        sAs + r * 128 + (((4 * hk + c) ^ ((r >> 1) & 7)) * 16)));
+                for (int ns = 0; ns < NT32; ++ns) {
+                    const int n = wn * WN + ns * 32 + l32;
+                    bq[ns] = *reinterpret_cast<const v4u_t*>(sBs + n * (BK / 2) + (((2 * q + hk) ^ b_swz<BK>(n)) * 16));
+                    bsc[ns] = (sc_w[ns] >> (8 * (blk0 + 2 * q + hk))) & 0xFFu;
                 }
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
+                for (int c = 0; c < 4; ++c) {
+                    bf16x8v bfr[NT32];
 #pragma unroll
                     for (int ns = 0; ns < NT32; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+                        bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(bq[ns][c], bsc[ns]));
+                    bf16x8v af[2];
+#pragma unroll
+                    for (int ms = 0; ms < 2; ++ms) {
+                        const int r = wm * 64 + ms * 32 + l32;
+                        af[ms] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const v4u_t*>(
+                            sAs + r * (BK * 2) + (((8 * q + 4 * hk + c) ^ a_swz<BK>(r)) * 16)));
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                        for (int ns = 0; ns < NT32; ++ns)
+                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
+                }
             }
             continue;
         }
@@ -886,20 +901,22 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
         // workgroup per CU) halves the activation reads per weight row at little LDS cost
         constexpr int BN = 512, NWN = 4;
         const unsigned grid = grid8(max_tiles(T, k, E, n_shared, f / (BN / 2), n_shared ? fs / (BN / 2) : 0));
-        // 64-element K stages (128-byte x rows, 32 code bytes per weight row, half the barriers
-        // per flop) when K = d is a whole number of scale dwords' worth of stage pairs
-        const bool kb64 = d % 128 == 0;
+        // 128-element K stages (256-byte x rows, 64 code bytes per weight row, a quarter of the
+        // barriers per flop of 32-element stages; two of them fill 128 KB of LDS) when K = d is a
+        // whole number of stages: c3 gate/up 2349 -> 1899 us with 64-element stages three deep,
+        // 1882 us with these
+        const bool kb_long = d % 128 == 0;
         if (lo_fp8(wt, d, f, fs, n_shared)) {
             lo_planes(p, a, T, k, f, fs, n_shared);
-            if (kb64)
-                MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 3, false, true, 64>), dim3(grid),
+            if (kb_long)
+                MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 2, false, true, 128>), dim3(grid),
                            dim3(128 * NWN), 0, st, p);
             else
                 MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 3, false, true>), dim3(grid), dim3(128 * NWN),
                            0, st, p);
-        } else if (kb64) {
-            MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 3, false, false, 64>), dim3(grid), dim3(128 * NWN),
-                       0, st, p);
+        } else if (kb_long) {
+            MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN, 2, false, false, 128>), dim3(grid),
+                       dim3(128 * NWN), 0, st, p);
         } else {
             MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
         }
