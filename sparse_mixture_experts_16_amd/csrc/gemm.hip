@@ -106,10 +106,12 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
 // chunk per row; each B fragment (8 codes, one dword) is expanded at read time with the
 // scaled bf16 converts (exact: E2M1 x 2^k fits bf16).  The E8M0 scales travel as one dword
 // (4 consecutive blocks) per row every fourth stage into a double-buffered LDS row list.
-// KB = 64 or 128 (MXFP4 gate/up): long stages, x rows of 128 or 256 bytes and 2 or 4 code
+// KB = 64 or 128 (gate/up): long stages, x rows of 128 or 256 bytes and 2 or 4 MXFP4 code
 // chunks per weight row (swizzled by a_swz / b_swz), the scale dword every second or every
 // stage; inside each 64 of a stage K is permuted so that MFMA c of lane half h takes
-// K = 32h + 8c .. +7: the lane's 32 codes of one block feed four of its MFMAs.
+// K = 32h + 8c .. +7: the lane's 32 codes of one block feed four of its MFMAs.  bf16 weight
+// rows of 128 bytes are laid out and read as the x rows.  TM = 256 (bf16 gate/up): tiles of
+// 256 token rows, 4 x NWN wavefronts.
 // SPLIT: the A operand comes as two bf16 planes a = hi + lo (lo = a - hi rounded to bf16), and
 // every B fragment is applied to both, so the fp32 SwiGLU output keeps ~16 significant bits
 // through the bf16 matrix cores.
@@ -121,23 +123,25 @@ typedef int v8i_t __attribute__((ext_vector_type(8)));
 // combine that follows sums unrounded expert outputs.
 // LOQ (gate/up only): the lo plane is written as MXFP8 (E4M3 codes with an E8M0 scale per 32
 // columns) for ggemm_w2q instead of as bf16.
-template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 = false, bool LOQ = false, int KB = 32>
-__global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p) {  // 2 waves per SIMD: <= 256 registers
-    constexpr int BM = TBM, BK = KB;
+template <int MODE, int WT, int BN, bool SPLIT, int NWN, int NS = 3, bool YF32 = false, bool LOQ = false, int KB = 32,
+          int TM = TBM>
+__global__ void __launch_bounds__(TM / 64 * 64 * NWN, TM / 64 * NWN >= 8 ? 1 : 2) ggemm(GemmArgs p) {  // <= 256 registers
+    constexpr int BM = TM, BK = KB;
+    static_assert(TM == 128 || (TM == 256 && KB == 64 && WT == 1), "256-row tiles: bf16 gate/up on 64-element stages");
     // 64-element stages: MXFP4 gate/up only (x rows of 128 bytes, 32 code bytes per weight row)
-    static_assert(KB == 32 || ((KB == 64 || KB == 128) && WT == 2 && MODE == MODE_W13 && !SPLIT), "stage depth");
+    static_assert(KB == 32 || ((KB == 64 || (KB == 128 && WT == 2)) && MODE == MODE_W13 && !SPLIT), "stage depth");
     constexpr int SPG = 128 / BK;                   // stages per MXFP4 scale dword (4 blocks of 32)
     constexpr int CPR = BK / 32;                    // MXFP4 code chunks (blocks) per weight row and stage
     static_assert(NS == 2 || NS == 3, "ring depth");
-    constexpr int THREADS = 128 * NWN;              // 2 wavefronts along M x NWN along N
+    constexpr int THREADS = BM / 64 * 64 * NWN;     // BM / 64 wavefronts along M x NWN along N
     constexpr int NPL = SPLIT ? 2 : 1;              // A planes
     constexpr int WN = BN / NWN;                    // wave tile columns
     constexpr int NT32 = WN / 32;                   // 32-wide MFMA column tiles per wave (2 or 4)
     constexpr int ROWE = BK;                        // bf16 elements per LDS tile row (64 or 128 B)
-    constexpr int BROW = (WT == 1) ? 32 : BK / 4;   // uint16 per LDS B row (bf16: 64 B, MXFP4 codes: 16 or 32 B)
+    constexpr int BROW = (WT == 1) ? BK : BK / 4;   // uint16 per LDS B row (bf16: 64 or 128 B, MXFP4 codes: 16, 32 or 64 B)
     constexpr int NA = BM * (BK / 8) / THREADS;     // A chunks per thread per plane
-    constexpr int NB = (WT == 1) ? BN * 4 / THREADS : (BN * CPR + THREADS - 1) / THREADS;  // B chunks per thread (max)
-    static_assert(BK == 32 || (BN * CPR) % THREADS == 0, "long stages: every thread loads whole B chunks");
+    constexpr int NB = (WT == 1) ? BN * (BK / 8) / THREADS : (BN * CPR + THREADS - 1) / THREADS;  // B chunks per thread (max)
+    static_assert(BK == 32 || WT == 1 || (BN * CPR) % THREADS == 0, "long stages: every thread loads whole B chunks");
     static_assert(NA >= 1 && (WT != 1 || NB >= 1), "tile / thread count");
     // vector-memory ops one stage adds per thread, counted for the wave that issues the fewest
     constexpr int OPS = NPL * NA + ((WT == 1) ? NB : (BK > 32 ? NB : (BN >= THREADS ? 1 : 0)));
@@ -283,7 +287,14 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
     const uint8_t* bsrc[NB];
     const uint8_t* ssrc = nullptr;
     bool b_on = true, s_on = false;
-    if (WT == 1) {
+    if (WT == 1 && BK == 64) {
+        // bf16 weight rows of 128 bytes a stage, laid out as the x rows (chunk c at c ^ a_swz(n))
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int n = (i * THREADS + tid) >> 3, c = (tid & 7) ^ a_swz<64>(n);
+            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + c * 16;
+        }
+    } else if (WT == 1) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int n = i * (THREADS / 4) + (tid >> 2);
@@ -378,15 +389,23 @@ __global__ void __launch_bounds__(128 * NWN, NWN == 4 ? 1 : 2) ggemm(GemmArgs p)
 #pragma unroll
                 for (int ns = 0; ns < NT32; ++ns) {
                     const int n = wn * WN + ns * 32 + l32;
-                    bq[ns] = *reinterpret_cast<const v4u_t*>(sBs + n * (BK / 2) + (((2 * q + hk) ^ b_swz<BK>(n)) * 16));
-                    bsc[ns] = (sc_w[ns] >> (8 * (blk0 + 2 * q + hk))) & 0xFFu;
+                    if (WT == 2) {
+                        bq[ns] = *reinterpret_cast<const v4u_t*>(sBs + n * (BK / 2) + (((2 * q + hk) ^ b_swz<BK>(n)) * 16));
+                        bsc[ns] = (sc_w[ns] >> (8 * (blk0 + 2 * q + hk))) & 0xFFu;
+                    }
                 }
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     bf16x8v bfr[NT32];
 #pragma unroll
-                    for (int ns = 0; ns < NT32; ++ns)
-                        bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(bq[ns][c], bsc[ns]));
+                    for (int ns = 0; ns < NT32; ++ns) {
+                        const int n = wn * WN + ns * 32 + l32;
+                        if (WT == 1)  // bf16 rows: chunk 4h + c, as the x fragment
+                            bfr[ns] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const v4u_t*>(
+                                sBs + n * 128 + (((4 * hk + c) ^ a_swz<64>(n)) * 16)));
+                        else
+                            bfr[ns] = __builtin_bit_cast(bf16x8v, fp4x8_to_bf16(bq[ns][c], bsc[ns]));
+                    }
                     bf16x8v af[2];
 #pragma unroll
                     for (int ms = 0; ms < 2; ++ms) {
@@ -872,10 +891,10 @@ static int64_t a_lo_offset(int T, int k, int f, int fs, int n_shared) {
     return (int64_t)T * k * f + (n_shared ? (int64_t)T * fs : 0);
 }
 
-static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt) {
+static int64_t max_tiles(int T, int k, int E, int n_shared, int rows_nt, int shared_nt, int bm = TBM) {
     const int64_t P = (int64_t)T * k;
-    const int64_t routed_mt = (P + TBM - 1) / TBM + (P < E ? P : E);
-    const int64_t shared_mt = n_shared ? (T + TBM - 1) / TBM : 0;
+    const int64_t routed_mt = (P + bm - 1) / bm + (P < E ? P : E);
+    const int64_t shared_mt = n_shared ? (T + bm - 1) / bm : 0;
     return routed_mt * rows_nt + shared_mt * shared_nt;
 }
 
@@ -924,7 +943,15 @@ hipError_t launch_ggemm_w13(int wt, const uint16_t* x, const int32_t* perm, cons
     }
     constexpr int BN = 256, NWN = 2;  // 128 gate/up column pairs per tile, 4 wavefronts
     const unsigned grid = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2), n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0));
-    if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
+    if (wt == 1 && d % 64 == 0) {
+        // bf16 weights: 256 x 256 tiles of 8 wavefronts on 64-element stages two deep (128-byte
+        // x and weight rows, 128 KB of LDS, one workgroup per CU): half the barriers per flop of
+        // the 128 x 256 tiles on 32-element stages (c2 gate/up 358 -> 333 us)
+        const unsigned grid2 = grid8(max_tiles(T, k, E, n_shared, (f + BN / 2 - 1) / (BN / 2),
+                                               n_shared ? (fs + BN / 2 - 1) / (BN / 2) : 0, 256));
+        MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false, NWN, 2, false, false, 64, 256>), dim3(grid2),
+                   dim3(256 * NWN), 0, st, p);
+    } else if (wt == 1) MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 1, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
     else MOE_LAUNCH(PROF_FFN_UP, (ggemm<MODE_W13, 2, BN, false, NWN>), dim3(grid), dim3(128 * NWN), 0, st, p);
     return hipGetLastError();
 }
