@@ -87,8 +87,8 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c3nv_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=27769.8, write_kib=96.2),
     "c4_stack": dict(src="decode:e7bf335d72a637b6", fetch_kib=26249.0, write_kib=96.7),
     "c4_stack_persistent": dict(src="decode:e7bf335d72a637b6", fetch_kib=1751431.0, write_kib=20210.0),
-    "c2_prefill": dict(src="gemm:42a81c7f11294bb9", fetch_kib=758399.4, write_kib=110702.9),
-    "c3_prefill": dict(src="gemm:42a81c7f11294bb9", fetch_kib=1909472.4, write_kib=298153.5),
+    "c2_prefill": dict(src="gemm:4c15bee888b49cac", fetch_kib=563483.5, write_kib=110645.8),
+    "c3_prefill": dict(src="gemm:4c15bee888b49cac", fetch_kib=1909294.1, write_kib=298152.1),
     "c3_prefill_mx": dict(src="mx:a8543ccbbdad988e", fetch_kib=1386020.6, write_kib=102293.9),
 }
 
