@@ -36,6 +36,11 @@ SMALL = [
     # included; with d_model a multiple of 256 too, the down projection's MXFP8 correction plane
     mi.LayerSpec("g_mxfp4_f256_shared256", 150, 256, 256, 8, 2, 1, 256, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=29),
     mi.LayerSpec("g_mxfp4_f256_shared512", 70, 384, 256, 10, 3, 1, 512, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=30),
+    # gate/up stage lengths: d_model not a multiple of 64 keeps bf16 weights on the 128-row tiles
+    # with 32-element stages; MXFP4 with d_ff a multiple of 256 but d_model not of 128 keeps the
+    # 128 x 512 tiles on 32-element stages (the others above take the long stages)
+    mi.LayerSpec("g_bf16_d224", 120, 224, 128, 8, 2, 1, 128, "bf16", "bf16", 1.0, 0.05, 0.05, seed=31),
+    mi.LayerSpec("g_mxfp4_f256_d160", 90, 160, 256, 8, 2, 0, 0, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=32),
 ]
 
 
