@@ -91,6 +91,32 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     u += dpp<0x143, 0xC>(0u, u);
     return (int)u;
 }
+// Exclusive prefix of per-group tile counts into s_pref[0..G] (s_pref[G] = the total), by one
+// wavefront: lane l takes groups l*per .. l*per+per-1 (per <= TPL), issues all of their count
+// loads at once, and a single wave scan joins the lanes.
+template <int TPL, typename F>
+__device__ __forceinline__ void wave_tile_prefix(int G, int* s_pref, F&& tiles_of) {
+    const int lane = threadIdx.x & 63;
+    const int per = (G + 63) / 64;
+    const int lo = min(lane * per, G), hi = min(lo + per, G);
+    int t[TPL];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+        t[j] = (j < per && lo + j < hi) ? tiles_of(lo + j) : 0;
+        sum += t[j];
+    }
+    const int incl = wave_incl_scan(sum);
+    int run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+        if (j < per && lo + j < hi) {
+            s_pref[lo + j] = run;
+            run += t[j];
+        }
+    if (lane == 63) s_pref[G] = incl;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

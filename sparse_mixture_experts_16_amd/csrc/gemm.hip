@@ -177,24 +177,7 @@ __global__ void __launch_bounds__(TM / 64 * 64 * NWN, TM / 64 * NWN >= 8 ? 1 : 2
         }
         return ((rows + BM - 1) / BM) * nt;
     };
-    if (wv == 0) {
-        const int per = (G + 63) / 64;
-        const int lo = min(lane * per, G), hi = min(lo + per, G);
-        int sum = 0;
-        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            int u = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += u;
-        }
-        int run = incl - sum;
-        for (int g = lo; g < hi; ++g) {
-            s_pref[g] = run;
-            run += tiles_of(g);
-        }
-        if (lane == 63) s_pref[G] = incl;
-    }
+    if (wv == 0) wave_tile_prefix<(MOE_MAX_E + 64) / 64>(G, s_pref, tiles_of);
     __syncthreads();
 
     // workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of the actual list (the grid is
@@ -634,24 +617,7 @@ __global__ void __launch_bounds__(256, 2) ggemm_w2q(GemmArgs p) {
         const int rows = (p.mask && !p.mask[g]) ? 0 : (sh ? p.T : p.offsets[g + 1] - p.offsets[g]);
         return ((rows + BM - 1) / BM) * ((p.d + BN - 1) / BN);
     };
-    if (wv == 0) {
-        const int per = (G + 63) / 64;
-        const int lo = min(lane * per, G), hi = min(lo + per, G);
-        int sum = 0;
-        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            int u = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += u;
-        }
-        int run = incl - sum;
-        for (int g = lo; g < hi; ++g) {
-            s_pref[g] = run;
-            run += tiles_of(g);
-        }
-        if (lane == 63) s_pref[G] = incl;
-    }
+    if (wv == 0) wave_tile_prefix<(MOE_MAX_E + 64) / 64>(G, s_pref, tiles_of);
     __syncthreads();
     const int total = s_pref[G];
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;

@@ -179,19 +179,7 @@ __global__ void __launch_bounds__(BM * 2, 256 / BM) mxgemm(MxGemmArgs p) {
         const int nt = (MODE == MX_W13) ? (sh ? p.fs : p.f) / (BN / 2) : p.d / BN;
         return ((rows + BM - 1) / BM) * nt;
     };
-    if (wv == 0) {
-        const int per = (G + 63) / 64;
-        const int lo = min(lane * per, G), hi = min(lo + per, G);
-        int sum = 0;
-        for (int g = lo; g < hi; ++g) sum += tiles_of(g);
-        const int incl = wave_incl_scan(sum);
-        int run = incl - sum;
-        for (int g = lo; g < hi; ++g) {
-            s_pref[g] = run;
-            run += tiles_of(g);
-        }
-        if (lane == 63) s_pref[G] = incl;
-    }
+    if (wv == 0) wave_tile_prefix<(MOE_MAX_E + 64) / 64>(G, s_pref, tiles_of);
     __syncthreads();
     // workgroup b runs on XCD b % 8; XCD x takes the x-th eighth of the actual list (the grid is
     // only a bound on its length), so all eight share the work and each walks a contiguous stretch
