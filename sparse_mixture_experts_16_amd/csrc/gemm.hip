@@ -67,9 +67,9 @@ __device__ __forceinline__ int a_swz(int r) { return BK == 64 ? ((r >> 1) & 7) :
 template <int BK>
 __device__ __forceinline__ int b_swz(int n) { return BK == 64 ? ((n >> 3) & 1) : chunk_swz(n); }
 
-// 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4); a 0xFF scale gives NaN.  The NaN case is
-// a select, not a branch: a branch closes the basic block, and the compiler's wait insertion
-// then drains every LDS read in flight at it, one fragment at a time.
+// 8 E2M1 codes (one 32-bit word) -> 8 bf16 (uint4).  A 0xFF scale (NaN by the MX rule) is an
+// infinite fp32 scale here, and the scaled convert returns NaN for every code under an infinite
+// or NaN scale (checked over all 16 codes on gfx950), so the block comes out NaN with no select.
 __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     const float sc = e8m0_to_f32(s);
     uint4 r;
@@ -77,13 +77,6 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, uint32_t s) {
     r.y = cvt2(w, sc, 1);
     r.z = cvt2(w, sc, 2);
     r.w = cvt2(w, sc, 3);
-    // (the empty asm pins the converts ahead of the select, so they are not sunk under it)
-    asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
-    const bool nan = s == 255u;
-    r.x = nan ? 0x7FC07FC0u : r.x;
-    r.y = nan ? 0x7FC07FC0u : r.y;
-    r.z = nan ? 0x7FC07FC0u : r.z;
-    r.w = nan ? 0x7FC07FC0u : r.w;
     return r;
 }
 
