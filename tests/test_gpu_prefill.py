@@ -139,3 +139,27 @@ def test_prefill_c3_full_size():
     """The tokens at the first and last row of every m-tile of every expert."""
     counts = _full_size_case("c3", 8192, all_tokens=False)
     assert counts.sum() == 8192 * 6
+
+
+# An E8M0 scale byte of 0xFF makes its whole 32-element block NaN (OCP MX rule).  Planted in one
+# gate/up block of expert 0 and one down block of expert 1, the NaN must reach exactly the outputs
+# the oracle's does: every column of the tokens routed to expert 0, column 5 of those routed to
+# expert 1.  (The GEMM's expansion relies on the scaled convert returning NaN under the infinite
+# scale that byte decodes to.)
+@pytest.mark.parametrize("s", [SMALL[2], SMALL[6]], ids=lambda s: s.name)
+def test_gemm_mxfp4_nan_scale_block(s):
+    x, wr, b, _ = margin_x(s)
+    w = mi.host_experts(s)
+    sh = mi.host_experts(s, shared=True) if s.n_shared else None
+    w["w13_scale"] = w["w13_scale"].copy()
+    w["w2_scale"] = w["w2_scale"].copy()
+    w["w13_scale"][0, 3, 1] = 0xFF
+    w["w2_scale"][1, 5, 0] = 0xFF
+    wd, shd = _dev_weights(w, sh)
+    ref = oracle.layer_forward(s, x, wr, b, w, sh)
+    res = moe.layer_forward(s, dev(x), dev(wr), dev(b), wd, shd)
+    torch.cuda.synchronize()
+    out = host(res["out"])
+    np.testing.assert_array_equal(host(res["topk_idx"]), ref["topk_idx"])
+    assert np.isnan(ref["out"]).any() and not np.isnan(ref["out"]).all()
+    assert_close(out, ref["out"], what=s.name + " with NaN scale blocks")
