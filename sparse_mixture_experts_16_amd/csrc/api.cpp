@@ -240,11 +240,13 @@ int run_layer(const moe_shape* s, const void* x, const void* w_router, const flo
     int32_t* blk = at<int32_t>(ws, L.blk);
     const bool gemm = use_gemm(s);
     if (use_decode(s)) return run_decode(s, x, w_router, b, w, out, out_dtype, accumulate, idx_out, false, ws, L, mask, st);
+    RouterPartials rp{};  // the MFMA router's K-split partials are added up by the top-k kernel
     if (gemm && T > DECODE_MAX_T)
-        MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, at<float>(ws, L.y), L.ysh - L.y, st));
+        MOE_TRY(launch_route_logits_mfma(x, w_router, b, logits, T, d, E, at<float>(ws, L.y), L.ysh - L.y, st, &rp));
     else
         MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b, logits, T, d, E, st));
-    MOE_TRY(launch_route_topk(logits, T, E, k, (s->flags & MOE_F_NO_RENORM) != 0, idx, g, idx_out, st));
+    MOE_TRY(launch_route_topk(logits, T, E, k, (s->flags & MOE_F_NO_RENORM) != 0, idx, g, idx_out, st,
+                              rp.part ? &rp : nullptr));
     MOE_TRY(launch_permute(idx, P, E, GEMM_BM, counts, offsets, perm, inv, act_list, tile_off, meta, blk, st));
     if (!gemm && T <= 64 && !mask) {
         float* a = at<float>(ws, L.a);
@@ -388,18 +390,20 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
     hipStream_t st = (hipStream_t)stream;
     const int T = s->T, E = s->n_experts;
     const float* logits = logits_in;
+    RouterPartials rp{};  // the MFMA router's K-split partials are added up by the top-k kernel
     if (!logits_in) {
         float* dst = logits_out ? logits_out : at<float>(ws, L.logits);
         if (use_gemm(s) && T > DECODE_MAX_T)
             MOE_TRY(launch_route_logits_mfma(x, w_router, b_router, dst, T, s->d_model, E, at<float>(ws, L.y),
-                                             L.ysh - L.y, st));
+                                             L.ysh - L.y, st, &rp));
         else
             MOE_TRY(launch_route_logits(s->act_dtype, x, w_router, b_router, dst, T, s->d_model, E, st));
         logits = dst;
     } else if (logits_out && logits_out != logits_in) {
         MOE_TRY(hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
     }
-    MOE_TRY(launch_route_topk(logits, T, E, s->top_k, (s->flags & MOE_F_NO_RENORM) != 0, topk_idx, topk_w, nullptr, st));
+    MOE_TRY(launch_route_topk(logits, T, E, s->top_k, (s->flags & MOE_F_NO_RENORM) != 0, topk_idx, topk_w, nullptr,
+                              st, rp.part ? &rp : nullptr));
     return MOE_OK;
 }
 

@@ -802,18 +802,8 @@ static unsigned grid8(int64_t tiles) {
     return (unsigned)(g < 8 ? 8 : g);
 }
 
-// Router partial sums of a K split, added in split order (then the bias): deterministic.
-__global__ void __launch_bounds__(256) router_reduce(const float* __restrict__ part, const float* __restrict__ b,
-                                                     float* __restrict__ logits, int64_t n, int E, int ks) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        float v = 0.0f;
-        for (int q = 0; q < ks; ++q) v += part[(int64_t)q * n + i];
-        logits[i] = v + (b ? b[i % E] : 0.0f);
-    }
-}
-
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
-                                    int E, float* part, size_t part_bytes, hipStream_t st) {
+                                    int E, float* part, size_t part_bytes, hipStream_t st, RouterPartials* rp) {
     // T/128 x E/128 tiles alone leave most CUs idle: split K (>= 4 steps of 32 each) over up to 8
     // workgroups when the partials fit the scratch given, but not beyond one round of the device's
     // workgroup slots (two per CU): a second round and its larger partials cost more than they
@@ -836,11 +826,7 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     p.T = T; p.d = d; p.E = E; p.k = 1;
     p.ksplit = ks;
     hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false, 2>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || ks == 1) return e;
-    const int64_t n = (int64_t)T * E;
-    const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(router_reduce, dim3(grid), dim3(256), 0, st, part, b, logits, n, E, ks);
+    *rp = RouterPartials{ks > 1 ? part : nullptr, ks, b, logits};
     return hipGetLastError();
 }
 

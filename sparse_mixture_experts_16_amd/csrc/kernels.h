@@ -7,7 +7,7 @@
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 64
 #define PERMUTE_SMALL_MAX 4096
-#define PERMUTE_SCAN_LDS 16384  // chunk counts (ints) the one-workgroup scan holds in LDS
+#define PERMUTE_MAX_COUNTS 16384  // chunk counts (nblk x E ints) every scatter workgroup reads
 #define GEMM_BM 128  // token rows per grouped-GEMM tile (tile list granularity)
 
 namespace moe {
@@ -15,7 +15,7 @@ namespace moe {
 // Pairs per chunk of the large-P permute: as many chunks as the scan can hold in LDS (at most
 // 256), each a multiple of 64 pairs (one wavefront scatters a chunk).
 inline int permute_chunk(int64_t P, int E) {
-    int64_t nmax = PERMUTE_SCAN_LDS / (E > 0 ? E : 1);
+    int64_t nmax = PERMUTE_MAX_COUNTS / (E > 0 ? E : 1);
     if (nmax > 256) nmax = 256;
     if (nmax < 1) nmax = 1;
     int64_t c = (P + nmax - 1) / nmax;
@@ -36,11 +36,22 @@ void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop);
 
 hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
                                int T, int d, int E, hipStream_t st);
-// part: scratch for the K-split partial sums (part_bytes of it; 0 = no split)
+// The MFMA router's K-split partial sums, left for the top-k kernel to add up (in split order,
+// then the bias) into `logits`.
+struct RouterPartials {
+    const float* part;  // ks x [T, E]
+    int ks;
+    const float* bias;  // [E] or null
+    float* logits;      // [T, E]: receives the summed logits
+};
+// part: scratch for the K-split partial sums (part_bytes of it; 0 = no split).  A split leaves
+// the partials for launch_route_topk, described in *rp (rp->part null: no split, and logits
+// already holds the logits).
 hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* b, float* logits, int T, int d,
-                                    int E, float* part, size_t part_bytes, hipStream_t st);
+                                    int E, float* part, size_t part_bytes, hipStream_t st, RouterPartials* rp);
+// rp (nullable): form the logits from the router GEMM's partial sums first (logits is then unused)
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, bool no_renorm, int32_t* idx, float* w,
-                             int32_t* idx2, hipStream_t st);
+                             int32_t* idx2, hipStream_t st, const RouterPartials* rp = nullptr);
 
 hipError_t launch_permute(const int32_t* idx, int P, int E, int bm, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, int32_t* act_list, int32_t* tile_off, int32_t* meta,

@@ -1,5 +1,6 @@
 // Grouping tokens by expert: a stable counting sort of the flat (token, slot) pairs
-// p = t*k + j by expert id, with an LDS histogram, a prefix scan and a stable scatter.
+// p = t*k + j by expert id, with an LDS histogram, a prefix scan and a stable scatter
+// (large batches: per-chunk histograms, then one kernel that scans and scatters).
 //
 // At prefill thousands of tokens reach nearly every expert (dothoosh.com FreeToken article,
 // "FreeToken architecture and the sparsity puzzle", first failure mode), so the sort must
@@ -16,7 +17,8 @@ namespace moe {
 
 // Wave 0 of the block: from LDS counts s_cnt[0..E), write counts/offsets, the ascending list of
 // experts with tokens, the per-expert tile offsets (ceil(count/bm) tiles each) and meta
-// (meta[0] = active experts, meta[1] = tiles); leaves s_cur[e] = offsets[e].
+// (meta[0] = active experts, meta[1] = tiles); leaves s_cur[e] = offsets[e].  Lane l handles
+// experts l*per .. l*per+per-1 (per = ceil(E/64)).  Null outputs are skipped.
 __device__ void scan_counts_wave0(const int* s_cnt, int* s_cur, int E, int bm, int32_t* counts, int32_t* offsets,
                                   int32_t* act_list, int32_t* tile_off, int32_t* meta) {
     const int lane = lane_id();
@@ -35,16 +37,19 @@ __device__ void scan_counts_wave0(const int* s_cnt, int* s_cur, int E, int bm, i
         if (counts) counts[e] = c;
         if (offsets) offsets[e] = pc;
         if (s_cur) s_cur[e] = pc;
-        tile_off[e] = pt;
-        if (c > 0) act_list[pa++] = e;
+        if (tile_off) tile_off[e] = pt;
+        if (c > 0 && act_list) act_list[pa] = e;
+        pa += (c > 0);
         pc += c;
         pt += (c + bm - 1) / bm;
     }
     if (lane == MOE_WAVE - 1) {
         if (offsets) offsets[E] = pc;
-        tile_off[E] = pt;
-        meta[0] = pa;
-        meta[1] = pt;
+        if (tile_off) tile_off[E] = pt;
+        if (meta) {
+            meta[0] = pa;
+            meta[1] = pt;
+        }
     }
 }
 
@@ -115,77 +120,65 @@ __global__ void __launch_bounds__(256) permute_hist(const int32_t* __restrict__ 
     for (int e = threadIdx.x; e < E; e += blockDim.x) blk[(int64_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// Large P, pass 2 (one workgroup): totals, offsets, lists, and each chunk's starting cursor
-// blk[b][e] = offsets[e] + (pairs of expert e in chunks before b).  The nblk x E counts are
-// staged in LDS with coalesced loads; each expert's chunks are split into segments, one thread
-// per (expert, segment) sums its segment, the segment sums are scanned per expert, and each
-// thread writes its chunks' running sums.
-__global__ void __launch_bounds__(1024) permute_scan(int32_t* __restrict__ blk, int nblk, int E, int bm,
-                                                     int32_t* counts, int32_t* offsets, int32_t* act_list,
-                                                     int32_t* tile_off, int32_t* meta) {
-    __shared__ int s_blk[PERMUTE_SCAN_LDS];
-    __shared__ int s_seg[1024];
-    __shared__ int s_cnt[MOE_MAX_E];
+// Large P, pass 2: one workgroup per chunk.  Every workgroup reads all nblk x E chunk counts
+// (consecutive threads take consecutive experts, so the reads are coalesced) and forms each
+// expert's total and the part of it in the chunks before its own; wave 0 scans the totals into
+// the expert offsets, adds its chunk's prefix, and scatters the chunk's pairs stably from
+// there.  Workgroup 0 also writes counts, offsets, the active-expert list, tile offsets and
+// meta.  (Integer sums: the LDS atomics that gather the partial sums cannot change them.)
+constexpr int PERMUTE_SCATTER_THREADS = 512;
+constexpr int PERMUTE_BATCH = 32;  // chunk counts per thread in flight at once
+__global__ void __launch_bounds__(PERMUTE_SCATTER_THREADS) permute_scatter(
+    const int32_t* __restrict__ idx, int P, int E, int chunk, int nblk, int bm, const int32_t* __restrict__ blk,
+    int32_t* counts, int32_t* offsets, int32_t* act_list, int32_t* tile_off, int32_t* meta,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int s_tot[MOE_MAX_E];
+    __shared__ int s_pre[MOE_MAX_E];
     __shared__ int s_cur[MOE_MAX_E];
-    const int n = nblk * E;
-    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * blockDim.x) {  // 8 loads in flight per thread
-        int v[8];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) {
+        s_tot[e] = 0;
+        s_pre[e] = 0;
+    }
+    __syncthreads();
+    // (expert, part) items: each part covers a contiguous run of L chunks of one expert
+    const int np = E >= (int)blockDim.x ? 1 : (int)blockDim.x / E;
+    const int L = (nblk + np - 1) / np;
+    for (int s = tid; s < E * np; s += blockDim.x) {
+        const int e = s % E, q0 = (s / E) * L, q1 = min(q0 + L, nblk);
+        int tot = 0, pre = 0;
+        for (int qb = q0; qb < q1; qb += PERMUTE_BATCH) {
+            int c[PERMUTE_BATCH];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = i0 + j * blockDim.x;
-            v[j] = i < n ? blk[i] : 0;
-        }
+            for (int j = 0; j < PERMUTE_BATCH; ++j) {
+                const int q = qb + j;
+                c[j] = q < q1 ? blk[(int64_t)q * E + e] : 0;
+            }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = i0 + j * blockDim.x;
-            if (i < n) s_blk[i] = v[j];
+            for (int j = 0; j < PERMUTE_BATCH; ++j) {
+                tot += c[j];
+                pre += (qb + j < b) ? c[j] : 0;
+            }
+        }
+        if (np == 1) {
+            s_tot[e] = tot;
+            s_pre[e] = pre;
+        } else {
+            atomicAdd(&s_tot[e], tot);
+            atomicAdd(&s_pre[e], pre);
         }
     }
-    const int nseg = E >= (int)blockDim.x ? 1 : (int)blockDim.x / E;
-    const int seg_len = (nblk + nseg - 1) / nseg;
     __syncthreads();
-    for (int t = threadIdx.x; t < E * nseg; t += blockDim.x) {
-        const int e = t % E, sg = t / E;
-        const int b0 = sg * seg_len, b1 = min(b0 + seg_len, nblk);
-        int sum = 0;
-        for (int b = b0; b < b1; ++b) sum += s_blk[b * E + e];
-        s_seg[t] = sum;
+    if (wave_id() == 0) {
+        const bool first = b == 0;
+        scan_counts_wave0(s_tot, s_cur, E, bm, first ? counts : nullptr, first ? offsets : nullptr,
+                          first ? act_list : nullptr, first ? tile_off : nullptr, first ? meta : nullptr);
+        // the lane that wrote s_cur[e] (experts lane*per ..) adds this chunk's prefix
+        const int per = (E + MOE_WAVE - 1) / MOE_WAVE, lo = min(lane_id() * per, E), hi = min(lo + per, E);
+        for (int e = lo; e < hi; ++e) s_cur[e] += s_pre[e];
+        const int p0 = b * chunk, p1 = min(p0 + chunk, P);
+        stable_scatter_wave(idx, p0, p1, bits_for(E), E, s_cur, perm, inv);
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int run = 0;
-        for (int sg = 0; sg < nseg; ++sg) {
-            const int c = s_seg[sg * E + e];
-            s_seg[sg * E + e] = run;
-            run += c;
-        }
-        s_cnt[e] = run;
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < E * nseg; t += blockDim.x) {
-        const int e = t % E, sg = t / E;
-        const int b0 = sg * seg_len, b1 = min(b0 + seg_len, nblk);
-        int run = s_seg[t];
-        for (int b = b0; b < b1; ++b) {
-            const int c = s_blk[b * E + e];
-            s_blk[b * E + e] = run;
-            run += c;
-        }
-    }
-    if (wave_id() == 0) scan_counts_wave0(s_cnt, s_cur, E, bm, counts, offsets, act_list, tile_off, meta);
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) blk[i] = s_blk[i] + s_cur[i % E];
-}
-
-// Large P, pass 3: one wavefront per chunk scatters its pairs stably from its cursors.
-__global__ void __launch_bounds__(64) permute_scatter(const int32_t* __restrict__ idx, int P, int E, int chunk,
-                                                      const int32_t* __restrict__ blk, int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ inv) {
-    __shared__ int s_cur[MOE_MAX_E];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) s_cur[e] = blk[(int64_t)blockIdx.x * E + e];
-    __syncthreads();
-    const int p0 = blockIdx.x * chunk, p1 = min(p0 + chunk, P);
-    stable_scatter_wave(idx, p0, p1, bits_for(E), E, s_cur, perm, inv);
 }
 
 // From caller-provided offsets (moe_grouped_ffn): the active-expert list, tile offsets, meta.
@@ -217,9 +210,8 @@ hipError_t launch_permute(const int32_t* idx, int P, int E, int bm, int32_t* cou
     const int chunk = permute_chunk(P, E);
     const int nblk = (P + chunk - 1) / chunk;
     hipLaunchKernelGGL(permute_hist, dim3(nblk), dim3(256), 0, st, idx, P, E, chunk, blk);
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, st, blk, nblk, E, bm, counts, offsets, act_list,
-                       tile_off, meta);
-    hipLaunchKernelGGL(permute_scatter, dim3(nblk), dim3(64), 0, st, idx, P, E, chunk, blk, perm, inv);
+    hipLaunchKernelGGL(permute_scatter, dim3(nblk), dim3(PERMUTE_SCATTER_THREADS), 0, st, idx, P, E, chunk, nblk, bm,
+                       blk, counts, offsets, act_list, tile_off, meta, perm, inv);
     return hipGetLastError();
 }
 

@@ -70,16 +70,50 @@ __global__ void __launch_bounds__(256) route_logits_gemv(const A* __restrict__ x
 // Top-k + gates: one wavefront per token.  Lane l holds the EPL logits of experts l*EPL ..
 // l*EPL+EPL-1 as order-preserving 32-bit keys (NaN lowest, -0 equal to +0); k rounds of a
 // wave-wide max, ties to the lowest expert, pick the experts in selection order.
+// With `part` (the router GEMM's ks K-split partial sums, ks x [T, E]) the logits are formed
+// here first -- the partials added in split order, then the bias -- and stored to `logits`.
 // ------------------------------------------------------------------------------------------------
 template <int EPL>
-__global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logits, int T, int E, int k,
+__global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logits_in, const float* __restrict__ part,
+                                                  int ks, const float* __restrict__ bias,
+                                                  float* __restrict__ logits_out, int T, int E, int k,
                                                   uint32_t no_renorm, int32_t* __restrict__ idx_out,
                                                   float* __restrict__ w_out, int32_t* __restrict__ idx_out2) {
-    const int t = blockIdx.x * 4 + wave_id();
+    __shared__ float s_row[4][EPL * MOE_WAVE];
+    const int wv = wave_id();
+    const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
     const int lane = lane_id();
-    const float* l = logits + (int64_t)t * E;
+    float* l = s_row[wv];
     uint32_t key[EPL];
+    if (part) {
+        const int64_t n = (int64_t)T * E;
+        float v[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) v[j] = 0.0f;
+        for (int q = 0; q < ks; ++q) {
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                const int e = lane * EPL + j;
+                if (e < E) v[j] += part[(int64_t)q * n + (int64_t)t * E + e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane * EPL + j;
+            if (e < E) {
+                const float lv = v[j] + (bias ? bias[e] : 0.0f);
+                logits_out[(int64_t)t * E + e] = lv;
+                l[e] = lv;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane * EPL + j;
+            if (e < E) l[e] = logits_in[(int64_t)t * E + e];
+        }
+    }
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int e = lane * EPL + j;
@@ -91,13 +125,13 @@ __global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logi
     const float term = (lane < k) ? expf(l[my_sel] - m) : 0.0f;
     float den;
     if (no_renorm) {
-        float part = 0.0f;
+        float sum = 0.0f;
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
             const int e = lane * EPL + j;
-            if (e < E) part += expf(l[e] - m);
+            if (e < E) sum += expf(l[e] - m);
         }
-        den = wave_sum(part);
+        den = wave_sum(sum);
     } else {
         den = wave_sum(term);
     }
@@ -124,19 +158,21 @@ hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, con
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, bool no_renorm, int32_t* idx, float* w,
-                             int32_t* idx2, hipStream_t st) {
+                             int32_t* idx2, hipStream_t st, const RouterPartials* rp) {
     dim3 grid((T + 3) / 4), block(256);
-    uint32_t nr = no_renorm ? 1u : 0u;
-    if (E <= 64)
-        hipLaunchKernelGGL((route_topk<1>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
-    else if (E <= 128)
-        hipLaunchKernelGGL((route_topk<2>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
-    else if (E <= 256)
-        hipLaunchKernelGGL((route_topk<4>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
-    else if (E <= 512)
-        hipLaunchKernelGGL((route_topk<8>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
-    else
-        hipLaunchKernelGGL((route_topk<16>), grid, block, 0, st, logits, T, E, k, nr, idx, w, idx2);
+    const uint32_t nr = no_renorm ? 1u : 0u;
+    const float* part = rp ? rp->part : nullptr;
+    const int ks = rp ? rp->ks : 1;
+    const float* bias = rp ? rp->bias : nullptr;
+    float* lout = rp ? rp->logits : nullptr;
+#define MOE_TOPK(EPLV) \
+    hipLaunchKernelGGL((route_topk<EPLV>), grid, block, 0, st, logits, part, ks, bias, lout, T, E, k, nr, idx, w, idx2)
+    if (E <= 64) MOE_TOPK(1);
+    else if (E <= 128) MOE_TOPK(2);
+    else if (E <= 256) MOE_TOPK(4);
+    else if (E <= 512) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
     return hipGetLastError();
 }
 
