@@ -518,6 +518,166 @@ __device__ __forceinline__ void a_chunk(const float* row, int ncp, int c, float 
 template <int WT> struct DecAct { using T = uint16_t; };
 template <> struct DecAct<0> { using T = float; };
 
+// One token, every picked expert taken (no expert mask, renormalised gates, E <= 256) and one
+// K step per row: every wavefront runs the top-k itself on the logits in its registers, and
+// issues its first item's weight loads as soon as the round that picks that item's expert is
+// done -- a shared-expert item's right away, since the routing does not decide it -- instead of
+// after the whole workgroup's routing and its barrier.  Where an item's output row goes (its
+// sorted position: the number of picks with a lower expert id) is known once all k rounds are
+// done, while those loads are in flight.  Selections, gates, the published table and every
+// row's arithmetic are those of the general path (dec_route_one and the item loop).
+template <int WT, int R, int U, int KPL>
+__device__ void dec_w13_one(const DecFfnArgs& p, DecRoute& rs, unsigned char* dyn_lds) {
+    using W = WChunk<WT>;
+    constexpr int EC = W::EC;
+    const int lane = lane_id(), wv = wave_id();
+    const int E = p.rt.E, k = p.rt.k;
+    const int ngr = (p.f + R - 1) / R, ngs = (p.fs + R - 1) / R;
+    const int NC = p.d / EC;
+    const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
+    const int NWB = blockDim.x / MOE_WAVE;
+    const bool shared_on = p.rt.n_shared != 0;
+    const int s_items = shared_on ? ngs : 0;
+    const int n_items = s_items + k * ngr;
+    const int stride = gridDim.x * NWB;
+    const int item0 = blockIdx.x * NWB + wv;
+
+    // the logits first: the waits for them leave the item loads issued below in flight
+    float lg[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int e = lane * KPL + j;
+        lg[j] = e < E ? p.rt.logits[e] : 0.0f;
+    }
+    W wg[R][U], wu[R][U];
+    auto issue = [&](int item, int ex) {
+        const bool sh = item < s_items;
+        const int fc = sh ? p.fs : p.f;
+        const int j0 = (sh ? item : (item - s_items) % ngr) * R;
+        const uint8_t* wb = sh ? p.s13 : p.w13 + (int64_t)ex * 2 * p.f * rb;
+        const uint8_t* sbp = (WT >= 2) ? (sh ? p.s13s : p.w13s + (int64_t)ex * 2 * p.f * sb) : nullptr;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = lane + MOE_WAVE * u, j = j0 + r;
+                if (c < NC && j < fc) {
+                    wg[r][u].load(wb + (int64_t)j * rb, sbp ? sbp + (int64_t)j * sb : nullptr, c);
+                    wu[r][u].load(wb + (int64_t)(fc + j) * rb, sbp ? sbp + (int64_t)(fc + j) * sb : nullptr, c);
+                } else {
+                    wg[r][u].zero();
+                    wu[r][u].zero();
+                }
+            }
+    };
+    const bool has = item0 < n_items;
+    if (has && item0 < s_items) issue(item0, E);
+    const int r0 = (has && item0 >= s_items) ? (item0 - s_items) / ngr : -1;
+
+    // top-k on order-preserving keys, k rounds of a wave-wide max (ties to the lowest expert):
+    // lane r keeps pick r
+    uint32_t key[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) key[j] = lane * KPL + j < E ? sel_ord(lg[j]) : 0u;
+    int mine = 0;
+    for (int r = 0; r < k; ++r) {
+        uint32_t lb = 0u;
+        int lj = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if (key[j] > lb) {
+                lb = key[j];
+                lj = j;
+            }
+        const uint32_t m = wave_max_u32(lb);
+        const uint64_t bal = __ballot(lb == m);
+        const int wl = __ffsll((unsigned long long)bal) - 1;
+        const int wj = __builtin_amdgcn_readlane(lj, wl);
+        if (lane == wl) {
+#pragma unroll
+            for (int j = 0; j < KPL; ++j)
+                if (j == wj) key[j] = 0u;
+        }
+        const int pk = wl * KPL + wj;
+        if (lane == r) mine = pk;
+        if (r == r0) issue(item0, pk);
+    }
+    // a pick's sorted position: the number of picks with a lower expert id
+    auto pos_of = [&](int ex) { return __popcll(__ballot(lane < k && mine < ex)); };
+
+    // workgroup 0 keeps what it publishes at the end: picks, gates, the slot table (one token:
+    // slot = sorted position), the shared slot last
+    if (blockIdx.x == 0 && wv == 0) {
+        int4* s_slot = reinterpret_cast<int4*>(dyn_lds);
+        float* s_logits = reinterpret_cast<float*>(dyn_lds + (size_t)(E + 1) * 16);
+        float* s_gate = s_logits + E;
+        int* s_sel = reinterpret_cast<int*>(s_gate + k);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+            const int e = lane * KPL + j;
+            if (e < E) s_logits[e] = lg[j];
+        }
+        const bool pick = lane < k;
+        const float m = s_logits[__builtin_amdgcn_readlane(mine, 0)];
+        const float term = pick ? expf(s_logits[mine] - m) : 0.0f;
+        const float den = wave_sum(term);
+        int pos = 0;
+        for (int j = 0; j < k; ++j) pos += __builtin_amdgcn_readlane(mine, j) < mine;
+        if (pick) {
+            s_sel[lane] = mine;
+            s_gate[lane] = term / den;
+            s_slot[pos] = make_int4(mine, pos, 1, 1);
+        }
+        if (lane == 0) {
+            rs.n_routed = k;
+            rs.n_slots = k + (shared_on ? 1 : 0);
+            if (shared_on) s_slot[k] = make_int4(E, k, 1, 1);
+        }
+    }
+
+    // the items: gate/up dot products of the loaded rows, SwiGLU, the output row at its position
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(p.x);
+    for (int item = item0; item < n_items; item += stride) {
+        const bool sh = item < s_items;
+        const int ex = sh ? E : __builtin_amdgcn_readlane(mine, (item - s_items) / ngr);
+        if (item != item0) issue(item, ex);
+        const int fc = sh ? p.fs : p.f;
+        const int j0 = (sh ? item : (item - s_items) % ngr) * R;
+        const int pos = sh ? k : pos_of(ex);
+        const float gsc = sh ? p.gs13 : p.g13;
+        float ag[R], au[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) ag[r] = au[r] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = lane + MOE_WAVE * u;
+            if (c < NC) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if constexpr (WT == 0) {
+                        const float* xf = reinterpret_cast<const float*>(p.x);
+                        ag[r] = wg[r][u].dot_f32(xf + (int64_t)c * EC, ag[r]);
+                        au[r] = wu[r][u].dot_f32(xf + (int64_t)c * EC, au[r]);
+                    } else {
+                        ag[r] = wg[r][u].dot_bf16(xr + (int64_t)c * EC, ag[r]);
+                        au[r] = wu[r][u].dot_bf16(xr + (int64_t)c * EC, au[r]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float g = wave_sum(ag[r]) * gsc, u = wave_sum(au[r]) * gsc;
+            const int j = j0 + r;
+            if (lane == 0 && j < fc) p.a[(int64_t)pos * p.fmax + a_off<EC>(j, p.fmax / EC)] = g / (1.0f + expf(-g)) * u;
+        }
+    }
+    if (blockIdx.x == 0) {
+        __syncthreads();
+        dec_route_publish(p.rt, rs);
+    }
+}
+
 template <int WT, int R, int U, int TQ>
 __global__ void __launch_bounds__(512, (WT == 1 && TQ == 1) ? 8 : 1) dec_w13(DecFfnArgs p) {
     using W = WChunk<WT>;
@@ -531,6 +691,22 @@ __global__ void __launch_bounds__(512, (WT == 1 && TQ == 1) ? 8 : 1) dec_w13(Dec
     const int64_t rb = row_bytes(WT, p.d), sb = scale_row_bytes(WT, p.d);
     const int nsteps = (NC + MOE_WAVE * U - 1) / (MOE_WAVE * U);
     const int NWB = blockDim.x / MOE_WAVE;
+    if constexpr (TQ == 1) {
+        if (p.rt.T == 1 && !p.rt.emask && !p.rt.no_renorm && p.rt.E <= 256 && nsteps == 1) {
+            {
+                // the routing struct's table, gate and pick arrays, as dec_route_publish reads them
+                unsigned char* q = dyn_lds;
+                rs.slot = reinterpret_cast<int4*>(q); q += (size_t)(p.rt.E + 1) * 16;
+                q += (size_t)p.rt.E * 4;
+                rs.gate = reinterpret_cast<float*>(q); q += (size_t)p.rt.k * 4;
+                rs.sel = reinterpret_cast<int*>(q);
+            }
+            if (p.rt.E <= 64) dec_w13_one<WT, R, U, 1>(p, rs, dyn_lds);
+            else if (p.rt.E <= 128) dec_w13_one<WT, R, U, 2>(p, rs, dyn_lds);
+            else dec_w13_one<WT, R, U, 4>(p, rs, dyn_lds);
+            return;
+        }
+    }
     // The shared expert does not depend on the routing, so its items come first: a wavefront
     // whose first item is one touches the 64-byte pieces of that item's rows (one dword each,
     // the first NP * 4 KB of a row) while its workgroup routes -- after the logits are in LDS,
