@@ -12,7 +12,8 @@ several copies of the layer's weights (like successive layers of a model), so th
 256 MB Infinity Cache cannot serve repeated weight reads.
 
 Timing: hipEvents on the stream the library launches on (torch's current stream).
-Pass 1 times K steps end to end (value, ms_per_step).  Pass 2 repeats K steps with the
+Pass 1 times K steps end to end (value, ms_per_step), with events between five consecutive
+groups of the steps for the median of five repeats (ms_per_step_median_of_5).  Pass 2 repeats K steps with the
 library's timing hook bracketing the gate/up FFN kernel (the largest share of the
 layer's bytes and flops) to get that kernel's average duration for the roofline; pass 3
 does the same for the down projection.  The device's own peaks (an HBM read stream, the
@@ -194,8 +195,13 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
+REPEATS = 5  # the timed steps are split into this many consecutive groups for the median
+
+
 def _timed(hip, stream, step, steps, warmup, profile=None):
-    """Run warmup + timed steps; returns total ms (and per-step kernel ms if profiling)."""
+    """Run warmup + timed steps.  Unprofiled: (total ms, ms per step of each of REPEATS
+    consecutive groups of the steps, events between groups).  Profiled: (None, per-step ms of
+    the profiled kernel)."""
     import torch
     import sparse_mixture_experts_16_amd as moe
     for i in range(warmup):
@@ -203,16 +209,19 @@ def _timed(hip, stream, step, steps, warmup, profile=None):
     torch.cuda.synchronize()
     kern = []
     if profile is None:
-        e0, e1 = hip.event(), hip.event()
-        hip.record(e0, stream)
+        cuts = sorted({steps * g // REPEATS for g in range(REPEATS + 1)})
+        evs = [hip.event() for _ in cuts]
+        hip.record(evs[0], stream)
         for i in range(steps):
             step(warmup + i)
-        hip.record(e1, stream)
+            if i + 1 in cuts:
+                hip.record(evs[cuts.index(i + 1)], stream)
         torch.cuda.synchronize()
-        total = hip.elapsed_ms(e0, e1)
-        hip.destroy(e0)
-        hip.destroy(e1)
-        return total, kern
+        total = hip.elapsed_ms(evs[0], evs[-1])
+        groups = [hip.elapsed_ms(evs[g], evs[g + 1]) / (cuts[g + 1] - cuts[g]) for g in range(len(cuts) - 1)]
+        for e in evs:
+            hip.destroy(e)
+        return total, groups
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
     for i in range(steps):
         moe.profile_kernel(profile, evs[i][0], evs[i][1])
@@ -260,7 +269,7 @@ def run_layer_workload(hip, name, steps, warmup):
         moe.layer_forward_raw(shape, x_pool[i % n_batches], wr, b, W, out,
                               idx_log[log, :T * s.k] if log is not None else None, ws)
 
-    total, _ = _timed(hip, stream, step, steps, warmup)
+    total, groups = _timed(hip, stream, step, steps, warmup)
     _, k_up = _timed(hip, stream, lambda i: step(i, log=(i - warmup) if i >= warmup else None), steps, warmup,
                      profile=moe.KERNEL_FFN_UP)
     _, k_down = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_DOWN)
@@ -273,6 +282,7 @@ def run_layer_workload(hip, name, steps, warmup):
     sh_up, sh_down = expert_bytes(s, s.f_shared) if s.n_shared else (0, 0)
     ms = total / steps
     rec = dict(workload=name, desc=desc, T=T, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3),
+               ms_per_step_median_of_5=float(np.median(groups)),
                ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3) if k_down else None,
                experts_hit_per_step=float(uniq.mean()),
                experts_never_hit=int((counts == 0).sum()), load_max_over_mean=float(counts.max() / counts.mean()))
@@ -345,7 +355,7 @@ def run_stack_workload(hip, steps, warmup, persistent=False):
         h.copy_(h0[i % POOL].view(1, -1))
         graph.replay()
 
-    total, _ = _timed(hip, stream, step_graph, steps, warmup)
+    total, groups = _timed(hip, stream, step_graph, steps, warmup)
     # the timing hook's events ride on eager launches
     _, k_up = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_UP)
     _, k_down = _timed(hip, stream, step, steps, warmup, profile=moe.KERNEL_FFN_DOWN)
@@ -354,6 +364,7 @@ def run_stack_workload(hip, steps, warmup, persistent=False):
     # T = 1, k = 6 distinct experts per layer
     layer_bytes = s.k * (up_b + down_b)
     rec = dict(workload="c4_stack", desc=WORKLOADS["c4_stack"][3], T=1, ms_per_step=ms, tokens_per_s=1.0 / (ms * 1e-3),
+               ms_per_step_median_of_5=float(np.median(groups)),
                bound="hbm", alg_bytes_per_step=float(layer_bytes * s.n_layers),
                step_GBps=layer_bytes * s.n_layers / (ms * 1e-3) / 1e9,
                ffn_up_us=float(np.mean(k_up) * 1e3), ffn_down_us=float(np.mean(k_down) * 1e3) if k_down else None)
@@ -379,7 +390,7 @@ def _run_stack_persistent(hip, steps, warmup, s, shape, h, h0, wrs, bs, Ws, keep
         h.copy_(h0[i % POOL].view(1, -1))
         moe.stack_forward_persistent(shape, h, wrs, bs, Ws, pws)
 
-    total, _ = _timed(hip, stream, step, steps, warmup)
+    total, groups = _timed(hip, stream, step, steps, warmup)
     if moe.stack_persistent_status(pws) != 0:
         raise RuntimeError("persistent stack: a grid-barrier wait ran out")
     ms = total / steps
@@ -387,6 +398,7 @@ def _run_stack_persistent(hip, steps, warmup, s, shape, h, h0, wrs, bs, Ws, keep
     layer_bytes = s.k * (up_b + down_b)
     step_bytes = float(layer_bytes * s.n_layers)
     rec = dict(workload="c4_stack_persistent", desc=WORKLOADS["c4_stack_persistent"][3], T=1, ms_per_step=ms,
+               ms_per_step_median_of_5=float(np.median(groups)),
                tokens_per_s=1.0 / (ms * 1e-3), bound="hbm", alg_bytes_per_step=step_bytes,
                step_GBps=step_bytes / (ms * 1e-3) / 1e9)
     rec["step_frac_hbm"] = rec["step_GBps"] / HBM_PEAK_GBS
@@ -670,7 +682,8 @@ def main():
     line = {
         "metric": "MoE-layer tokens/s; decode HBM GB/s % peak; prefill MFMA util %",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median_of_5": head.get("ms_per_step_median_of_5"), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": head["desc"], "name": head["workload"], "T": head["T"],
                    **{key: head[key] for key in ("experts_hit_per_step", "step_GBps", "step_frac_hbm",

@@ -49,6 +49,20 @@ def assert_close(got, ref, rel: float = 2e-2, abs_of_rms: float = 1e-2, what: st
     return max_abs, max_rel
 
 
+def assert_literal(got, ref, what: str = ""):
+    """The layer specification's bound read literally, |got - ref| <= 1e-2 + 2e-2 * |ref| (an
+    absolute 1e-2), for workloads whose outputs are of order one (the bf16 128-expert layers);
+    NaN positions must agree.  Prints the largest error relative to that bound."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape and np.array_equal(np.isnan(got), np.isnan(ref)), what
+    fin = np.isfinite(ref)
+    ratio = np.abs(got[fin] - ref[fin]) / (1e-2 + 2e-2 * np.abs(ref[fin]))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    print(f"{what}: largest error / literal bound (1e-2 + 2e-2|ref|) {worst:.3e}", flush=True)
+    assert worst <= 1.0, f"{what}: outside the literal bound 1e-2 + 2e-2*|ref| (ratio {worst:.3e})"
+
+
 def ref_select(l: np.ndarray, k: int):
     """Brute-force selection: full stable sort of experts by (-logit, index) with NaN last."""
     E = len(l)

@@ -17,7 +17,7 @@ import pytest
 import moe_inputs as mi
 import oracle
 from _gpu import dev, host, margin_x, oracle_on_tokens, tile_boundary_tokens
-from _helpers import assert_close
+from _helpers import assert_close, assert_literal
 
 torch = pytest.importorskip("torch")
 moe = pytest.importorskip("sparse_mixture_experts_16_amd")
@@ -119,6 +119,8 @@ def _full_size_case(name, T, all_tokens):
     print(f"{name}: largest error / bound {ratio.max():.3f}; {int((ratio > 0.5).sum())} elements above half the bound",
           flush=True)
     assert_close(got, want, what=f"{name} out")
+    if name.startswith("c2"):
+        assert_literal(got, want, what=f"{name} out")
     return counts
 
 
