@@ -815,7 +815,7 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     const int64_t slots = 2 * (int64_t)cus;
     const int64_t tiles = (int64_t)((T + TBM - 1) / TBM) * ((E + 127) / 128);
     int ks = 1;
-    while (ks < 8 && tiles * ks * 2 <= slots && d % (32 * ks * 2) == 0 && d / (ks * 2) >= 128 &&
+    while (ks < ROUTER_MAX_SPLIT && tiles * ks * 2 <= slots && d % (32 * ks * 2) == 0 && d / (ks * 2) >= 128 &&
            (size_t)ks * 2 * T * E * 4 <= part_bytes)
         ks *= 2;
     GemmArgs p{};

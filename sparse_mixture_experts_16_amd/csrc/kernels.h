@@ -37,7 +37,8 @@ void prof_events(int cls, hipEvent_t* start, hipEvent_t* stop);
 hipError_t launch_route_logits(int act_dtype, const void* x, const void* wr, const float* b, float* logits,
                                int T, int d, int E, hipStream_t st);
 // The MFMA router's K-split partial sums, left for the top-k kernel to add up (in split order,
-// then the bias) into `logits`.
+// then the bias) into `logits`; at most ROUTER_MAX_SPLIT of them.
+#define ROUTER_MAX_SPLIT 8
 struct RouterPartials {
     const float* part;  // ks x [T, E]
     int ks;

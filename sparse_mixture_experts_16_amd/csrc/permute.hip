@@ -123,10 +123,13 @@ __global__ void __launch_bounds__(256) permute_hist(const int32_t* __restrict__ 
 // Large P, pass 2: one workgroup per chunk.  Every workgroup reads all nblk x E chunk counts
 // (consecutive threads take consecutive experts, so the reads are coalesced) and forms each
 // expert's total and the part of it in the chunks before its own; wave 0 scans the totals into
-// the expert offsets, adds its chunk's prefix, and scatters the chunk's pairs stably from
-// there.  Workgroup 0 also writes counts, offsets, the active-expert list, tile offsets and
-// meta.  (Integer sums: the LDS atomics that gather the partial sums cannot change them.)
+// the expert offsets and adds its chunk's prefix.  The chunk is cut into one contiguous piece
+// per wavefront; each wavefront counts its piece's pairs per expert, the counts are turned into
+// per-piece cursors (the pieces in order), and every wavefront scatters its piece stably from
+// its own cursors.  Workgroup 0 also writes counts, offsets, the active-expert list, tile
+// offsets and meta.  (Integer sums: the LDS atomics that gather them cannot change them.)
 constexpr int PERMUTE_SCATTER_THREADS = 512;
+constexpr int PERMUTE_WAVES = PERMUTE_SCATTER_THREADS / MOE_WAVE;
 constexpr int PERMUTE_BATCH = 32;  // chunk counts per thread in flight at once
 __global__ void __launch_bounds__(PERMUTE_SCATTER_THREADS) permute_scatter(
     const int32_t* __restrict__ idx, int P, int E, int chunk, int nblk, int bm, const int32_t* __restrict__ blk,
@@ -135,11 +138,13 @@ __global__ void __launch_bounds__(PERMUTE_SCATTER_THREADS) permute_scatter(
     __shared__ int s_tot[MOE_MAX_E];
     __shared__ int s_pre[MOE_MAX_E];
     __shared__ int s_cur[MOE_MAX_E];
-    const int tid = threadIdx.x, b = blockIdx.x;
+    __shared__ int s_wcur[PERMUTE_WAVES][MOE_MAX_E];  // per-piece counts, then cursors
+    const int tid = threadIdx.x, b = blockIdx.x, wv = wave_id(), lane = lane_id();
     for (int e = tid; e < E; e += blockDim.x) {
         s_tot[e] = 0;
         s_pre[e] = 0;
     }
+    for (int i = tid; i < PERMUTE_WAVES * E; i += blockDim.x) s_wcur[i / E][i % E] = 0;
     __syncthreads();
     // (expert, part) items: each part covers a contiguous run of L chunks of one expert
     const int np = E >= (int)blockDim.x ? 1 : (int)blockDim.x / E;
@@ -168,17 +173,36 @@ __global__ void __launch_bounds__(PERMUTE_SCATTER_THREADS) permute_scatter(
             atomicAdd(&s_pre[e], pre);
         }
     }
+    // this wavefront's piece of the chunk, and its pairs per expert
+    const int p0 = b * chunk, p1 = min(p0 + chunk, P);
+    const int piece = (chunk / PERMUTE_WAVES + MOE_WAVE - 1) / MOE_WAVE * MOE_WAVE;
+    const int w0 = min(p0 + wv * piece, p1), w1 = min(w0 + piece, p1);
+    for (int p = w0 + lane; p < w1; p += MOE_WAVE) {
+        const int e = idx[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&s_wcur[wv][e], 1);
+    }
     __syncthreads();
-    if (wave_id() == 0) {
+    if (wv == 0) {
         const bool first = b == 0;
         scan_counts_wave0(s_tot, s_cur, E, bm, first ? counts : nullptr, first ? offsets : nullptr,
                           first ? act_list : nullptr, first ? tile_off : nullptr, first ? meta : nullptr);
         // the lane that wrote s_cur[e] (experts lane*per ..) adds this chunk's prefix
-        const int per = (E + MOE_WAVE - 1) / MOE_WAVE, lo = min(lane_id() * per, E), hi = min(lo + per, E);
+        const int per = (E + MOE_WAVE - 1) / MOE_WAVE, lo = min(lane * per, E), hi = min(lo + per, E);
         for (int e = lo; e < hi; ++e) s_cur[e] += s_pre[e];
-        const int p0 = b * chunk, p1 = min(p0 + chunk, P);
-        stable_scatter_wave(idx, p0, p1, bits_for(E), E, s_cur, perm, inv);
     }
+    __syncthreads();
+    // per-piece cursors: the chunk's cursor plus the pairs of the pieces before
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = s_cur[e];
+#pragma unroll
+        for (int w = 0; w < PERMUTE_WAVES; ++w) {
+            const int c = s_wcur[w][e];
+            s_wcur[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    stable_scatter_wave(idx, w0, w1, bits_for(E), E, s_wcur[wv], perm, inv);
 }
 
 // From caller-provided offsets (moe_grouped_ffn): the active-expert list, tile offsets, meta.

@@ -87,16 +87,23 @@ __global__ void __launch_bounds__(256) route_topk(const float* __restrict__ logi
     float* l = s_row[wv];
     uint32_t key[EPL];
     if (part) {
+        // every split's values loaded at once (ks <= ROUTER_MAX_SPLIT), then added in split order
         const int64_t n = (int64_t)T * E;
-        float v[EPL];
+        float pv[ROUTER_MAX_SPLIT][EPL];
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) v[j] = 0.0f;
-        for (int q = 0; q < ks; ++q) {
+        for (int q = 0; q < ROUTER_MAX_SPLIT; ++q)
 #pragma unroll
             for (int j = 0; j < EPL; ++j) {
                 const int e = lane * EPL + j;
-                if (e < E) v[j] += part[(int64_t)q * n + (int64_t)t * E + e];
+                pv[q][j] = (q < ks && e < E) ? part[(int64_t)q * n + (int64_t)t * E + e] : 0.0f;
             }
+        float v[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            v[j] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < ROUTER_MAX_SPLIT; ++q)
+                if (q < ks) v[j] += pv[q][j];
         }
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
