@@ -83,14 +83,14 @@ KERNEL_SOURCES = {
 }
 COPY_CAL = dict(fetch_factor=1.99981, write_factor=1.00000)  # profiles/read_counters__calibration.txt
 TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<workload>.txt)
-    "c1_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=27752.8, write_kib=54.4),
-    "c3_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=26249.3, write_kib=96.8),
-    "c3nv_decode_T1": dict(src="decode:e7bf335d72a637b6", fetch_kib=27769.8, write_kib=96.2),
-    "c4_stack": dict(src="decode:e7bf335d72a637b6", fetch_kib=26249.0, write_kib=96.7),
-    "c4_stack_persistent": dict(src="decode:e7bf335d72a637b6", fetch_kib=1751431.0, write_kib=20210.0),
-    "c2_prefill": dict(src="gemm:4c15bee888b49cac", fetch_kib=563483.5, write_kib=110645.8),
-    "c3_prefill": dict(src="gemm:4c15bee888b49cac", fetch_kib=1909294.1, write_kib=298152.1),
-    "c3_prefill_mx": dict(src="mx:a8543ccbbdad988e", fetch_kib=1386020.6, write_kib=102293.9),
+    "c1_decode_T1": dict(src="decode:ffe63db048e10eda", fetch_kib=27747.6, write_kib=54.3),
+    "c3_decode_T1": dict(src="decode:ffe63db048e10eda", fetch_kib=26241.9, write_kib=96.3),
+    "c3nv_decode_T1": dict(src="decode:ffe63db048e10eda", fetch_kib=27761.8, write_kib=96.2),
+    "c4_stack": dict(src="decode:ffe63db048e10eda", fetch_kib=26241.8, write_kib=96.3),
+    "c4_stack_persistent": dict(src="decode:ffe63db048e10eda", fetch_kib=1751435.4, write_kib=20210.0),
+    "c2_prefill": dict(src="gemm:1871c6b16504e32b", fetch_kib=551344.9, write_kib=110653.8),
+    "c3_prefill": dict(src="gemm:1871c6b16504e32b", fetch_kib=1870669.9, write_kib=298141.8),
+    "c3_prefill_mx": dict(src="mx:17c5a4a5b4bc3658", fetch_kib=1372018.6, write_kib=102147.9),
 }
 
 
