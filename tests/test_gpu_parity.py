@@ -83,8 +83,11 @@ def test_route_computed_logits(name, T):
 # ---------------------------------------------------------------------------------------------
 # Permute
 # ---------------------------------------------------------------------------------------------
+# (4099, 24, 1): just past the one-workgroup sort, a last chunk of 3 pairs (one wavefront's piece
+# partly filled, the others empty); (4500, 7, 3): an odd expert count of many counts per thread
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 8, 2), (16, 128, 8), (32, 256, 6), (512, 128, 8),
-                                   (4096, 128, 8), (8192, 256, 6), (3000, 1000, 7), (777, 16, 16)])
+                                   (4096, 128, 8), (8192, 256, 6), (3000, 1000, 7), (777, 16, 16),
+                                   (4099, 24, 1), (4500, 7, 3)])
 def test_permute_bit_exact(T, E, k):
     rng = np.random.default_rng(T + E + k)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
