@@ -88,9 +88,9 @@ TRAFFIC = {  # workload -> counters of its roofline kernel (profiles/<kernel>__<
     "c3nv_decode_T1": dict(src="decode:ffe63db048e10eda", fetch_kib=27761.8, write_kib=96.2),
     "c4_stack": dict(src="decode:ffe63db048e10eda", fetch_kib=26241.8, write_kib=96.3),
     "c4_stack_persistent": dict(src="decode:ffe63db048e10eda", fetch_kib=1751435.4, write_kib=20210.0),
-    "c2_prefill": dict(src="gemm:1871c6b16504e32b", fetch_kib=551344.9, write_kib=110653.8),
-    "c3_prefill": dict(src="gemm:1871c6b16504e32b", fetch_kib=1870669.9, write_kib=298141.8),
-    "c3_prefill_mx": dict(src="mx:17c5a4a5b4bc3658", fetch_kib=1372018.6, write_kib=102147.9),
+    "c2_prefill": dict(src="gemm:9b7c98358210386a", fetch_kib=550290.0, write_kib=110649.8),
+    "c3_prefill": dict(src="gemm:9b7c98358210386a", fetch_kib=1860059.2, write_kib=298145.2),
+    "c3_prefill_mx": dict(src="mx:17c5a4a5b4bc3658", fetch_kib=1383077.5, write_kib=102177.9),
 }
 
 

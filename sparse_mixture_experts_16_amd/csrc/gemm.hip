@@ -122,7 +122,8 @@ __global__ void __launch_bounds__(TM / 64 * 64 * NWN, TM / 64 * NWN >= 8 ? 1 : 2
     constexpr int BM = TM, BK = KB;
     static_assert(TM == 128 || (TM == 256 && KB == 64 && WT == 1), "256-row tiles: bf16 gate/up on 64-element stages");
     // 64-element stages: MXFP4 gate/up only (x rows of 128 bytes, 32 code bytes per weight row)
-    static_assert(KB == 32 || ((KB == 64 || (KB == 128 && WT == 2)) && MODE == MODE_W13 && !SPLIT), "stage depth");
+    static_assert(KB == 32 || ((KB == 64 || (KB == 128 && WT == 2)) && MODE == MODE_W13 && !SPLIT) ||
+                      (KB == 64 && MODE == MODE_ROUTER && WT == 1), "stage depth");
     constexpr int SPG = 128 / BK;                   // stages per MXFP4 scale dword (4 blocks of 32)
     constexpr int CPR = BK / 32;                    // MXFP4 code chunks (blocks) per weight row and stage
     static_assert(NS == 2 || NS == 3, "ring depth");
@@ -268,7 +269,7 @@ __global__ void __launch_bounds__(TM / 64 * 64 * NWN, TM / 64 * NWN >= 8 ? 1 : 2
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int n = (i * THREADS + tid) >> 3, c = (tid & 7) ^ a_swz<64>(n);
-            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + c * 16;
+            bsrc[i] = W + (int64_t)wrow_of(n) * wrb + (int64_t)ks * K * 2 + c * 16;
         }
     } else if (WT == 1) {
 #pragma unroll
@@ -825,7 +826,13 @@ hipError_t launch_route_logits_mfma(const void* x, const void* wr, const float* 
     p.out = ks > 1 ? (void*)part : (void*)logits;
     p.T = T; p.d = d; p.E = E; p.k = 1;
     p.ksplit = ks;
-    hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false, 2>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
+    // 64-element K stages two deep when every split is whole 64s (half the waits and barriers of
+    // 32-element stages, whole 128-byte row pieces), else 32-element stages three deep
+    if ((d / ks) % 64 == 0)
+        hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false, 2, 2, false, false, 64>), dim3(grid8(tiles * ks)),
+                           dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((ggemm<MODE_ROUTER, 1, 128, false, 2>), dim3(grid8(tiles * ks)), dim3(256), 0, st, p);
     *rp = RouterPartials{ks > 1 ? part : nullptr, ks, b, logits};
     return hipGetLastError();
 }
