@@ -243,6 +243,10 @@ DECODE_ODD = [
     mi.LayerSpec("dec1_mxfp4_k12", 1, 160, 96, 24, 12, 1, 64, "bf16", "mxfp4", 1.0, 0.0, 0.05, seed=39),
     mi.LayerSpec("dec1_f32", 1, 100, 40, 8, 5, 1, 24, "f32", "f32", 0.5, 0.1, 0.1, seed=40),
     mi.LayerSpec("dec1_long_f", 1, 64, 2048, 8, 2, 0, 0, "bf16", "bf16", 1.0, 0.02, 0.02, seed=41),
+    # a single token the per-wavefront gate/up routing leaves to the general one: rows longer than
+    # one K step, and more than 256 experts
+    mi.LayerSpec("dec1_long_k", 1, 4096, 64, 8, 2, 1, 32, "bf16", "bf16", 1.0, 0.02, 0.02, seed=42),
+    mi.LayerSpec("dec1_E300", 1, 128, 64, 300, 4, 0, 0, "bf16", "bf16", 1.0, 0.05, 0.05, seed=43),
 ]
 
 
